@@ -44,6 +44,10 @@ those points stays float64. Standard: X0, A, B and X1..X4 are stored; X5 is not.
 Gram: X0, R0, every Q, P and R, and the intermediate R Q are stored; P X0 is not.
 The Gram state may carry an exact power-of-two scale s (R is kept as s X X^T, and
 b, c become b/s, c/s^2); with s = 1 this is the plain recurrence.
+A, B, R and Q are symmetric by definition (A = X X^T and R = X X^T, the article's
+Gram matrix, and B, Q are polynomials in them), so a stored one is a symmetric
+matrix: its lower triangle (row index >= column index) is rounded and mirrored.
+The exact mode evaluates the products as they are.
 """
 from __future__ import annotations
 
@@ -71,6 +75,14 @@ def _ident(z):
     return z
 
 
+def _symmetric(store: Store) -> Store:
+    """Store a matrix that is symmetric by definition: lower triangle, mirrored
+    (storage-faithful mode only; the exact mode keeps the product as computed)."""
+    if store is _ident:
+        return store
+    return lambda z: store(np.tril(z) + np.tril(z, -1).T)
+
+
 def momentum_update(M: np.ndarray, G: np.ndarray, mu: float) -> np.ndarray:
     """[DS] 什么是 Muon 优化器？: momentum is formed from the gradient first."""
     return mu * M + G
@@ -87,10 +99,11 @@ def newton_schulz_standard(X0: np.ndarray, steps: int = NS_STEPS,
     """[DS] 核心算子, zeropower_via_newtonschulz5: `steps` quintic steps on a
     matrix with no more rows than columns."""
     a, b, c = coeffs
+    sym = _symmetric(store)
     X = store(X0)
     for k in range(steps):
-        A = store(X @ X.T)
-        B = store(b * A + c * (A @ A))
+        A = sym(X @ X.T)
+        B = sym(b * A + c * (A @ A))
         X_next = a * X + B @ X
         X = X_next if k == steps - 1 else store(X_next)
     return X
@@ -104,16 +117,17 @@ def newton_schulz_gram(X0: np.ndarray, steps: int = NS_STEPS,
     a, b, c = coeffs
     m = X0.shape[0]
     eye = np.eye(m)
+    sym = _symmetric(store)
     X = store(X0)
-    R = store(scale * (X @ X.T))
+    R = sym(scale * (X @ X.T))
     bs, cs = b / scale, c / (scale * scale)
     P = None
     for k in range(steps):
-        Q = store(a * eye + bs * R + cs * (R @ R))
+        Q = sym(a * eye + bs * R + cs * (R @ R))
         P = Q if k == 0 else store(Q @ P)
         if k < steps - 1:
             RQ = store(R @ Q)
-            R = store(Q @ RQ)
+            R = sym(Q @ RQ)
     return P @ X
 
 

@@ -252,6 +252,65 @@ def test_faithful_gram_on_hadamard_reduces_to_scalars():
     assert np.array_equal(O, (p * x0) * H)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_faithful_row_scaled_hadamard_is_per_row_scalars(fmt):
+    """Y = D H with D diagonal and H rows of a Hadamard matrix (H H^T = n I): every
+    stored iterate is diagonal, so each row follows its own scalar recurrence,
+    rounded at every storage point. Distinct row scales catch transposed or
+    misordered products (B X vs X B, Q P vs P Q, P X0) that a single scale hides."""
+    m, n = 8, 32
+    H = _hadamard(n)[:m]
+    d = np.array([1.0, 0.5, 2.0, 0.125, 3.0, 0.75, 1.5, 0.3])
+    nu = np.sqrt(n * np.sum(d * d))
+    rnd = lambda z: float(rounding.round_to(z, fmt))
+    a, b, c = 3.4445, -4.7750, 2.0315
+    # standard
+    t = np.array([rnd(di / nu) for di in d])
+    for k in range(5):
+        al = np.array([rnd(n * ti * ti) for ti in t])
+        be = np.array([rnd(b * x + c * x * x) for x in al])
+        nxt = a * t + be * t
+        t = nxt if k == 4 else np.array([rnd(x) for x in nxt])
+    O = oracle.orthogonalise(d[:, None] * H, "standard", eps=0.0, store_fmt=fmt)
+    assert np.array_equal(O, t[:, None] * H)
+    if fmt != "f16":
+        return
+    # gram, with the fp16 scale of the Gram state
+    s = oracle.gram_scale(m)
+    x0 = np.array([rnd(di / nu) for di in d])
+    r = np.array([rnd(s * n * x * x) for x in x0])
+    p = None
+    for k in range(5):
+        q = np.array([rnd(a + (b / s) * ri + (c / s ** 2) * ri * ri) for ri in r])
+        p = q if k == 0 else np.array([rnd(qi * pi) for qi, pi in zip(q, p)])
+        if k < 4:
+            rq = np.array([rnd(ri * qi) for ri, qi in zip(r, q)])
+            r = np.array([rnd(qi * x) for qi, x in zip(q, rq)])
+    O = oracle.orthogonalise(d[:, None] * H, "gram", eps=0.0, store_fmt="f16")
+    assert np.array_equal(O, (p * x0)[:, None] * H)
+
+
+def test_faithful_symmetric_iterates_are_stored_symmetric():
+    """A, B (standard) and R, Q (gram) are symmetric by definition; the faithful
+    mode stores them as symmetric matrices (lower triangle mirrored). Checked
+    through a storer that records what it is given."""
+    rng = np.random.default_rng(21)
+    X0 = rng.standard_normal((6, 10)) / 8
+    seen = []
+    def rec(z):
+        z = rounding.round_to(z, "f16")
+        seen.append(z)
+        return z
+    oracle.newton_schulz_gram(X0, 5, store=rec)
+    sq = [z for z in seen if z.shape == (6, 6)]
+    # R0; step 0 stores Q, R Q, R; steps 1-3 store Q, P, R Q, R; step 4 stores Q, P
+    assert len(sq) == 1 + 3 + 3 * 4 + 2
+    sym_idx = [0, 1, 3] + [4 * k + j for k in (1, 2, 3) for j in (0, 3)] + [16]
+    for i in sym_idx:
+        assert np.array_equal(sq[i], sq[i].T), i
+    assert not np.array_equal(sq[2], sq[2].T)          # R Q itself is not symmetric
+
+
 def test_faithful_first_storage_point_is_x0():
     rng = np.random.default_rng(11)
     Y = rng.standard_normal((8, 12))
