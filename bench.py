@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of one Muon optimizer step on one MI355X.
+
+A step is one muon_step call over a whole packed buffer of Muon-target
+matrices: momentum, Frobenius normalisation, five Newton-Schulz iterations per
+matrix, weight decay and the lr-scaled update, all in libmuonstep's kernels.
+The default workload is an owner's packed buffer at 1/8 share of a 7B-class
+model (16 x 4096x4096, 8 x 11008x4096, 4 x 4096x11008; bf16 gradients, fp32
+params and momentum) with the standard quintic in bf16.
+
+Prints one JSON line: Muon-target elements per second (whole job), the
+per-step time, the roofline of the dominant kernel (the Newton-Schulz update
+GEMM, timed per launch with HIP events on its stream over the timed region),
+NS TFLOP/s against the bf16 dense MFMA peak, and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload 3]
+                    [--method standard|gram] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16/fp16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (vector / MFMA)
+HBM_PEAK_GBS = 8000.0
+METRIC = "Muon-target elements/s per step; NS TFLOP/s as % of bf16 MFMA peak"
+
+
+def ns_flops(m: int, n: int, method: str) -> float:
+    """Nominal Newton-Schulz FLOPs of one m x n problem (m <= n), five steps:
+    standard 5 x (2 m^2 n + 2 m^3 + 2 m^2 n); gram 2 m^2 n (R0) + 5 x (2 m^3 for Q)
+    + 4 x (2 m^3 for P) + 4 x (4 m^3 for R) + 2 m^2 n (P X0)."""
+    if method == "standard":
+        return 20.0 * m * m * n + 10.0 * m ** 3
+    return 4.0 * m * m * n + 34.0 * m ** 3
+
+
+def problems(wl):
+    out = []
+    for e in wl.entries:
+        pr = e.split_rows or e.rows
+        for _ in range(e.rows // pr):
+            out.append((min(pr, e.cols), max(pr, e.cols)))
+    return out
+
+
+def device_inputs(wl, dev, seed=0):
+    """Synthetic inputs on the device, the workload's recipe: params N(0,1) fp32;
+    grads (1e-3/4) U V^T + 1e-5 E (rank 16) stored bf16 (N(0,1) for fp32 grads);
+    momentum zero."""
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    n = wl.numel
+    params = torch.randn(n, device=dev, generator=gen)
+    gdt = torch.float32 if wl.grad_dtype == "f32" else torch.bfloat16
+    grads = torch.zeros(n, device=dev, dtype=gdt)
+    for off, e in zip(wl.offsets, wl.entries):
+        if wl.kind == "gaussian":
+            g = torch.randn(e.rows, e.cols, device=dev, generator=gen)
+        else:
+            u = torch.randn(e.rows, 16, device=dev, generator=gen)
+            v = torch.randn(e.cols, 16, device=dev, generator=gen)
+            g = (1e-3 / 4.0) * (u @ v.t()) + 1e-5 * torch.randn(e.rows, e.cols, device=dev,
+                                                                 generator=gen)
+        grads[off:off + e.rows * e.cols] = g.reshape(-1).to(gdt)
+        del g
+    mom = torch.zeros(n, device=dev)
+    return params, grads, mom
+
+
+def gemm_source_hash() -> str:
+    src = os.path.join(ROOT, "newton_schulz_step_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: int):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, or
+    None when there are none or the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_ns_gemm_update_w{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel") != kernel or rec.get("gemm_sha256_16") != gemm_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, method, budget_s=25.0):
+    """The float64 oracle (as it stands) on one matrix per shape group, in table
+    order, while the budget lasts; the untimed groups and the other matrices of
+    each group are extrapolated by nominal NS FLOPs."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 0) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    groups = {}
+    for i, e in enumerate(wl.entries):
+        pr = e.split_rows or e.rows
+        key = (min(pr, e.cols), max(pr, e.cols))
+        groups.setdefault(key, []).append(i)
+    timed_flops, timed_s, names = 0.0, 0.0, []
+    for key, idx in groups.items():
+        if timed_s > budget_s * 0.4 and names:
+            break
+        i = idx[0]
+        e = wl.entries[i]
+        g, p = W.entry_values(wl, i)
+        g64 = W.grad_as_f64(wl, g.ravel())
+        t0 = time.perf_counter()
+        oracle.muon_step(p.ravel(), g64, np.zeros(g64.size), [(0, e.rows, e.cols, e.split_rows)],
+                         lr=wl.lr, mu=wl.momentum, weight_decay=wl.weight_decay, method=method)
+        dt = time.perf_counter() - t0
+        blocks = e.rows // (e.split_rows or e.rows)
+        timed_flops += blocks * ns_flops(key[0], key[1], method)
+        timed_s += dt
+        names.append(f"{e.rows}x{e.cols}" + (f"/split{e.split_rows}" if e.split_rows else ""))
+    total_flops = sum(ns_flops(m, n, method) for m, n in problems(wl))
+    est_step_s = timed_s * total_flops / timed_flops
+    return {"value": wl.muon_elements / est_step_s, "unit": "elements/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"float64 exact-mode oracle, {method} NS, one matrix per shape group "
+                       f"({', '.join(names)}) timed {timed_s:.1f} s; whole step extrapolated "
+                       f"by nominal NS FLOPs to {est_step_s:.1f} s")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--method", default="standard", choices=["standard", "gram"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "owner exchange is not part of this library", file=sys.stderr)
+        return 2
+
+    import torch
+    import newton_schulz_step_amd as nss
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    nss.load()
+    dev = torch.device("cuda:0")
+    wl = W.workload(args.workload)
+    ns_dtype = "bf16" if args.method == "standard" else "f16"
+    if wl.ns_dtype == "f32":
+        ns_dtype = "f32"
+    h = nss.hyper(ns_method=args.method, ns_dtype=ns_dtype, grad_dtype=wl.grad_dtype, lr=wl.lr,
+                  momentum=wl.momentum, weight_decay=wl.weight_decay)
+    tab = wl.table()
+    params, grads, mom = device_inputs(wl, dev)
+    ws = nss.workspace(nss.workspace_size(tab, h), dev)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        nss.step(params, grads, mom, tab, h, ws=ws)
+    torch.cuda.synchronize()
+
+    nss.profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        nss.step(params, grads, mom, tab, h, ws=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kstats = nss.profile_end()
+
+    probs = problems(wl)
+    elems = wl.muon_elements
+    value = elems * args.steps / elapsed
+    ns_total = sum(ns_flops(m, n, args.method) for m, n in probs) * args.steps
+    ns_kinds = [k for k in kstats if k.startswith(("ns_gemm", "gram_gemm"))]
+    ns_ms = sum(kstats[k][1] for k in ns_kinds)
+    peak = FP32_PEAK_TFLOPS if ns_dtype == "f32" else BF16_PEAK_TFLOPS
+
+    # dominant kernel: the standard update GEMM B X (+ a X); algorithmic 2 m^2 n per
+    # problem per launch. Gram: its symmetric GEMM family (nominal FLOPs of the chain).
+    if args.method == "standard":
+        dom_kind = "ns_gemm_update"
+        tile = 256 if probs and probs[0][0] >= 512 else 128
+        dt_name = {"bf16": "__bf16", "f16": "_Float16", "f32": "float"}[ns_dtype]
+        dom_kernel = f"muon::ns_gemm<{dt_name}, {tile}, false, 0>"
+        launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
+        dom_flops = sum(2.0 * m * m * n for m, n in probs) * (h.ns_steps - 1) * args.steps
+    else:
+        # symmetric launches: R0 = X0 X0^T, five Q = aI + bR + cRR, four R <- Q (R Q)
+        dom_kind = "gram_gemm_sym"
+        tile = 256 if probs and probs[0][0] >= 512 else 128
+        dom_kernel = f"muon::ns_gemm<{'_Float16' if ns_dtype == 'f16' else 'float'}, {tile}, true, 0>"
+        launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
+        dom_flops = sum(2.0 * m * m * n + 18.0 * m ** 3 for m, n in probs) * args.steps
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
+    traffic = measured_traffic(dom_kernel, args.workload)
+    mom_launches, mom_ms = kstats.get("momentum_sumsq", (0, 0.0))
+    gbytes = elems * (10 if wl.grad_dtype != "f32" else 12) * args.steps / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ns_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.title + ": " + ", ".join(
+                sorted({f"{sum(1 for x in wl.entries if (x.rows, x.cols) == (e.rows, e.cols))}x"
+                        f"{e.rows}x{e.cols}" for e in wl.entries})),
+            "ns_method": args.method, "ns_dtype": ns_dtype, "grad_dtype": wl.grad_dtype,
+            "param_dtype": "f32", "muon_elements": elems, "problems": len(probs),
+            "lr": wl.lr, "momentum": wl.momentum, "weight_decay": wl.weight_decay,
+            "ns_steps": h.ns_steps, "parallelism": "single GPU",
+        },
+        "ns_tflops": ns_total / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None,
+        "ns_frac_of_peak": (ns_total / (ns_ms * 1e-3) / 1e12 / peak) if ns_ms > 0 else None,
+        "roofline": {
+            "bound": "mfma", "kernel": dom_kernel, "launches": launches,
+            "avg_launch_ms": dom_ms / launches if launches else None,
+            "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak if achieved else None,
+            "traffic": traffic,
+        },
+        "momentum_pass": {
+            "launches": mom_launches,
+            "gbs": gbytes / (mom_ms * 1e-3) if mom_ms > 0 else None,
+            "frac_of_hbm": gbytes / (mom_ms * 1e-3) / HBM_PEAK_GBS if mom_ms > 0 else None,
+        },
+        "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kstats.items()},
+    }
+    del params, grads, mom, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.method)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

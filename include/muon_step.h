@@ -1,0 +1,216 @@
+/*
+ * muon_step.h — C ABI of libmuonstep, one Muon optimizer step on one AMD
+ * Instinct MI355X (gfx950) GPU.
+ *
+ * The step follows the DeepSpeed-Muon article ("DeepSpeed 集成 Muon 优化器实战：
+ * 从正交化原理到 ZeRO 微调配置"):
+ *   - section "什么是 Muon 优化器？": form the momentum from the gradient, then
+ *     orthogonalise the momentum matrix by Newton-Schulz iterations, then update
+ *     the weights with the result; 2D hidden weights only;
+ *   - section "核心算子：牛顿-舒尔茨正交化内核": the quintic iteration with
+ *     a = 3.4445, b = -4.7750, c = 2.0315, five steps ("standard", stable in
+ *     bf16), the variant iterating on the small Gram matrix R = X X^T in fp16
+ *     ("gram"), the method set {"standard", "gram"}, decoupled weight decay
+ *     p *= 1 - lr*wd followed by p -= lr * update, and the Adam(W) fallback for
+ *     parameters that are not 2D;
+ *   - section "如何用 DeepSpeed 配置启用 Muon": defaults (Muon lr 0.02,
+ *     momentum 0.95, ns_method "gram"; Adam lr 3e-4, betas (0.9, 0.95)).
+ * The input layout is the DMuon owner's packed buffer ("Z2 与 Z3 模式", section on
+ * the two packed-buffer lifecycles): all Muon-target matrices of one owner in
+ * one contiguous buffer; here each matrix is row-major at an element offset.
+ *
+ * Per matrix (or per split block, see muon_matrix_t) the step computes
+ *   M <- mu * M + G                                 (fp32 momentum, in place)
+ *   Y  = M, transposed if it has more rows than columns
+ *   X0 = Y / (||Y||_F + ns_eps)
+ *   X  = NS(X0)  (ns_steps iterations; standard: A = X X^T, B = b A + c A A,
+ *                 X <- a X + B X; gram: R = X0 X0^T, Q = a I + b R + c R R,
+ *                 P <- Q P, R <- Q R Q, X = P X0)
+ *   O  = X, transposed back
+ *   p <- p * (1 - lr * weight_decay) - lr * O      (fp32 params, in place)
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device memory (for example torch CUDA tensors);
+ *     host pointers are ordinary memory read during the call and not retained.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the default stream). All
+ *     device work is enqueued on it asynchronously; nothing synchronises the
+ *     host. Faults in device work surface at the caller's next synchronisation.
+ *   - Return value: MUON_OK or one of the MUON_ERR_* codes below. Every argument
+ *     check runs before the first launch, so a call that fails a check leaves
+ *     every buffer unchanged. muon_last_error() gives a message for the last
+ *     failing call on the calling thread.
+ *   - The caller owns all buffers, including the workspace. The library keeps
+ *     one small device array of per-problem descriptors (16 bytes per problem
+ *     plus 16 bytes per 32768-element chunk) for each distinct shape table it
+ *     has seen, created on the first call with that table and reused after;
+ *     muon_release_plans() frees them.
+ *   - Calls that share a workspace, or that update the same buffers, must be
+ *     ordered by the caller (same stream, or events).
+ */
+#ifndef MUON_STEP_H
+#define MUON_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. Invalid combinations raise errors, as the article's DeepSpeed
+ * integration does for unsupported configurations. */
+enum {
+  MUON_OK = 0,
+  MUON_ERR_NULL = 1,        /* a required pointer is NULL */
+  MUON_ERR_BAD_METHOD = 2,  /* ns_method is neither STANDARD nor GRAM */
+  MUON_ERR_BAD_SHAPE = 3,   /* rows/cols < 1, split_rows < 0 or not dividing rows,
+                               n_entries < 0, or a size beyond the limits below */
+  MUON_ERR_RANGE = 4,       /* offset < 0 or offset + rows*cols > numel */
+  MUON_ERR_OVERLAP = 5,     /* two entries overlap, or two buffers overlap */
+  MUON_ERR_ALIGN = 6,       /* an offset not a multiple of 8 elements, or a buffer
+                               pointer not 16-byte aligned */
+  MUON_ERR_UNSUPPORTED = 7, /* a dtype combination that is not implemented (gram
+                               with bf16 storage, params other than fp32, ...) */
+  MUON_ERR_WORKSPACE = 8,   /* workspace smaller than muon_workspace_size() */
+  MUON_ERR_HIP = 9,         /* a HIP runtime call or kernel launch failed */
+  MUON_ERR_BAD_HYPER = 10   /* a non-finite hyperparameter, ns_steps outside
+                               [1, 64], or AdamW step < 1 */
+};
+
+/* Element types. */
+enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1, MUON_DTYPE_F16 = 2 };
+
+/* Newton-Schulz methods (the article's NS_METHODS). */
+enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 };
+
+/* Size limits: min(rows, cols) of a problem <= MUON_MAX_SHORT_SIDE,
+ * max(rows, cols) <= MUON_MAX_LONG_SIDE. */
+#define MUON_MAX_SHORT_SIDE 16384
+#define MUON_MAX_LONG_SIDE (1 << 24)
+
+/* One Muon-target matrix inside the packed buffers. params, grads, momentum
+ * (and update_out / bf16_shadow when given) share one layout: the matrix is
+ * rows x cols, row-major, starting at element `offset` (the article recovers
+ * each gradient with reshape(p.shape), i.e. row-major).
+ * split_rows = 0 orthogonalises the whole matrix; split_rows = k > 0 cuts it
+ * into rows/k blocks of k consecutive rows, each orthogonalised on its own with
+ * its own norm (the "Muon Split" per-head orthogonalisation the article's TL;DR
+ * mentions). */
+typedef struct {
+  int64_t offset;
+  int64_t rows;
+  int64_t cols;
+  int64_t split_rows;
+} muon_matrix_t;
+
+/* Hyperparameters of the Muon group. Fill with muon_default_hyper() first. */
+typedef struct {
+  float lr;            /* default 0.02 (the article's Muon default; muon_lr overrides lr) */
+  float momentum;      /* default 0.95 */
+  float weight_decay;  /* default 0.0 */
+  float ns_a;          /* default 3.4445 */
+  float ns_b;          /* default -4.7750 */
+  float ns_c;          /* default 2.0315 */
+  int32_t ns_steps;    /* default 5 */
+  float ns_eps;        /* default 1e-7: X0 = Y / (||Y||_F + ns_eps) */
+  int32_t ns_method;   /* MUON_NS_STANDARD | MUON_NS_GRAM; default GRAM */
+  int32_t param_dtype; /* MUON_DTYPE_F32 (the only one implemented) */
+  int32_t grad_dtype;  /* MUON_DTYPE_BF16 (default) | F32 | F16 */
+  int32_t ns_dtype;    /* storage/operand type of the iteration: standard F32 | BF16 |
+                          F16; gram F32 | F16. Default F16 (the default method is
+                          gram, which the article runs in fp16; it runs standard in
+                          bf16). MFMA accumulation is fp32 in every case. */
+} muon_hyper_t;
+
+/* AdamW hyperparameters (the Adam group: adam_lr overrides lr). */
+typedef struct {
+  float lr;            /* default 3e-4 */
+  float beta1;         /* default 0.9 */
+  float beta2;         /* default 0.95 */
+  float eps;           /* default 1e-10 (the article's default; its example config uses 1e-8) */
+  float weight_decay;  /* default 0.0 */
+  int32_t step;        /* t >= 1, used for bias correction */
+  int32_t grad_dtype;  /* MUON_DTYPE_BF16 (default) | F32 | F16 */
+} muon_adamw_hyper_t;
+
+/* Fill *h with the defaults listed above. */
+void muon_default_hyper(muon_hyper_t* h);
+void muon_default_adamw_hyper(muon_adamw_hyper_t* h);
+
+/* Bytes of device workspace that muon_step needs for this table and these
+ * hyperparameters (validates the table like muon_step, without the buffer and
+ * range checks). Host-only; no device work. */
+int muon_workspace_size(const muon_matrix_t* table, int32_t n_entries,
+                        const muon_hyper_t* h, size_t* bytes_out);
+
+/* One Muon step over the packed buffers.
+ *   params      device, float32[numel], updated in place (entries only).
+ *   grads       device, grad_dtype[numel], read only.
+ *   momentum    device, float32[numel], updated in place (entries only).
+ *   numel       element count of each packed buffer.
+ *   table       host, n_entries descriptors; entries must not overlap and each
+ *               offset must be a multiple of 8 elements.
+ *   h           host, hyperparameters.
+ *   workspace   device, >= muon_workspace_size() bytes, 256-byte aligned; its
+ *               contents on entry do not matter and are clobbered.
+ *   update_out  optional device float32[numel]: receives O (entries only).
+ *   bf16_shadow optional device bf16[numel] (raw 16-bit words): receives the
+ *               round-to-nearest-even bf16 copy of the new params (entries only),
+ *               the form an owner broadcasts.
+ * Elements outside the entries are never written in any output. */
+int muon_step(void* params, const void* grads, float* momentum, int64_t numel,
+              const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h,
+              void* workspace, size_t workspace_bytes,
+              float* update_out, uint16_t* bf16_shadow, void* stream);
+
+/* AdamW step over a flat buffer of non-2D parameters (the article's Adam
+ * fallback, AdamW mode):
+ *   m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2;
+ *   p <- p (1 - lr wd) - lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
+ * params, m, v: device float32[numel], updated in place; grads: device
+ * grad_dtype[numel]. */
+int adamw_step(float* params, const void* grads, float* m, float* v, int64_t numel,
+               const muon_adamw_hyper_t* h, void* stream);
+
+/* Pack n_entries device matrices into one packed buffer of `numel` elements:
+ * srcs[i] (device, rows*cols elements of `dtype`, row-major) is copied bit for
+ * bit to packed + table[i].offset. Elements of `packed` outside the entries are
+ * not written. `srcs` is a host array of device pointers. The table is checked
+ * as in muon_step (shapes, range, 8-element offset alignment, no overlap). */
+int muon_pack(void* packed, int64_t numel, const void* const* srcs, const muon_matrix_t* table,
+              int32_t n_entries, int32_t dtype, void* stream);
+
+/* The inverse of muon_pack: dsts[i] <- packed + table[i].offset, bit for bit. */
+int muon_unpack(void* const* dsts, const void* packed, int64_t numel, const muon_matrix_t* table,
+                int32_t n_entries, int32_t dtype, void* stream);
+
+/* Message for the last failing call on this thread ("" if none). Valid until the
+ * next call on this thread. */
+const char* muon_last_error(void);
+
+/* Free the cached per-table descriptor arrays (synchronises the device first). */
+int muon_release_plans(void);
+
+/* Kernel timing for measurement. Between muon_profile_begin() and
+ * muon_profile_end(), every launch made by this library is bracketed with HIP
+ * events on the stream it is launched on. muon_profile_end() waits for those
+ * events and reports, per kernel kind, the number of launches and the summed
+ * duration in milliseconds (at most `max_kinds` records). Not thread-safe
+ * against concurrent muon_step calls on other threads. */
+typedef struct {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} muon_kernel_stat_t;
+
+int muon_profile_begin(void);
+int muon_profile_end(muon_kernel_stat_t* out, int32_t max_kinds, int32_t* n_kinds_out);
+
+/* Library version string. */
+const char* muon_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_STEP_H */

@@ -1,0 +1,281 @@
+"""ctypes binding of libmuonstep (argument marshalling only).
+
+Every step of the Muon step runs in the library's HIP kernels; this module only
+turns torch tensors into device pointers and the current HIP stream, and turns
+status codes into MuonError. It never computes a result itself, and it raises
+if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuonstep.so")
+
+# status codes (include/muon_step.h)
+OK, ERR_NULL, ERR_BAD_METHOD, ERR_BAD_SHAPE, ERR_RANGE, ERR_OVERLAP, ERR_ALIGN, \
+    ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_BAD_HYPER = range(11)
+STATUS_NAMES = {
+    0: "MUON_OK", 1: "MUON_ERR_NULL", 2: "MUON_ERR_BAD_METHOD", 3: "MUON_ERR_BAD_SHAPE",
+    4: "MUON_ERR_RANGE", 5: "MUON_ERR_OVERLAP", 6: "MUON_ERR_ALIGN", 7: "MUON_ERR_UNSUPPORTED",
+    8: "MUON_ERR_WORKSPACE", 9: "MUON_ERR_HIP", 10: "MUON_ERR_BAD_HYPER",
+}
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
+NS_METHODS = {"standard": 0, "gram": 1}
+
+EXPORTED = (
+    "muon_default_hyper", "muon_default_adamw_hyper", "muon_workspace_size", "muon_step",
+    "adamw_step", "muon_pack", "muon_unpack", "muon_last_error", "muon_release_plans",
+    "muon_profile_begin", "muon_profile_end", "muon_version",
+)
+
+
+class MuonError(RuntimeError):
+    """A non-zero status from libmuonstep."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.message = message
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+class MuonMatrix(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("split_rows", ctypes.c_int64)]
+
+
+class MuonHyper(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("ns_a", ctypes.c_float),
+                ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
+                ("ns_steps", ctypes.c_int32), ("ns_eps", ctypes.c_float),
+                ("ns_method", ctypes.c_int32), ("param_dtype", ctypes.c_int32),
+                ("grad_dtype", ctypes.c_int32), ("ns_dtype", ctypes.c_int32)]
+
+
+class AdamWHyper(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("step", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m newton_schulz_step_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        pm = ctypes.POINTER(MuonMatrix)
+        lib.muon_default_hyper.argtypes = [ctypes.POINTER(MuonHyper)]
+        lib.muon_default_hyper.restype = None
+        lib.muon_default_adamw_hyper.argtypes = [ctypes.POINTER(AdamWHyper)]
+        lib.muon_default_adamw_hyper.restype = None
+        lib.muon_workspace_size.argtypes = [pm, i32, ctypes.POINTER(MuonHyper), ctypes.POINTER(sz)]
+        lib.muon_step.argtypes = [vp, vp, vp, i64, pm, i32, ctypes.POINTER(MuonHyper), vp, sz,
+                                  vp, vp, vp]
+        lib.adamw_step.argtypes = [vp, vp, vp, vp, i64, ctypes.POINTER(AdamWHyper), vp]
+        lib.muon_pack.argtypes = [vp, i64, ctypes.POINTER(vp), pm, i32, i32, vp]
+        lib.muon_unpack.argtypes = [ctypes.POINTER(vp), vp, i64, pm, i32, i32, vp]
+        lib.muon_last_error.restype = ctypes.c_char_p
+        lib.muon_version.restype = ctypes.c_char_p
+        lib.muon_profile_end.argtypes = [ctypes.POINTER(KernelStat), i32, ctypes.POINTER(i32)]
+        for name in ("muon_workspace_size", "muon_step", "adamw_step", "muon_pack", "muon_unpack",
+                     "muon_release_plans", "muon_profile_begin", "muon_profile_end"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise MuonError(status, load().muon_last_error().decode(errors="replace"))
+
+
+def version() -> str:
+    return load().muon_version().decode()
+
+
+# ----------------------------------------------------------------------------- hyperparameters
+
+def hyper(**kw) -> MuonHyper:
+    """Muon-group hyperparameters: the library defaults, then keyword overrides.
+
+    Accepts lr / muon_lr (muon_lr wins, as in the DeepSpeed config), momentum,
+    weight_decay, ns_method ("standard" | "gram"), ns_steps, ns_eps, ns_a/b/c,
+    grad_dtype and ns_dtype ("f32" | "bf16" | "f16")."""
+    h = MuonHyper()
+    load().muon_default_hyper(ctypes.byref(h))
+    kw = dict(kw)
+    if "muon_lr" in kw:
+        kw["lr"] = kw.pop("muon_lr")
+    for k, v in kw.items():
+        if k == "ns_method":
+            v = NS_METHODS.get(v, v) if isinstance(v, str) else v
+            if isinstance(v, str):
+                v = -1
+        elif k in ("grad_dtype", "ns_dtype", "param_dtype") and isinstance(v, str):
+            v = DTYPES[v]
+        if not hasattr(h, k):
+            raise TypeError(f"unknown Muon hyperparameter {k!r}")
+        setattr(h, k, v)
+    return h
+
+
+def table(entries: Iterable[Sequence[int]]):
+    """ctypes array of muon_matrix_t from (offset, rows, cols[, split_rows]) tuples."""
+    rows = [tuple(e) + (0,) * (4 - len(e)) for e in entries]
+    arr = (MuonMatrix * max(len(rows), 1))()
+    for i, (o, r, c, s) in enumerate(rows):
+        arr[i] = MuonMatrix(o, r, c, s)
+    return arr, len(rows)
+
+
+def workspace_size(entries, h: MuonHyper) -> int:
+    arr, n = table(entries)
+    out = ctypes.c_size_t(0)
+    _check(load().muon_workspace_size(arr, n, ctypes.byref(h), ctypes.byref(out)))
+    return out.value
+
+
+# ----------------------------------------------------------------------------- torch plumbing
+
+_TORCH_DT = None
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libmuonstep must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmuonstep must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t, stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+_ws_cache: Dict[Tuple[int, int], object] = {}
+
+
+def workspace(nbytes: int, device) -> "torch.Tensor":
+    """A cached device workspace of at least `nbytes` bytes (torch allocation)."""
+    torch = _torch()
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        _ws_cache.pop(key, None)
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf
+
+
+def step(params, grads, momentum, entries, h: MuonHyper, ws=None, update_out=None,
+         bf16_shadow=None, stream=None) -> None:
+    """One Muon step (muon_step) on packed torch tensors; updates params and momentum."""
+    torch = _torch()
+    if params.dtype != torch.float32 or momentum.dtype != torch.float32:
+        raise TypeError("params and momentum must be float32")
+    if _dtype_code(grads) != h.grad_dtype:
+        raise TypeError("grads dtype does not match hyper.grad_dtype")
+    numel = params.numel()
+    if grads.numel() != numel or momentum.numel() != numel:
+        raise ValueError("params, grads and momentum must have the same numel")
+    arr, n = table(entries)
+    need = ctypes.c_size_t(0)
+    _check(load().muon_workspace_size(arr, n, ctypes.byref(h), ctypes.byref(need)))
+    if ws is None:
+        ws = workspace(need.value, params.device)
+    if update_out is not None and (update_out.dtype != torch.float32 or update_out.numel() != numel):
+        raise ValueError("update_out must be float32 with params' numel")
+    if bf16_shadow is not None and (bf16_shadow.element_size() != 2 or bf16_shadow.numel() != numel):
+        raise ValueError("bf16_shadow must be a 16-bit tensor with params' numel")
+    _check(load().muon_step(_ptr(params), _ptr(grads), _ptr(momentum), numel, arr, n,
+                            ctypes.byref(h), _ptr(ws), ws.numel() * ws.element_size(),
+                            _ptr(update_out), _ptr(bf16_shadow), _stream(params, stream)))
+
+
+def adamw(params, grads, m, v, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-10, weight_decay=0.0,
+          step: int = 1, stream=None) -> None:
+    """AdamW step (adamw_step) on flat torch tensors; updates params, m and v."""
+    torch = _torch()
+    for t in (params, m, v):
+        if t.dtype != torch.float32:
+            raise TypeError("params, m and v must be float32")
+    numel = params.numel()
+    if any(t.numel() != numel for t in (grads, m, v)):
+        raise ValueError("params, grads, m and v must have the same numel")
+    h = AdamWHyper()
+    load().muon_default_adamw_hyper(ctypes.byref(h))
+    h.lr, h.beta1, h.beta2, h.eps, h.weight_decay = lr, beta1, beta2, eps, weight_decay
+    h.step = step
+    h.grad_dtype = _dtype_code(grads)
+    _check(load().adamw_step(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), numel, ctypes.byref(h),
+                             _stream(params, stream)))
+
+
+def pack(packed, tensors: Sequence, entries, stream=None) -> None:
+    """Copy each tensor bit for bit into `packed` at its table offset."""
+    arr, n = table(entries)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in tensors])
+    _check(load().muon_pack(_ptr(packed), packed.numel(), ptrs, arr, n, _dtype_code(packed),
+                            _stream(packed, stream)))
+
+
+def unpack(tensors: Sequence, packed, entries, stream=None) -> None:
+    """Copy each table entry of `packed` bit for bit into its tensor."""
+    arr, n = table(entries)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in tensors])
+    _check(load().muon_unpack(ptrs, _ptr(packed), packed.numel(), arr, n, _dtype_code(packed),
+                              _stream(packed, stream)))
+
+
+def release_plans() -> None:
+    _check(load().muon_release_plans())
+
+
+def profile_begin() -> None:
+    _check(load().muon_profile_begin())
+
+
+def profile_end() -> Dict[str, Tuple[int, float]]:
+    """{kernel kind: (launches, summed milliseconds)} since profile_begin()."""
+    out = (KernelStat * 64)()
+    n = ctypes.c_int32(0)
+    _check(load().muon_profile_end(out, 64, ctypes.byref(n)))
+    return {out[i].name.decode(): (out[i].launches, out[i].total_ms) for i in range(min(n.value, 64))}

@@ -1,0 +1,606 @@
+// C ABI of libmuonstep: argument checks, the per-table plan cache, and the
+// launch sequence of one Muon step (momentum -> norms -> X0 -> Newton-Schulz
+// chain -> fused apply), plus AdamW and pack/unpack.
+#include <math.h>
+#include <string.h>
+
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace muon {
+
+static thread_local std::string g_err;
+
+static int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing (measurement hooks)
+
+struct ProfRec {
+  const char* kind;
+  hipEvent_t a, b;
+};
+
+static std::mutex g_prof_mu;
+static bool g_prof_active = false;
+static std::vector<ProfRec> g_prof;
+
+template <typename F>
+static hipError_t timed(const char* kind, hipStream_t s, F&& launch) {
+  if (!g_prof_active) return launch();
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return hipErrorOutOfMemory;
+  hipEventRecord(a, s);
+  const hipError_t r = launch();
+  hipEventRecord(b, s);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back({kind, a, b});
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// plan cache: device copies of the problem and chunk descriptors per table
+
+struct Plan {
+  Layout L;
+  ProblemDesc* d_problems = nullptr;
+  ChunkDesc* d_chunks = nullptr;
+  int32_t* d_chunk_begin = nullptr;
+};
+
+static std::mutex g_plan_mu;
+static std::map<std::string, std::unique_ptr<Plan>> g_plans;
+static constexpr size_t kMaxPlans = 1024;
+
+static void free_plan(Plan& p) {
+  if (p.d_problems) hipFree(p.d_problems);
+  if (p.d_chunks) hipFree(p.d_chunks);
+  if (p.d_chunk_begin) hipFree(p.d_chunk_begin);
+  p.d_problems = nullptr;
+  p.d_chunks = nullptr;
+  p.d_chunk_begin = nullptr;
+}
+
+static std::string plan_key(int device, const muon_matrix_t* t, int32_t n, const muon_hyper_t* h) {
+  std::string k;
+  const int32_t hdr[5] = {device, n, h->ns_method, h->ns_dtype, h->grad_dtype};
+  k.append(reinterpret_cast<const char*>(hdr), sizeof(hdr));
+  if (n > 0) k.append(reinterpret_cast<const char*>(t), sizeof(muon_matrix_t) * static_cast<size_t>(n));
+  return k;
+}
+
+static int get_plan(const muon_matrix_t* t, int32_t n, const muon_hyper_t* h, Plan** out) {
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
+  const std::string key = plan_key(device, t, n, h);
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) {
+    *out = it->second.get();
+    return MUON_OK;
+  }
+  if (g_plans.size() >= kMaxPlans) {
+    hipDeviceSynchronize();
+    for (auto& kv : g_plans) free_plan(*kv.second);
+    g_plans.clear();
+  }
+  std::unique_ptr<Plan> p(new Plan);
+  p->L = build_layout(t, n, h);
+  std::vector<ProblemDesc> probs(p->L.problems.size());
+  for (size_t i = 0; i < probs.size(); ++i) {
+    probs[i].src_off = p->L.problems[i].src_off;
+    probs[i].transposed = p->L.problems[i].transposed;
+    probs[i].pad = 0;
+  }
+  std::vector<ChunkDesc> chunks(p->L.chunks.size());
+  for (size_t i = 0; i < chunks.size(); ++i) {
+    chunks[i].start = p->L.chunks[i].start;
+    chunks[i].len = p->L.chunks[i].len;
+    chunks[i].problem = p->L.chunks[i].problem;
+  }
+  const size_t pb = std::max<size_t>(probs.size(), 1) * sizeof(ProblemDesc);
+  const size_t cb = std::max<size_t>(chunks.size(), 1) * sizeof(ChunkDesc);
+  const size_t bb = p->L.chunk_begin.size() * sizeof(int32_t);
+  if (hipMalloc(&p->d_problems, pb) != hipSuccess || hipMalloc(&p->d_chunks, cb) != hipSuccess ||
+      hipMalloc(&p->d_chunk_begin, bb) != hipSuccess) {
+    free_plan(*p);
+    return fail(MUON_ERR_HIP, "hipMalloc of the descriptor arrays failed");
+  }
+  if ((!probs.empty() && hipMemcpy(p->d_problems, probs.data(), probs.size() * sizeof(ProblemDesc),
+                                   hipMemcpyHostToDevice) != hipSuccess) ||
+      (!chunks.empty() && hipMemcpy(p->d_chunks, chunks.data(), chunks.size() * sizeof(ChunkDesc),
+                                    hipMemcpyHostToDevice) != hipSuccess) ||
+      hipMemcpy(p->d_chunk_begin, p->L.chunk_begin.data(), bb, hipMemcpyHostToDevice) != hipSuccess) {
+    free_plan(*p);
+    return fail(MUON_ERR_HIP, "copying the descriptor arrays failed");
+  }
+  *out = p.get();
+  g_plans[key] = std::move(p);
+  return MUON_OK;
+}
+
+// ---------------------------------------------------------------------------
+// helpers
+
+static bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+struct Span {
+  const char* lo;
+  const char* hi;
+  const char* name;
+};
+
+static bool overlapping(const std::vector<Span>& v, std::string& which) {
+  for (size_t i = 0; i < v.size(); ++i)
+    for (size_t j = i + 1; j < v.size(); ++j)
+      if (v[i].lo < v[j].hi && v[j].lo < v[i].hi) {
+        which = std::string(v[i].name) + " and " + v[j].name;
+        return true;
+      }
+  return false;
+}
+
+#define MUON_LAUNCH(kind, stream, expr)                                                        \
+  do {                                                                                         \
+    const hipError_t _e = timed(kind, stream, [&]() { return (expr); });                      \
+    if (_e != hipSuccess)                                                                      \
+      return fail(MUON_ERR_HIP, std::string(kind) + " launch failed: " + hipGetErrorString(_e)); \
+  } while (0)
+
+static float gram_scale(int64_t m) {
+  int e = 0;
+  while ((int64_t(1) << e) < m && e < 15) ++e;
+  return static_cast<float>(int64_t(1) << e);
+}
+
+struct StepCtx {
+  const Plan* P;
+  const muon_hyper_t* h;
+  char* ws;
+  const float* M;
+  float* params;
+  float* update_out;
+  uint16_t* shadow;
+  float decay;
+  hipStream_t s;
+};
+
+static GemmArgs apply_args(const StepCtx& c, const Group& G) {
+  GemmArgs g{};
+  g.params = c.params;
+  g.probs = c.P->d_problems + G.first;
+  g.m_valid = static_cast<int32_t>(G.m);
+  g.n_valid = static_cast<int32_t>(G.n);
+  g.decay = c.decay;
+  g.lr = c.h->lr;
+  g.update_out = c.update_out;
+  g.shadow = c.shadow;
+  return g;
+}
+
+// C = alpha * P Q^T (+ beta D + gamma I) over the problems of a group, symmetric
+// (lower tiles, mirrored) when `sym`.
+static void set_sym(GemmArgs& g, const Group& G, const void* P, const void* Q, int64_t K, int64_t ldpq, int64_t pq_ps,
+                    void* C) {
+  const int T = static_cast<int>(G.mp / G.tile);
+  g.P = P; g.p_ps = pq_ps; g.ldp = static_cast<int32_t>(ldpq);
+  g.Q = Q; g.q_ps = pq_ps; g.ldq = static_cast<int32_t>(ldpq);
+  g.K = static_cast<int32_t>(K);
+  g.tiles_m = T; g.tiles_n = T;
+  g.tiles_per_problem = T * (T + 1) / 2;
+  g.total_tiles = g.tiles_per_problem * G.count;
+  g.C = C; g.c_ps = G.mp * G.mp; g.ldc = static_cast<int32_t>(G.mp);
+  g.Ct = C; g.ct_ps = G.mp * G.mp; g.ldct = static_cast<int32_t>(G.mp);
+}
+
+static void set_full(GemmArgs& g, const Group& G, const void* P, int64_t p_ps, int64_t ldp, const void* Q,
+                     int64_t q_ps, int64_t ldq, int64_t K, int64_t rows, int64_t cols) {
+  g.P = P; g.p_ps = p_ps; g.ldp = static_cast<int32_t>(ldp);
+  g.Q = Q; g.q_ps = q_ps; g.ldq = static_cast<int32_t>(ldq);
+  g.K = static_cast<int32_t>(K);
+  g.tiles_m = static_cast<int32_t>(rows / G.tile);
+  g.tiles_n = static_cast<int32_t>(cols / G.tile);
+  g.tiles_per_problem = g.tiles_m * g.tiles_n;
+  g.total_tiles = g.tiles_per_problem * G.count;
+}
+
+// X0 (and its transpose) of every problem of the group.
+static int run_prep(const StepCtx& c, const Group& G) {
+  const float* invn = reinterpret_cast<const float*>(c.ws + c.P->L.off_invnorm) + G.first;
+  MUON_LAUNCH("prep_x0", c.s,
+              launch_prep_x0(c.h->ns_dtype, c.M, c.P->d_problems + G.first, invn, G.count, static_cast<int>(G.m),
+                             static_cast<int>(G.n), static_cast<int>(G.mp), static_cast<int>(G.np), c.ws + G.x[0],
+                             c.ws + G.y[0], c.s));
+  return MUON_OK;
+}
+
+// Standard quintic (DeepSpeed-Muon article, section 核心算子): per step
+//   A = X X^T;  B = b A + c A A;  X <- a X + B X,
+// the last step's epilogue applying p <- p * decay - lr * X.
+static int run_standard(const StepCtx& c, const Group& G) {
+  const int dt = c.h->ns_dtype;
+  char* ws = c.ws;
+  void* X[2] = {ws + G.x[0], ws + G.x[1]};
+  void* Y[2] = {ws + G.y[0], ws + G.y[1]};
+  void* A = ws + G.a;
+  void* B = ws + G.b;
+  const int64_t xs = G.mp * G.np, ss = G.mp * G.mp;
+  int st = run_prep(c, G);
+  if (st != MUON_OK) return st;
+  int cur = 0;
+  for (int k = 0; k < c.h->ns_steps; ++k) {
+    GemmArgs g1{};
+    set_sym(g1, G, X[cur], X[cur], G.np, G.np, xs, A);
+    g1.alpha = 1.0f;
+    MUON_LAUNCH("ns_gemm_xxt", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, g1, c.s));
+
+    GemmArgs g2{};
+    set_sym(g2, G, A, A, G.mp, G.mp, ss, B);
+    g2.alpha = c.h->ns_c;
+    g2.beta = c.h->ns_b;
+    g2.D = A; g2.d_ps = ss; g2.ldd = static_cast<int32_t>(G.mp);
+    MUON_LAUNCH("ns_gemm_poly", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, g2, c.s));
+
+    const bool last = (k == c.h->ns_steps - 1);
+    GemmArgs g3 = last ? apply_args(c, G) : GemmArgs{};
+    set_full(g3, G, B, ss, G.mp, Y[cur], xs, G.mp, G.mp, G.mp, G.np);
+    g3.alpha = 1.0f;
+    g3.beta = c.h->ns_a;
+    g3.D = X[cur]; g3.d_ps = xs; g3.ldd = static_cast<int32_t>(G.np);
+    if (!last) {
+      g3.C = X[cur ^ 1]; g3.c_ps = xs; g3.ldc = static_cast<int32_t>(G.np);
+      g3.Ct = Y[cur ^ 1]; g3.ct_ps = xs; g3.ldct = static_cast<int32_t>(G.mp);
+      MUON_LAUNCH("ns_gemm_update", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, g3, c.s));
+      cur ^= 1;
+    } else {
+      MUON_LAUNCH("ns_gemm_apply", c.s, launch_ns_gemm(dt, G.tile, false, EPI_APPLY, g3, c.s));
+    }
+  }
+  return MUON_OK;
+}
+
+// Gram variant (same section): R0 = s X0 X0^T (s an exact power of two keeping
+// R's entries in fp16's normal range; b and c are rescaled to match); per step
+//   Q = a I + (b/s) R + (c/s^2) R R;  P <- Q P (P = Q first);  R <- Q (R Q)
+// (not after the last step); finally X = P X0 with the apply fused.
+static int run_gram(const StepCtx& c, const Group& G) {
+  const int dt = c.h->ns_dtype;
+  char* ws = c.ws;
+  void* X0 = ws + G.x[0];
+  void* Y0 = ws + G.y[0];
+  void* R[2] = {ws + G.a, ws + G.r2};
+  void* Qb = ws + G.b;
+  void* PT[2] = {ws + G.pt[0], ws + G.pt[1]};
+  void* Pm = ws + G.p;
+  void* Tt = ws + G.t;
+  const int64_t xs = G.mp * G.np, ss = G.mp * G.mp;
+  const float s = (dt == MUON_DTYPE_F16) ? gram_scale(G.m) : 1.0f;
+  const int S = c.h->ns_steps;
+  int st = run_prep(c, G);
+  if (st != MUON_OK) return st;
+
+  GemmArgs r0{};
+  set_sym(r0, G, X0, X0, G.np, G.np, xs, R[0]);
+  r0.alpha = s;
+  MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, r0, c.s));
+
+  int rc = 0, pc = 0;
+  const void* Pfinal = nullptr;
+  for (int k = 0; k < S; ++k) {
+    // Q_k (symmetric); on the first step it is also P (and P^T)
+    void* Qdst = (k == 0) ? PT[0] : Qb;
+    GemmArgs gq{};
+    set_sym(gq, G, R[rc], R[rc], G.mp, G.mp, ss, Qdst);
+    gq.alpha = c.h->ns_c / (s * s);
+    gq.beta = c.h->ns_b / s;
+    gq.gamma = c.h->ns_a;
+    gq.D = R[rc]; gq.d_ps = ss; gq.ldd = static_cast<int32_t>(G.mp);
+    MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, gq, c.s));
+    if (k == 0) {
+      pc = 0;
+      Pfinal = PT[0];
+    } else {
+      // P <- Q P, with P^T as the second operand; stored transposed, or row-major after the last step
+      GemmArgs gp{};
+      set_full(gp, G, Qdst, ss, G.mp, PT[pc], ss, G.mp, G.mp, G.mp, G.mp);
+      gp.alpha = 1.0f;
+      if (k == S - 1) {
+        gp.C = Pm; gp.c_ps = ss; gp.ldc = static_cast<int32_t>(G.mp);
+        Pfinal = Pm;
+      } else {
+        gp.Ct = PT[pc ^ 1]; gp.ct_ps = ss; gp.ldct = static_cast<int32_t>(G.mp);
+        pc ^= 1;
+        Pfinal = nullptr;
+      }
+      MUON_LAUNCH("gram_gemm_full", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, gp, c.s));
+    }
+    if (k < S - 1) {
+      const void* Qk = Qdst;
+      // T = R Q, stored as T^T
+      GemmArgs gt{};
+      set_full(gt, G, R[rc], ss, G.mp, Qk, ss, G.mp, G.mp, G.mp, G.mp);
+      gt.alpha = 1.0f;
+      gt.Ct = Tt; gt.ct_ps = ss; gt.ldct = static_cast<int32_t>(G.mp);
+      MUON_LAUNCH("gram_gemm_full", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, gt, c.s));
+      // R <- Q T (symmetric: lower tiles, mirrored)
+      GemmArgs gr{};
+      set_sym(gr, G, Qk, Tt, G.mp, G.mp, ss, R[rc ^ 1]);
+      gr.alpha = 1.0f;
+      MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, gr, c.s));
+      rc ^= 1;
+    }
+  }
+  if (Pfinal == nullptr) return fail(MUON_ERR_HIP, "internal: gram chain left no final P");
+  GemmArgs ga = apply_args(c, G);
+  set_full(ga, G, Pfinal, ss, G.mp, Y0, xs, G.mp, G.mp, G.mp, G.np);
+  ga.alpha = 1.0f;
+  MUON_LAUNCH("gram_gemm_apply", c.s, launch_ns_gemm(dt, G.tile, false, EPI_APPLY, ga, c.s));
+  return MUON_OK;
+}
+
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+const char* muon_version(void) { return "libmuonstep 0.1 (gfx950)"; }
+
+const char* muon_last_error(void) { return g_err.c_str(); }
+
+void muon_default_hyper(muon_hyper_t* h) {
+  if (!h) return;
+  h->lr = 0.02f;
+  h->momentum = 0.95f;
+  h->weight_decay = 0.0f;
+  h->ns_a = 3.4445f;
+  h->ns_b = -4.7750f;
+  h->ns_c = 2.0315f;
+  h->ns_steps = 5;
+  h->ns_eps = 1e-7f;
+  h->ns_method = MUON_NS_GRAM;
+  h->param_dtype = MUON_DTYPE_F32;
+  h->grad_dtype = MUON_DTYPE_BF16;
+  h->ns_dtype = MUON_DTYPE_F16;
+}
+
+void muon_default_adamw_hyper(muon_adamw_hyper_t* h) {
+  if (!h) return;
+  h->lr = 3e-4f;
+  h->beta1 = 0.9f;
+  h->beta2 = 0.95f;
+  h->eps = 1e-10f;
+  h->weight_decay = 0.0f;
+  h->step = 1;
+  h->grad_dtype = MUON_DTYPE_BF16;
+}
+
+int muon_workspace_size(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h, size_t* bytes_out) {
+  g_err.clear();
+  if (bytes_out == nullptr) return fail(MUON_ERR_NULL, "bytes_out is NULL");
+  std::string err;
+  const int st = validate(table, n_entries, h, err);
+  if (st != MUON_OK) return fail(st, err);
+  *bytes_out = build_layout(table, n_entries, h).ws_bytes;
+  return MUON_OK;
+}
+
+int muon_step(void* params, const void* grads, float* momentum, int64_t numel, const muon_matrix_t* table,
+              int32_t n_entries, const muon_hyper_t* h, void* workspace, size_t workspace_bytes, float* update_out,
+              uint16_t* bf16_shadow, void* stream) {
+  g_err.clear();
+  std::string err;
+  int st = validate(table, n_entries, h, err);
+  if (st != MUON_OK) return fail(st, err);
+  if (params == nullptr || grads == nullptr || momentum == nullptr)
+    return fail(MUON_ERR_NULL, "params, grads and momentum must not be NULL");
+  if (numel < 0) return fail(MUON_ERR_RANGE, "numel < 0");
+  for (int32_t i = 0; i < n_entries; ++i)
+    if (table[i].offset + table[i].rows * table[i].cols > numel)
+      return fail(MUON_ERR_RANGE, "entry " + std::to_string(i) + " ends beyond numel");
+  if (n_entries == 0 || numel == 0) return MUON_OK;
+  if (workspace == nullptr) return fail(MUON_ERR_NULL, "workspace is NULL");
+  if (misaligned(params, 16) || misaligned(grads, 16) || misaligned(momentum, 16) ||
+      (update_out && misaligned(update_out, 16)) || (bf16_shadow && misaligned(bf16_shadow, 16)))
+    return fail(MUON_ERR_ALIGN, "a buffer pointer is not 16-byte aligned");
+  if (misaligned(workspace, 256)) return fail(MUON_ERR_ALIGN, "workspace is not 256-byte aligned");
+  const size_t gsz = static_cast<size_t>(element_size(h->grad_dtype));
+  const size_t ne = static_cast<size_t>(numel);
+  std::vector<Span> spans = {
+      {static_cast<const char*>(params), static_cast<const char*>(params) + ne * 4, "params"},
+      {static_cast<const char*>(grads), static_cast<const char*>(grads) + ne * gsz, "grads"},
+      {reinterpret_cast<const char*>(momentum), reinterpret_cast<const char*>(momentum) + ne * 4, "momentum"},
+      {static_cast<const char*>(workspace), static_cast<const char*>(workspace) + workspace_bytes, "workspace"}};
+  if (update_out)
+    spans.push_back({reinterpret_cast<const char*>(update_out), reinterpret_cast<const char*>(update_out) + ne * 4,
+                     "update_out"});
+  if (bf16_shadow)
+    spans.push_back({reinterpret_cast<const char*>(bf16_shadow), reinterpret_cast<const char*>(bf16_shadow) + ne * 2,
+                     "bf16_shadow"});
+  std::string which;
+  if (overlapping(spans, which)) return fail(MUON_ERR_OVERLAP, "buffers overlap: " + which);
+
+  Plan* P = nullptr;
+  st = get_plan(table, n_entries, h, &P);
+  if (st != MUON_OK) return st;
+  if (workspace_bytes < P->L.ws_bytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(P->L.ws_bytes) + " bytes");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* partials = reinterpret_cast<float*>(ws + P->L.off_partials);
+  float* invn = reinterpret_cast<float*>(ws + P->L.off_invnorm);
+  const float mu = h->momentum;
+  MUON_LAUNCH("momentum_sumsq", s,
+              launch_momentum_sumsq(h->grad_dtype, momentum, grads, P->d_chunks, static_cast<int>(P->L.chunks.size()),
+                                    mu, partials, s));
+  MUON_LAUNCH("finalize_norm", s,
+              launch_finalize_norm(partials, P->d_chunk_begin, static_cast<int>(P->L.problems.size()), h->ns_eps,
+                                   invn, s));
+  StepCtx c{P, h, ws, momentum, static_cast<float*>(params), update_out, bf16_shadow,
+            static_cast<float>(1.0 - static_cast<double>(h->lr) * static_cast<double>(h->weight_decay)), s};
+  for (const Group& G : P->L.groups) {
+    st = (h->ns_method == MUON_NS_STANDARD) ? run_standard(c, G) : run_gram(c, G);
+    if (st != MUON_OK) return st;
+  }
+  return MUON_OK;
+}
+
+int adamw_step(float* params, const void* grads, float* m, float* v, int64_t numel, const muon_adamw_hyper_t* h,
+               void* stream) {
+  g_err.clear();
+  if (h == nullptr) return fail(MUON_ERR_NULL, "hyperparameter pointer is NULL");
+  if (numel < 0) return fail(MUON_ERR_RANGE, "numel < 0");
+  const float fs[] = {h->lr, h->beta1, h->beta2, h->eps, h->weight_decay};
+  for (float f : fs)
+    if (!std::isfinite(f)) return fail(MUON_ERR_BAD_HYPER, "a hyperparameter is not finite");
+  if (h->step < 1) return fail(MUON_ERR_BAD_HYPER, "step must be >= 1");
+  if (h->beta1 < 0.0f || h->beta1 >= 1.0f || h->beta2 < 0.0f || h->beta2 >= 1.0f)
+    return fail(MUON_ERR_BAD_HYPER, "betas must lie in [0, 1)");
+  const int gsz = element_size(h->grad_dtype);
+  if (gsz == 0) return fail(MUON_ERR_UNSUPPORTED, "grad_dtype must be F32, BF16 or F16");
+  if (numel == 0) return MUON_OK;
+  if (!params || !grads || !m || !v) return fail(MUON_ERR_NULL, "params, grads, m and v must not be NULL");
+  if (misaligned(params, 16) || misaligned(grads, 16) || misaligned(m, 16) || misaligned(v, 16))
+    return fail(MUON_ERR_ALIGN, "a buffer pointer is not 16-byte aligned");
+  const size_t ne = static_cast<size_t>(numel);
+  std::vector<Span> spans = {
+      {reinterpret_cast<const char*>(params), reinterpret_cast<const char*>(params) + ne * 4, "params"},
+      {static_cast<const char*>(grads), static_cast<const char*>(grads) + ne * gsz, "grads"},
+      {reinterpret_cast<const char*>(m), reinterpret_cast<const char*>(m) + ne * 4, "m"},
+      {reinterpret_cast<const char*>(v), reinterpret_cast<const char*>(v) + ne * 4, "v"}};
+  std::string which;
+  if (overlapping(spans, which)) return fail(MUON_ERR_OVERLAP, "buffers overlap: " + which);
+  const double bc1 = 1.0 - pow(static_cast<double>(h->beta1), h->step);
+  const double bc2 = 1.0 - pow(static_cast<double>(h->beta2), h->step);
+  const float step_size = static_cast<float>(static_cast<double>(h->lr) / bc1);
+  const float inv_bc2 = static_cast<float>(1.0 / bc2);
+  const float decay = static_cast<float>(1.0 - static_cast<double>(h->lr) * static_cast<double>(h->weight_decay));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MUON_LAUNCH("adamw", s,
+              launch_adamw(h->grad_dtype, params, grads, m, v, numel, h->beta1, h->beta2, step_size, inv_bc2, h->eps,
+                           decay, s));
+  return MUON_OK;
+}
+
+static int check_pack_table(const muon_matrix_t* table, int32_t n, int64_t numel, int32_t dtype) {
+  if (element_size(dtype) == 0) return fail(MUON_ERR_UNSUPPORTED, "dtype must be F32, BF16 or F16");
+  muon_hyper_t h;
+  muon_default_hyper(&h);
+  h.ns_method = MUON_NS_STANDARD;
+  std::string err;
+  const int st = validate(table, n, &h, err);
+  if (st != MUON_OK) return fail(st, err);
+  for (int32_t i = 0; i < n; ++i)
+    if (table[i].offset + table[i].rows * table[i].cols > numel)
+      return fail(MUON_ERR_RANGE, "entry " + std::to_string(i) + " ends beyond numel");
+  return MUON_OK;
+}
+
+static int run_copies(const std::vector<CopyItem>& items, hipStream_t s) {
+  for (size_t i = 0; i < items.size(); i += kCopyBatch) {
+    const int n = static_cast<int>(std::min<size_t>(kCopyBatch, items.size() - i));
+    MUON_LAUNCH("copy_batch", s, launch_copy_batch(items.data() + i, n, s));
+  }
+  return MUON_OK;
+}
+
+int muon_pack(void* packed, int64_t numel, const void* const* srcs, const muon_matrix_t* table, int32_t n_entries,
+              int32_t dtype, void* stream) {
+  g_err.clear();
+  int st = check_pack_table(table, n_entries, numel, dtype);
+  if (st != MUON_OK) return st;
+  if (n_entries == 0) return MUON_OK;
+  if (!packed || !srcs) return fail(MUON_ERR_NULL, "packed and srcs must not be NULL");
+  const size_t esz = static_cast<size_t>(element_size(dtype));
+  std::vector<CopyItem> items;
+  for (int32_t i = 0; i < n_entries; ++i) {
+    if (!srcs[i]) return fail(MUON_ERR_NULL, "srcs[" + std::to_string(i) + "] is NULL");
+    items.push_back({srcs[i], static_cast<char*>(packed) + table[i].offset * esz,
+                     static_cast<int64_t>(table[i].rows * table[i].cols * esz)});
+  }
+  return run_copies(items, static_cast<hipStream_t>(stream));
+}
+
+int muon_unpack(void* const* dsts, const void* packed, int64_t numel, const muon_matrix_t* table, int32_t n_entries,
+                int32_t dtype, void* stream) {
+  g_err.clear();
+  int st = check_pack_table(table, n_entries, numel, dtype);
+  if (st != MUON_OK) return st;
+  if (n_entries == 0) return MUON_OK;
+  if (!packed || !dsts) return fail(MUON_ERR_NULL, "packed and dsts must not be NULL");
+  const size_t esz = static_cast<size_t>(element_size(dtype));
+  std::vector<CopyItem> items;
+  for (int32_t i = 0; i < n_entries; ++i) {
+    if (!dsts[i]) return fail(MUON_ERR_NULL, "dsts[" + std::to_string(i) + "] is NULL");
+    items.push_back({static_cast<const char*>(packed) + table[i].offset * esz, dsts[i],
+                     static_cast<int64_t>(table[i].rows * table[i].cols * esz)});
+  }
+  return run_copies(items, static_cast<hipStream_t>(stream));
+}
+
+int muon_release_plans(void) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  if (!g_plans.empty()) hipDeviceSynchronize();
+  for (auto& kv : g_plans) free_plan(*kv.second);
+  g_plans.clear();
+  return MUON_OK;
+}
+
+int muon_profile_begin(void) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  g_prof_active = true;
+  return MUON_OK;
+}
+
+int muon_profile_end(muon_kernel_stat_t* out, int32_t max_kinds, int32_t* n_kinds_out) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_active = false;
+  std::vector<muon_kernel_stat_t> stats;
+  int status = MUON_OK;
+  for (auto& r : g_prof) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      status = fail(MUON_ERR_HIP, "reading kernel timing events failed");
+    }
+    muon_kernel_stat_t* k = nullptr;
+    for (auto& s : stats)
+      if (strncmp(s.name, r.kind, sizeof(s.name)) == 0) k = &s;
+    if (!k) {
+      muon_kernel_stat_t s{};
+      strncpy(s.name, r.kind, sizeof(s.name) - 1);
+      stats.push_back(s);
+      k = &stats.back();
+    }
+    k->launches += 1;
+    k->total_ms += ms;
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  const int32_t n = static_cast<int32_t>(stats.size());
+  if (n_kinds_out) *n_kinds_out = n;
+  if (out)
+    for (int32_t i = 0; i < n && i < max_kinds; ++i) out[i] = stats[i];
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Shared device/host definitions of libmuonstep (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "muon_step.h"
+#include "common_host.hpp"
+
+#define MUON_LDS __attribute__((address_space(3)))
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+namespace muon {
+
+// Per-problem descriptor (one Newton-Schulz problem = a matrix or a split block).
+struct ProblemDesc {
+  int64_t src_off;     // element offset of the block in the packed buffers
+  int32_t transposed;  // 1: stored rows x cols with rows > cols, canonical = stored^T
+  int32_t pad;
+};
+
+// Momentum chunk: a contiguous piece of one problem's elements.
+struct ChunkDesc {
+  int64_t start;       // element offset in the packed buffers
+  int32_t len;         // element count (<= kChunkElems)
+  int32_t problem;     // problem index within its group's problem list (global index)
+};
+
+constexpr int kChunkElems = kChunkElemsHost;
+
+// ---------------------------------------------------------------------------
+// element conversions (round to nearest even, the hardware default)
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return static_cast<__bf16>(x); }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return static_cast<_Float16>(x); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
+
+__device__ __forceinline__ unsigned short bf16_bits(float x) {
+  __bf16 b = static_cast<__bf16>(x);
+  return __builtin_bit_cast(unsigned short, b);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned short u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(unsigned short u) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, u));
+}
+
+// grad element -> float (grad dtype chosen at run time per launch template)
+template <int GDT> __device__ __forceinline__ float grad_to_f32(const void* g, int64_t i);
+template <> __device__ __forceinline__ float grad_to_f32<MUON_DTYPE_F32>(const void* g, int64_t i) {
+  return static_cast<const float*>(g)[i];
+}
+template <> __device__ __forceinline__ float grad_to_f32<MUON_DTYPE_BF16>(const void* g, int64_t i) {
+  return bf16_bits_to_f32(static_cast<const unsigned short*>(g)[i]);
+}
+template <> __device__ __forceinline__ float grad_to_f32<MUON_DTYPE_F16>(const void* g, int64_t i) {
+  return f16_bits_to_f32(static_cast<const unsigned short*>(g)[i]);
+}
+
+// 8 consecutive grad elements (16-byte aligned for 16-bit types, 32-byte for f32)
+template <int GDT> __device__ __forceinline__ void load_grad8(const void* g, int64_t i, float (&o)[8]);
+template <> __device__ __forceinline__ void load_grad8<MUON_DTYPE_F32>(const void* g, int64_t i, float (&o)[8]) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(g) + i);
+  f32x4 a = p[0], b = p[1];
+  o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
+  o[4] = b[0]; o[5] = b[1]; o[6] = b[2]; o[7] = b[3];
+}
+template <> __device__ __forceinline__ void load_grad8<MUON_DTYPE_BF16>(const void* g, int64_t i, float (&o)[8]) {
+  u16x8 v = *reinterpret_cast<const u16x8*>(static_cast<const unsigned short*>(g) + i);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = bf16_bits_to_f32(v[e]);
+}
+template <> __device__ __forceinline__ void load_grad8<MUON_DTYPE_F16>(const void* g, int64_t i, float (&o)[8]) {
+  u16x8 v = *reinterpret_cast<const u16x8*>(static_cast<const unsigned short*>(g) + i);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = f16_bits_to_f32(v[e]);
+}
+
+// ---------------------------------------------------------------------------
+// wave / block reductions (fixed order: deterministic)
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace muon

@@ -1,0 +1,338 @@
+// Streaming kernels of the Muon step (gfx950): momentum with per-problem sums of
+// squares, the Frobenius normalisation into the iteration's storage type, AdamW,
+// and bit-exact batched copies for packing.
+//
+// All of these are bound by HBM bandwidth; each thread moves 8 elements per
+// access (16/32-byte vector loads and stores), consecutive threads touch
+// consecutive vectors, and reductions run in a fixed order (wave butterflies,
+// then a fixed sum over waves) so results do not depend on scheduling.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace muon {
+
+// ---------------------------------------------------------------------------
+// momentum (DeepSpeed-Muon article, "什么是 Muon 优化器？": momentum first) and the
+// sum of squares that the Frobenius normalisation needs
+
+template <int GDT>
+__device__ __forceinline__ float momentum8(float* M, const void* G, int64_t i, float mu) {
+  float g[8];
+  load_grad8<GDT>(G, i, g);
+  f32x4* mp = reinterpret_cast<f32x4*>(M + i);
+  f32x4 m0 = mp[0], m1 = mp[1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m0[e] = mu * m0[e] + g[e];
+    m1[e] = mu * m1[e] + g[e + 4];
+  }
+  mp[0] = m0;
+  mp[1] = m1;
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s += m0[e] * m0[e] + m1[e] * m1[e];
+  return s;
+}
+
+template <int GDT>
+__global__ __launch_bounds__(256) void momentum_sumsq_kernel(float* M, const void* G, const ChunkDesc* chunks,
+                                                             float mu, float* partials) {
+  __shared__ float red[4];
+  const ChunkDesc c = chunks[blockIdx.x];
+  const int tid = threadIdx.x;
+  float ss = 0.0f;
+  if ((c.start & 7) == 0) {
+    const int nv = c.len >> 3;
+    int v = tid;
+    for (; v + 3 * 256 < nv; v += 4 * 256) {
+      // four independent vectors in flight per thread
+      const float s0 = momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v) * 8, mu);
+      const float s1 = momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v + 256) * 8, mu);
+      const float s2 = momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v + 512) * 8, mu);
+      const float s3 = momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v + 768) * 8, mu);
+      ss += (s0 + s1) + (s2 + s3);
+    }
+    for (; v < nv; v += 256) ss += momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v) * 8, mu);
+    for (int k = nv * 8 + tid; k < c.len; k += 256) {
+      const int64_t i = c.start + k;
+      const float m = mu * M[i] + grad_to_f32<GDT>(G, i);
+      M[i] = m;
+      ss += m * m;
+    }
+  } else {
+    for (int k = tid; k < c.len; k += 256) {
+      const int64_t i = c.start + k;
+      const float m = mu * M[i] + grad_to_f32<GDT>(G, i);
+      M[i] = m;
+      ss += m * m;
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const ChunkDesc* chunks,
+                                 int n_chunks, float mu, float* partials, hipStream_t s) {
+  if (n_chunks <= 0) return hipSuccess;
+  switch (grad_dtype) {
+    case MUON_DTYPE_BF16:
+      hipLaunchKernelGGL(momentum_sumsq_kernel<MUON_DTYPE_BF16>, dim3(n_chunks), dim3(256), 0, s, M, G, chunks, mu, partials);
+      break;
+    case MUON_DTYPE_F16:
+      hipLaunchKernelGGL(momentum_sumsq_kernel<MUON_DTYPE_F16>, dim3(n_chunks), dim3(256), 0, s, M, G, chunks, mu, partials);
+      break;
+    default:
+      hipLaunchKernelGGL(momentum_sumsq_kernel<MUON_DTYPE_F32>, dim3(n_chunks), dim3(256), 0, s, M, G, chunks, mu, partials);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 1 / (||Y||_F + eps) per problem; partial sums combined in double, fixed order
+
+__global__ __launch_bounds__(256) void finalize_norm_kernel(const float* partials, const int32_t* cb, int n_problems,
+                                                            float eps, float* inv_norm) {
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (p >= n_problems) return;
+  double s = 0.0;
+  for (int k = cb[p] + lane; k < cb[p + 1]; k += 64) s += static_cast<double>(partials[k]);
+  s = wave_sum_d(s);
+  if (lane == 0) inv_norm[p] = static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(eps)));
+}
+
+hipError_t launch_finalize_norm(const float* partials, const int32_t* chunk_begin, int n_problems, float eps,
+                                float* inv_norm, hipStream_t s) {
+  if (n_problems <= 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_norm_kernel, dim3((n_problems + 3) / 4), dim3(256), 0, s, partials, chunk_begin,
+                     n_problems, eps, inv_norm);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// X0 = round(M / (||M||_F + eps)) in canonical orientation (short side = rows),
+// written twice: X (mp x np, row-major) and Y = X^T (np x mp). A 64x64 tile is
+// read in the stored orientation (coalesced), turned in LDS, and written in both
+// orientations (coalesced). Padding rows/columns are written as zeros.
+
+template <typename T>
+__device__ __forceinline__ void store16(T* dst, const float (&v)[16]) {
+  if constexpr (sizeof(T) == 4) {
+    f32x4* d = reinterpret_cast<f32x4*>(dst);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = v[q * 4 + e];
+      d[q] = w;
+    }
+  } else {
+    u16x8 w0, w1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      w0[e] = __builtin_bit_cast(unsigned short, from_f32<T>(v[e]));
+      w1[e] = __builtin_bit_cast(unsigned short, from_f32<T>(v[e + 8]));
+    }
+    u16x8* d = reinterpret_cast<u16x8*>(dst);
+    d[0] = w0;
+    d[1] = w1;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const ProblemDesc* probs, const float* inv_norm,
+                                                      int m, int n, int mp, int np, T* X, T* Y) {
+  __shared__ float tile[64][65];
+  const int tiles_j = np >> 6;
+  const int per = (mp >> 6) * tiles_j;
+  const int p = blockIdx.x / per;
+  const int t = blockIdx.x - p * per;
+  const int i0 = (t / tiles_j) * 64, j0 = (t % tiles_j) * 64;
+  const ProblemDesc pd = probs[p];
+  const float inv = inv_norm[p];
+  const int r = threadIdx.x >> 2, c16 = (threadIdx.x & 3) * 16;
+
+  if (!pd.transposed) {
+    // stored m x n: element (i, j) at src + i * n + j; this thread reads row i0 + r
+    const int gi = i0 + r;
+    const int64_t base = pd.src_off + static_cast<int64_t>(gi) * n + j0 + c16;
+    if (gi < m && j0 + c16 + 16 <= n && (base & 3) == 0) {
+      const f32x4* s = reinterpret_cast<const f32x4*>(M + base);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 w = s[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[r][c16 + q * 4 + e] = w[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int gj = j0 + c16 + e;
+        tile[r][c16 + e] = (gi < m && gj < n) ? M[base + e] : 0.0f;
+      }
+    }
+  } else {
+    // stored n x m: element (i, j) at src + j * m + i; this thread reads stored row j0 + r
+    const int gj = j0 + r;
+    const int64_t base = pd.src_off + static_cast<int64_t>(gj) * m + i0 + c16;
+    if (gj < n && i0 + c16 + 16 <= m && (base & 3) == 0) {
+      const f32x4* s = reinterpret_cast<const f32x4*>(M + base);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 w = s[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[c16 + q * 4 + e][r] = w[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int gi = i0 + c16 + e;
+        tile[c16 + e][r] = (gj < n && gi < m) ? M[base + e] : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int64_t xs = static_cast<int64_t>(mp) * np;
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = tile[r][c16 + e] * inv;
+  store16<T>(X + p * xs + static_cast<int64_t>(i0 + r) * np + j0 + c16, v);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = tile[c16 + e][r] * inv;
+  store16<T>(Y + p * xs + static_cast<int64_t>(j0 + r) * mp + i0 + c16, v);
+}
+
+hipError_t launch_prep_x0(int ns_dtype, const float* M, const ProblemDesc* probs, const float* inv_norm,
+                          int n_problems, int m, int n, int mp, int np, void* X, void* Y, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(n_problems) * (mp / 64) * (np / 64);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  switch (ns_dtype) {
+    case MUON_DTYPE_BF16:
+      hipLaunchKernelGGL(prep_x0_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, M, probs, inv_norm, m, n, mp, np,
+                         static_cast<__bf16*>(X), static_cast<__bf16*>(Y));
+      break;
+    case MUON_DTYPE_F16:
+      hipLaunchKernelGGL(prep_x0_kernel<_Float16>, dim3(blocks), dim3(256), 0, s, M, probs, inv_norm, m, n, mp, np,
+                         static_cast<_Float16*>(X), static_cast<_Float16*>(Y));
+      break;
+    default:
+      hipLaunchKernelGGL(prep_x0_kernel<float>, dim3(blocks), dim3(256), 0, s, M, probs, inv_norm, m, n, mp, np,
+                         static_cast<float*>(X), static_cast<float*>(Y));
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// AdamW (the article's Adam fallback for non-2D parameters, AdamW mode)
+
+template <int GDT>
+__device__ __forceinline__ void adamw8(float* p, const void* g, float* m, float* v, int64_t i, float b1, float b2,
+                                       float step_size, float inv_bc2, float eps, float decay) {
+  float gg[8];
+  load_grad8<GDT>(g, i, gg);
+  f32x4* pp = reinterpret_cast<f32x4*>(p + i);
+  f32x4* mp = reinterpret_cast<f32x4*>(m + i);
+  f32x4* vp = reinterpret_cast<f32x4*>(v + i);
+  f32x4 P[2] = {pp[0], pp[1]}, Mv[2] = {mp[0], mp[1]}, Vv[2] = {vp[0], vp[1]};
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gi = gg[h * 4 + e];
+      const float mn = b1 * Mv[h][e] + (1.0f - b1) * gi;
+      const float vn = b2 * Vv[h][e] + (1.0f - b2) * gi * gi;
+      Mv[h][e] = mn;
+      Vv[h][e] = vn;
+      P[h][e] = P[h][e] * decay - step_size * (mn / (sqrtf(vn * inv_bc2) + eps));
+    }
+  pp[0] = P[0]; pp[1] = P[1];
+  mp[0] = Mv[0]; mp[1] = Mv[1];
+  vp[0] = Vv[0]; vp[1] = Vv[1];
+}
+
+template <int GDT>
+__global__ __launch_bounds__(256) void adamw_kernel(float* p, const void* g, float* m, float* v, int64_t n, float b1,
+                                                    float b2, float step_size, float inv_bc2, float eps, float decay) {
+  const int64_t nv = n >> 3;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; k < nv; k += stride)
+    adamw8<GDT>(p, g, m, v, k * 8, b1, b2, step_size, inv_bc2, eps, decay);
+  if (blockIdx.x == 0) {
+    for (int64_t i = nv * 8 + threadIdx.x; i < n; i += 256) {
+      const float gi = grad_to_f32<GDT>(g, i);
+      const float mn = b1 * m[i] + (1.0f - b1) * gi;
+      const float vn = b2 * v[i] + (1.0f - b2) * gi * gi;
+      m[i] = mn;
+      v[i] = vn;
+      p[i] = p[i] * decay - step_size * (mn / (sqrtf(vn * inv_bc2) + eps));
+    }
+  }
+}
+
+hipError_t launch_adamw(int grad_dtype, float* p, const void* g, float* m, float* v, int64_t n, float beta1,
+                        float beta2, float step_size, float inv_bc2, float eps, float decay, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t nv = n >> 3;
+  int64_t blocks = (nv + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 16384) blocks = 16384;
+  switch (grad_dtype) {
+    case MUON_DTYPE_BF16:
+      hipLaunchKernelGGL(adamw_kernel<MUON_DTYPE_BF16>, dim3(blocks), dim3(256), 0, s, p, g, m, v, n, beta1, beta2,
+                         step_size, inv_bc2, eps, decay);
+      break;
+    case MUON_DTYPE_F16:
+      hipLaunchKernelGGL(adamw_kernel<MUON_DTYPE_F16>, dim3(blocks), dim3(256), 0, s, p, g, m, v, n, beta1, beta2,
+                         step_size, inv_bc2, eps, decay);
+      break;
+    default:
+      hipLaunchKernelGGL(adamw_kernel<MUON_DTYPE_F32>, dim3(blocks), dim3(256), 0, s, p, g, m, v, n, beta1, beta2,
+                         step_size, inv_bc2, eps, decay);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bit-exact batched copies (pack / unpack)
+
+struct CopyBatch {
+  CopyItem items[kCopyBatch];
+};
+
+__global__ __launch_bounds__(256) void copy_batch_kernel(CopyBatch b) {
+  const CopyItem it = b.items[blockIdx.y];
+  const char* s = static_cast<const char*>(it.src);
+  char* d = static_cast<char*>(it.dst);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  int64_t done = 0;
+  if (((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(d)) & 15) == 0) {
+    const int64_t nv = it.bytes >> 4;
+    const uint4* sv = reinterpret_cast<const uint4*>(s);
+    uint4* dv = reinterpret_cast<uint4*>(d);
+    for (int64_t k = t0; k < nv; k += stride) dv[k] = sv[k];
+    done = nv << 4;
+  }
+  for (int64_t k = done + t0; k < it.bytes; k += stride) d[k] = s[k];
+}
+
+hipError_t launch_copy_batch(const CopyItem* items, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  CopyBatch b;
+  int64_t maxb = 0;
+  for (int i = 0; i < n; ++i) {
+    b.items[i] = items[i];
+    if (items[i].bytes > maxb) maxb = items[i].bytes;
+  }
+  int64_t gx = (maxb / 16 + 255) / 256;
+  if (gx < 1) gx = 1;
+  if (gx > 1024) gx = 1024;
+  hipLaunchKernelGGL(copy_batch_kernel, dim3(gx, n), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+}  // namespace muon

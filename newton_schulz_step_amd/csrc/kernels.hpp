@@ -1,0 +1,53 @@
+// Launch interfaces of the HIP kernels (internal to libmuonstep).
+#pragma once
+
+#include "common.hpp"
+
+namespace muon {
+
+enum { EPI_STORE = 0, EPI_APPLY = 1 };
+
+// One batched NT GEMM launch: for every problem p of a shape group,
+//   C_p = epilogue(alpha * P_p Q_p^T + beta * D_p + gamma * I).
+// Strides (_ps) are elements between consecutive problems; ld* are row pitches
+// in elements. K, and the tile-padded extents, are multiples of the tile sizes,
+// so the main loop needs no bounds checks (padding holds zeros).
+struct GemmArgs {
+  const void* P; int64_t p_ps; int32_t ldp;
+  const void* Q; int64_t q_ps; int32_t ldq;
+  int32_t K;
+  int32_t tiles_m, tiles_n, tiles_per_problem, total_tiles;
+  float alpha, beta, gamma;
+  const void* D; int64_t d_ps; int32_t ldd;      // optional (beta term)
+  void* C; int64_t c_ps; int32_t ldc;            // optional row-major store
+  void* Ct; int64_t ct_ps; int32_t ldct;         // optional transposed store (SYM: mirror, = C)
+  // EPI_APPLY: p <- p * decay - lr * v at the problem's stored position
+  float* params; const ProblemDesc* probs; int32_t m_valid, n_valid;
+  float decay, lr;
+  float* update_out; unsigned short* shadow;
+};
+
+hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmArgs& a, hipStream_t s);
+
+// M <- mu M + G over each chunk; partial[c] = sum of squares of the new M in chunk c.
+hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const ChunkDesc* chunks,
+                                 int n_chunks, float mu, float* partials, hipStream_t s);
+
+// inv_norm[p] = 1 / (sqrt(sum of partials of p) + eps), partials summed in a fixed order.
+hipError_t launch_finalize_norm(const float* partials, const int32_t* chunk_begin, int n_problems,
+                                float eps, float* inv_norm, hipStream_t s);
+
+// X0 (canonical m x n, padded mp x np) and Y0 = X0^T (np x mp) of every problem of a group,
+// X0 = round(M * inv_norm); padding zero.
+hipError_t launch_prep_x0(int ns_dtype, const float* M, const ProblemDesc* probs, const float* inv_norm,
+                          int n_problems, int m, int n, int mp, int np, void* X, void* Y, hipStream_t s);
+
+hipError_t launch_adamw(int grad_dtype, float* p, const void* g, float* m, float* v, int64_t n,
+                        float beta1, float beta2, float step_size, float inv_bc2, float eps,
+                        float decay, hipStream_t s);
+
+struct CopyItem { const void* src; void* dst; int64_t bytes; };
+constexpr int kCopyBatch = 64;
+hipError_t launch_copy_batch(const CopyItem* items, int n, hipStream_t s);
+
+}  // namespace muon

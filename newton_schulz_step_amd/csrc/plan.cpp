@@ -1,0 +1,154 @@
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <map>
+#include <utility>
+
+#include "common_host.hpp"
+
+namespace muon {
+
+int element_size(int dtype) {
+  switch (dtype) {
+    case MUON_DTYPE_F32: return 4;
+    case MUON_DTYPE_BF16:
+    case MUON_DTYPE_F16: return 2;
+    default: return 0;
+  }
+}
+
+int tile_for(int64_t m) { return m >= 512 ? 256 : 128; }
+
+static int64_t round_up(int64_t v, int64_t q) { return (v + q - 1) / q * q; }
+static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+int validate(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h, std::string& err) {
+  if (h == nullptr) { err = "hyperparameter pointer is NULL"; return MUON_ERR_NULL; }
+  if (n_entries < 0) { err = "n_entries < 0"; return MUON_ERR_BAD_SHAPE; }
+  if (n_entries > 0 && table == nullptr) { err = "table is NULL"; return MUON_ERR_NULL; }
+  if (h->ns_method != MUON_NS_STANDARD && h->ns_method != MUON_NS_GRAM) {
+    err = "ns_method must be MUON_NS_STANDARD (\"standard\") or MUON_NS_GRAM (\"gram\"), got " +
+          std::to_string(h->ns_method);
+    return MUON_ERR_BAD_METHOD;
+  }
+  const float fs[] = {h->lr, h->momentum, h->weight_decay, h->ns_a, h->ns_b, h->ns_c, h->ns_eps};
+  for (float f : fs)
+    if (!std::isfinite(f)) { err = "a hyperparameter is not finite"; return MUON_ERR_BAD_HYPER; }
+  if (h->ns_eps < 0.0f) { err = "ns_eps < 0"; return MUON_ERR_BAD_HYPER; }
+  if (h->ns_steps < 1 || h->ns_steps > 64) { err = "ns_steps outside [1, 64]"; return MUON_ERR_BAD_HYPER; }
+  if (h->param_dtype != MUON_DTYPE_F32) { err = "only float32 params are implemented"; return MUON_ERR_UNSUPPORTED; }
+  if (element_size(h->grad_dtype) == 0) { err = "grad_dtype must be F32, BF16 or F16"; return MUON_ERR_UNSUPPORTED; }
+  if (element_size(h->ns_dtype) == 0) { err = "ns_dtype must be F32, BF16 or F16"; return MUON_ERR_UNSUPPORTED; }
+  if (h->ns_method == MUON_NS_GRAM && h->ns_dtype == MUON_DTYPE_BF16) {
+    err = "gram Newton-Schulz with bf16 storage is not supported (it diverges); use F16 or F32";
+    return MUON_ERR_UNSUPPORTED;
+  }
+  std::vector<std::pair<int64_t, int64_t>> spans;
+  spans.reserve(n_entries);
+  for (int32_t i = 0; i < n_entries; ++i) {
+    const muon_matrix_t& e = table[i];
+    const std::string at = " (entry " + std::to_string(i) + ")";
+    if (e.rows < 1 || e.cols < 1) { err = "rows and cols must be >= 1" + at; return MUON_ERR_BAD_SHAPE; }
+    if (e.split_rows < 0) { err = "split_rows < 0" + at; return MUON_ERR_BAD_SHAPE; }
+    if (e.split_rows > 0 && e.rows % e.split_rows != 0) { err = "split_rows does not divide rows" + at; return MUON_ERR_BAD_SHAPE; }
+    const int64_t pr = e.split_rows > 0 ? e.split_rows : e.rows;
+    const int64_t m = std::min(pr, e.cols), n = std::max(pr, e.cols);
+    if (m > MUON_MAX_SHORT_SIDE || n > MUON_MAX_LONG_SIDE) { err = "matrix beyond the size limits" + at; return MUON_ERR_BAD_SHAPE; }
+    if (e.offset < 0) { err = "offset < 0" + at; return MUON_ERR_RANGE; }
+    if (e.offset % 8 != 0) { err = "offset is not a multiple of 8 elements" + at; return MUON_ERR_ALIGN; }
+    spans.emplace_back(e.offset, e.rows * e.cols);
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i - 1].first + spans[i - 1].second > spans[i].first) { err = "table entries overlap"; return MUON_ERR_OVERLAP; }
+  return MUON_OK;
+}
+
+Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h) {
+  Layout L;
+  // canonical shape -> group, in order of first appearance
+  std::map<std::pair<int64_t, int64_t>, int> gid;
+  std::vector<std::vector<HostProblem>> per_group;
+  for (int32_t i = 0; i < n_entries; ++i) {
+    const muon_matrix_t& e = table[i];
+    const int64_t pr = e.split_rows > 0 ? e.split_rows : e.rows;
+    const int64_t nblk = e.rows / pr;
+    const int64_t m = std::min(pr, e.cols), n = std::max(pr, e.cols);
+    const auto key = std::make_pair(m, n);
+    auto it = gid.find(key);
+    int g;
+    if (it == gid.end()) {
+      g = static_cast<int>(L.groups.size());
+      gid[key] = g;
+      Group G;
+      G.m = m; G.n = n; G.tile = tile_for(m);
+      G.mp = round_up(m, G.tile); G.np = round_up(n, G.tile);
+      L.groups.push_back(G);
+      per_group.emplace_back();
+    } else {
+      g = it->second;
+    }
+    for (int64_t b = 0; b < nblk; ++b) {
+      HostProblem p;
+      p.src_off = e.offset + b * pr * e.cols;
+      p.transposed = pr > e.cols ? 1 : 0;
+      p.entry = i;
+      per_group[g].push_back(p);
+    }
+  }
+  for (size_t g = 0; g < L.groups.size(); ++g) {
+    L.groups[g].first = static_cast<int>(L.problems.size());
+    L.groups[g].count = static_cast<int>(per_group[g].size());
+    L.problems.insert(L.problems.end(), per_group[g].begin(), per_group[g].end());
+  }
+  // momentum chunks, by problem
+  L.chunk_begin.resize(L.problems.size() + 1);
+  for (const Group& G : L.groups) {
+    const int64_t total = G.m * G.n;
+    for (int p = G.first; p < G.first + G.count; ++p) {
+      L.chunk_begin[p] = static_cast<int32_t>(L.chunks.size());
+      for (int64_t s = 0; s < total; s += kChunkElemsHost) {
+        HostChunk c;
+        c.start = L.problems[p].src_off + s;
+        c.len = static_cast<int32_t>(std::min<int64_t>(kChunkElemsHost, total - s));
+        c.problem = p;
+        L.chunks.push_back(c);
+      }
+    }
+  }
+  L.chunk_begin[L.problems.size()] = static_cast<int32_t>(L.chunks.size());
+
+  // workspace
+  const size_t esz = static_cast<size_t>(element_size(h->ns_dtype));
+  size_t off = 0;
+  L.off_partials = off;
+  off = align256(off + L.chunks.size() * sizeof(float));
+  L.off_invnorm = off;
+  off = align256(off + L.problems.size() * sizeof(float));
+  for (Group& G : L.groups) {
+    const size_t cnt = static_cast<size_t>(G.count);
+    const size_t xbytes = cnt * static_cast<size_t>(G.mp * G.np) * esz;
+    const size_t sbytes = cnt * static_cast<size_t>(G.mp * G.mp) * esz;
+    G.x[0] = off; off = align256(off + xbytes);
+    G.y[0] = off; off = align256(off + xbytes);
+    if (h->ns_method == MUON_NS_STANDARD) {
+      G.x[1] = off; off = align256(off + xbytes);
+      G.y[1] = off; off = align256(off + xbytes);
+      G.a = off; off = align256(off + sbytes);
+      G.b = off; off = align256(off + sbytes);
+    } else {
+      G.a = off; off = align256(off + sbytes);      // R
+      G.r2 = off; off = align256(off + sbytes);     // next R
+      G.b = off; off = align256(off + sbytes);      // Q
+      G.pt[0] = off; off = align256(off + sbytes);  // P^T
+      G.pt[1] = off; off = align256(off + sbytes);  // P^T (next)
+      G.p = off; off = align256(off + sbytes);      // P, row-major, after the last step
+      G.t = off; off = align256(off + sbytes);      // (R Q)^T
+    }
+  }
+  L.ws_bytes = std::max<size_t>(off, 256);
+  return L;
+}
+
+}  // namespace muon

@@ -1,0 +1,61 @@
+// Host-side planning of a Muon step: table validation, problem expansion
+// (split blocks), canonical shapes, shape groups, momentum chunks and the
+// workspace layout. Pure host code, no HIP calls.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "muon_step.h"
+
+namespace muon {
+
+struct HostProblem {
+  int64_t src_off;
+  int32_t transposed;
+  int32_t entry;
+};
+
+struct HostChunk {
+  int64_t start;
+  int32_t len;
+  int32_t problem;
+};
+
+// All problems of one canonical shape (m <= n). Buffers are tile-padded
+// (mp x np), one slice per problem, consecutive.
+struct Group {
+  int64_t m = 0, n = 0, mp = 0, np = 0;
+  int tile = 0;
+  int first = 0, count = 0;          // problems [first, first + count) of the plan
+  // workspace byte offsets
+  size_t x[2] = {0, 0}, y[2] = {0, 0};   // X and X^T, ping-pong (standard); X0 / Y0 in [0] (gram)
+  size_t a = 0, b = 0;                   // standard: A, B; gram: R, Q
+  size_t r2 = 0, pt[2] = {0, 0}, p = 0, t = 0;   // gram: next R, P^T (ping-pong), P, (R Q)^T
+};
+
+struct Layout {
+  std::vector<HostProblem> problems;   // ordered by group
+  std::vector<Group> groups;
+  std::vector<HostChunk> chunks;       // ordered by problem
+  std::vector<int32_t> chunk_begin;    // size problems + 1
+  size_t off_partials = 0, off_invnorm = 0;
+  size_t ws_bytes = 0;
+};
+
+int element_size(int dtype);
+
+// Checks the hyperparameters and the table (shapes, splits, offsets, alignment,
+// overlap). Returns a MUON_* status and fills `err`.
+int validate(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h, std::string& err);
+
+// Builds the layout of a validated table.
+Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h);
+
+// Tile edge used for a problem whose short side is m.
+int tile_for(int64_t m);
+
+}  // namespace muon

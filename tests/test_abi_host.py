@@ -1,0 +1,154 @@
+"""The C ABI without a GPU: the library loads, exports what include/muon_step.h
+declares, and rejects bad arguments before it touches the device.
+
+Every check in muon_step, adamw_step, muon_pack and muon_unpack runs before
+the first HIP call, so these tests pass fake (never dereferenced) device
+addresses and only look at the returned status and message.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import newton_schulz_step_amd as nss
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon_step.h")
+
+FAKE = 0x7f0000000000          # a 256-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nss.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "muon_step" in names and "adamw_step" in names and "muon_pack" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(nss.EXPORTED)
+
+
+def test_defaults_match_article(lib):
+    h = nss.hyper()
+    assert abs(h.lr - 0.02) < 1e-9 and abs(h.momentum - 0.95) < 1e-7
+    assert (round(h.ns_a, 4), round(h.ns_b, 4), round(h.ns_c, 4)) == (3.4445, -4.775, 2.0315)
+    assert h.ns_steps == 5 and h.ns_method == nss.NS_METHODS["gram"]
+    assert abs(h.ns_eps - 1e-7) < 1e-12
+    # muon_lr overrides lr, as in the DeepSpeed config
+    assert abs(nss.hyper(lr=0.5, muon_lr=0.1).lr - 0.1) < 1e-7
+    with pytest.raises(TypeError):
+        nss.hyper(no_such_key=1)
+
+
+def _status(fn):
+    try:
+        fn()
+    except nss.MuonError as e:
+        return e.status, e.message
+    return nss.OK, ""
+
+
+def _ws(entries, **kw):
+    return _status(lambda: nss.workspace_size(entries, nss.hyper(**kw)))
+
+
+def test_workspace_size_validation(lib):
+    assert _ws([(0, 4, 4, 0)], ns_method="standard")[0] == nss.OK
+    assert _ws([(0, 4, 4, 0)], ns_method=7)[0] == nss.ERR_BAD_METHOD
+    assert _ws([(0, 4, 4, 0)], ns_method="newton")[0] == nss.ERR_BAD_METHOD
+    assert _ws([(0, 0, 4, 0)])[0] == nss.ERR_BAD_SHAPE
+    assert _ws([(0, 4, -1, 0)])[0] == nss.ERR_BAD_SHAPE
+    assert _ws([(0, 12, 4, 5)])[0] == nss.ERR_BAD_SHAPE          # split does not divide rows
+    assert _ws([(0, 12, 4, -2)])[0] == nss.ERR_BAD_SHAPE
+    assert _ws([(0, 20000, 20000, 0)])[0] == nss.ERR_BAD_SHAPE   # short side beyond the limit
+    assert _ws([(-8, 4, 4, 0)])[0] == nss.ERR_RANGE
+    assert _ws([(4, 4, 4, 0)])[0] == nss.ERR_ALIGN
+    assert _ws([(0, 4, 4, 0), (8, 4, 4, 0)])[0] == nss.ERR_OVERLAP
+    assert _ws([(0, 4, 4, 0)], ns_method="gram", ns_dtype="bf16")[0] == nss.ERR_UNSUPPORTED
+    assert _ws([(0, 4, 4, 0)], param_dtype=1)[0] == nss.ERR_UNSUPPORTED
+    assert _ws([(0, 4, 4, 0)], ns_steps=0)[0] == nss.ERR_BAD_HYPER
+    assert _ws([(0, 4, 4, 0)], lr=float("nan"))[0] == nss.ERR_BAD_HYPER
+    st, msg = _ws([(0, 4, 4, 0)], ns_method=7)
+    assert "standard" in msg and "gram" in msg
+
+
+def test_workspace_grows_with_the_table(lib):
+    h = nss.hyper(ns_method="standard", ns_dtype="bf16")
+    small = nss.workspace_size([(0, 128, 128, 0)], h)
+    big = nss.workspace_size([(0, 128, 128, 0), (16384, 512, 128, 0)], h)
+    assert 0 < small < big
+    assert nss.workspace_size([], h) > 0
+
+
+def _raw_step(lib, entries, numel, h, params=FAKE, grads=FAKE + (1 << 36), mom=FAKE + (2 << 36),
+              ws=FAKE + (3 << 36), ws_bytes=1 << 40, upd=None, shadow=None):
+    arr, n = nss.table(entries)
+    st = lib.muon_step(params, grads, mom, numel, arr, n, ctypes.byref(h), ws, ws_bytes,
+                       upd, shadow, None)
+    return st, lib.muon_last_error().decode()
+
+
+def test_step_rejects_before_any_device_work(lib):
+    h = nss.hyper(ns_method="standard", ns_dtype="bf16")
+    ent = [(0, 64, 64, 0)]
+    assert _raw_step(lib, ent, 4096, h, params=None)[0] == nss.ERR_NULL
+    assert _raw_step(lib, ent, 4095, h)[0] == nss.ERR_RANGE
+    assert _raw_step(lib, ent, 4096, h, params=FAKE + 8)[0] == nss.ERR_ALIGN
+    assert _raw_step(lib, ent, 4096, h, ws=FAKE + (3 << 36) + 16)[0] == nss.ERR_ALIGN
+    assert _raw_step(lib, ent, 4096, h, mom=FAKE + 1024)[0] == nss.ERR_OVERLAP
+    assert _raw_step(lib, ent, 4096, h, upd=FAKE + (1 << 36))[0] == nss.ERR_OVERLAP
+    assert _raw_step(lib, ent, 4096, h, ws=None)[0] == nss.ERR_NULL
+    bad = nss.hyper(ns_method=3)
+    assert _raw_step(lib, ent, 4096, bad)[0] == nss.ERR_BAD_METHOD
+    # an empty table is a no-op that succeeds without touching the device
+    assert _raw_step(lib, [], 4096, h)[0] == nss.OK
+    st, msg = _raw_step(lib, [(0, 64, 64, 0), (64 * 64, 8, 8, 0)], 4096, h)
+    assert st == nss.ERR_RANGE and "entry 1" in msg
+
+
+def test_adamw_rejects_before_any_device_work(lib):
+    h = nss.AdamWHyper()
+    lib.muon_default_adamw_hyper(ctypes.byref(h))
+    assert abs(h.lr - 3e-4) < 1e-10 and abs(h.beta1 - 0.9) < 1e-7 and abs(h.beta2 - 0.95) < 1e-7
+    a, b, c, d = FAKE, FAKE + (1 << 36), FAKE + (2 << 36), FAKE + (3 << 36)
+    assert lib.adamw_step(a, b, c, d, 1000, None, None) == nss.ERR_NULL
+    h.step = 0
+    assert lib.adamw_step(a, b, c, d, 1000, ctypes.byref(h), None) == nss.ERR_BAD_HYPER
+    h.step = 1
+    h.beta1 = 1.0
+    assert lib.adamw_step(a, b, c, d, 1000, ctypes.byref(h), None) == nss.ERR_BAD_HYPER
+    h.beta1 = 0.9
+    assert lib.adamw_step(a, b, c + 4, d, 1000, ctypes.byref(h), None) == nss.ERR_ALIGN
+    assert lib.adamw_step(a, b, a + 64, d, 1000, ctypes.byref(h), None) == nss.ERR_OVERLAP
+    assert lib.adamw_step(a, b, c, d, 0, ctypes.byref(h), None) == nss.OK
+    h.grad_dtype = 9
+    assert lib.adamw_step(a, b, c, d, 1000, ctypes.byref(h), None) == nss.ERR_UNSUPPORTED
+
+
+def test_pack_rejects_before_any_device_work(lib):
+    arr, n = nss.table([(0, 4, 4, 0), (16, 4, 4, 0)])
+    srcs = (ctypes.c_void_p * 2)(FAKE, FAKE + 4096)
+    assert lib.muon_pack(FAKE + (1 << 36), 31, srcs, arr, n, 0, None) == nss.ERR_RANGE
+    assert lib.muon_pack(FAKE + (1 << 36), 32, srcs, arr, n, 5, None) == nss.ERR_UNSUPPORTED
+    srcs_null = (ctypes.c_void_p * 2)(FAKE, None)
+    assert lib.muon_pack(FAKE + (1 << 36), 32, srcs_null, arr, n, 0, None) == nss.ERR_NULL
+    arr2, n2 = nss.table([(0, 4, 4, 0), (8, 4, 4, 0)])
+    assert lib.muon_unpack(srcs, FAKE + (1 << 36), 32, arr2, n2, 1, None) == nss.ERR_OVERLAP
+
+
+def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    from newton_schulz_step_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _binding.load()

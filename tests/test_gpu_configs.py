@@ -1,0 +1,142 @@
+"""Full-size workloads on the GPU, in the launch configuration the benchmark
+times (the whole packed table in one muon_step call), checked on sampled
+entries that the CPU oracle computes one by one.
+
+The sampled entries get their seeded host values; every other entry is filled
+on the device with Gaussian values of the same scale (problems are independent,
+so this does not change what the sampled ones must produce). Gates as in
+test_gpu_parity: bf16 / fp16 iterations within 3e-2 of the storage-faithful
+oracle, and within 3e-2 of the exact oracle on the top-16 signal subspace;
+momentum within 1e-6; untouched sampled neighbours' bytes are not checked here
+(test_gpu_parity covers them).
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import rel, to_device, top_subspace_err
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
+
+LP_GATE = 3e-2
+MOM_GATE = 1e-6
+
+
+def _device_inputs(wl, sample, dev):
+    import torch
+    n = wl.numel
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + wl.wid)
+    params = torch.randn(n, device=dev, generator=gen)
+    grads = (torch.randn(n, device=dev, generator=gen) * 1e-3).to(torch.bfloat16)
+    mom = torch.zeros(n, device=dev)
+    host = {}
+    for i in sample:
+        g, p = W.entry_values(wl, i)
+        off, e = wl.offsets[i], wl.entries[i]
+        sl = slice(off, off + e.rows * e.cols)
+        params[sl] = torch.from_numpy(p.ravel()).to(dev)
+        grads[sl] = to_device(g.ravel(), dev, torch)
+        host[i] = (g, p)
+    return params, grads, mom, host
+
+
+def _blocks(e):
+    return [(0, e.rows)] if e.split_rows == 0 else \
+        [(r, e.split_rows) for r in range(0, e.rows, e.split_rows)]
+
+
+def _run(nss, wid, method, ns_dtype, sample):
+    import torch
+    dev = "cuda:0"
+    wl = W.workload(wid)
+    print(f"[case] workload {wid} ({wl.title}) {method}/{ns_dtype} sample {sample}", flush=True)
+    params, grads, mom, host = _device_inputs(wl, sample, dev)
+    upd = torch.zeros_like(params)
+    h = nss.hyper(ns_method=method, ns_dtype=ns_dtype, grad_dtype="bf16", lr=wl.lr,
+                  momentum=wl.momentum, weight_decay=wl.weight_decay)
+    t0 = time.time()
+    nss.step(params, grads, mom, wl.table(), h, update_out=upd)
+    torch.cuda.synchronize()
+    print(f"  gpu step done in {time.time() - t0:.2f} s", flush=True)
+    for i in sample:
+        e, off = wl.entries[i], wl.offsets[i]
+        sl = slice(off, off + e.rows * e.cols)
+        O = upd[sl].cpu().numpy().reshape(e.rows, e.cols).astype(np.float64)
+        P = params[sl].cpu().numpy().reshape(e.rows, e.cols)
+        M = mom[sl].cpu().numpy().reshape(e.rows, e.cols)
+        g, p0 = host[i]
+        g64 = W.grad_as_f64(wl, g.ravel())
+        tab = [(0, e.rows, e.cols, e.split_rows)]
+        t0 = time.time()
+        kw = dict(lr=wl.lr, mu=wl.momentum, weight_decay=wl.weight_decay, method=method)
+        ref = oracle.muon_step(p0.ravel(), g64, np.zeros(g64.size), tab, store_fmt=ns_dtype, **kw)
+        exact = oracle.muon_step(p0.ravel(), g64, np.zeros(g64.size), tab, **kw)
+        print(f"  entry {i} {e.rows}x{e.cols}/{e.split_rows}: oracle {time.time() - t0:.1f} s",
+              flush=True)
+        Of = ref["update"].reshape(e.rows, e.cols)
+        Oe = exact["update"].reshape(e.rows, e.cols)
+        Me = exact["momentum"].reshape(e.rows, e.cols)
+        eo = rel(O, Of)
+        em = rel(M, Me)
+        dp = rel(P - p0, ref["params"].reshape(e.rows, e.cols) - p0)
+        worst_sub = 0.0
+        for r0, nr in _blocks(e):
+            Mb, Ob, Oeb = Me[r0:r0 + nr], O[r0:r0 + nr], Oe[r0:r0 + nr]
+            if nr > e.cols:
+                Mb, Ob, Oeb = Mb.T, Ob.T, Oeb.T
+            worst_sub = max(worst_sub, top_subspace_err(Ob, Oeb, Mb))
+        print(f"  entry {i}: O vs faithful {eo:.2e}, O vs exact {rel(O, Oe):.2e}, "
+              f"top-16 {worst_sub:.2e}, M {em:.2e}, dp {dp:.2e}", flush=True)
+        assert eo <= LP_GATE and dp <= LP_GATE and em <= MOM_GATE
+        assert worst_sub <= LP_GATE
+    del params, grads, mom, upd
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_one_layer(lib, method, ns_dtype):
+    _run(lib, 2, method, ns_dtype, sample=[0, 4, 6])
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_owner_share_7b(lib, method, ns_dtype):
+    _run(lib, 3, method, ns_dtype, sample=[5])
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_moe_experts(lib, method, ns_dtype):
+    _run(lib, 4, method, ns_dtype, sample=[0, 95, 191])
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_per_head_split(lib, method, ns_dtype):
+    _run(lib, 5, method, ns_dtype, sample=[0, 127])
+
+
+def test_per_head_adamw_part(lib):
+    """The AdamW part of the per-head workload: a 32000 x 4096 embedding and 65
+    vectors of 4096 in one flat buffer, one step, checked on sampled slices."""
+    import torch
+    dev = "cuda:0"
+    wl = W.workload(5)
+    n = sum(wl.adamw_sizes)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    p = torch.randn(n, device=dev, generator=gen)
+    g = torch.randn(n, device=dev, generator=gen).to(torch.bfloat16)
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    spans = [slice(0, 1 << 20), slice(n // 2, n // 2 + 4096 * 7), slice(n - 65 * 4096, n)]
+    before = [(p[s].cpu().numpy(), g[s].float().cpu().numpy()) for s in spans]
+    lr, b1, b2, eps, wd = 3e-4, 0.9, 0.95, 1e-8, 0.1
+    nss = lib
+    nss.adamw(p, g, m, v, lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, step=1)
+    torch.cuda.synchronize()
+    for s, (p0, g0) in zip(spans, before):
+        P, M, V = oracle.adamw_step(p0, g0, np.zeros(g0.size), np.zeros(g0.size), lr, b1, b2, eps, wd, 1)
+        assert rel(m[s].cpu().numpy(), M) <= MOM_GATE and rel(v[s].cpu().numpy(), V) <= MOM_GATE
+        assert rel(p[s].cpu().numpy() - p0, P - p0) <= 1e-3

@@ -1,0 +1,354 @@
+"""GPU parity of the Muon step (through the C ABI) against the CPU oracle.
+
+Sizes are ones the oracle finishes in seconds while still covering several
+MFMA tiles, both tile edges (128 for a short side below 512, 256 above), ragged
+tails, transposed (tall) matrices, split blocks and degenerate 1x1 problems.
+
+Gates (relative Frobenius error per entry):
+  fp32 iteration:            update and weight change vs the exact oracle <= 1e-4
+  bf16 / fp16 iteration:     vs the storage-faithful oracle <= 3e-2; on Gaussian
+                             inputs also vs the exact oracle <= 3e-2; on low-rank
+                             inputs the top-16 signal subspace vs exact <= 3e-2
+  momentum:                  <= 1e-6 (fp32 state vs float64)
+  copies, untouched bytes, lr = 0, mu = 0, split == separate entries,
+  batch invariance, run-to-run, resume: bit-exact
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import (entry_slices, outside_mask, rel, run_step, to_device,
+                         top_subspace_err)
+
+pytestmark = pytest.mark.gpu
+
+FP32_GATE = 1e-4
+LP_GATE = 3e-2
+MOM_GATE = 1e-6
+
+
+def _hyper(nss, wl, method, ns_dtype, **kw):
+    args = dict(ns_method=method, ns_dtype=ns_dtype, grad_dtype=wl.grad_dtype, lr=wl.lr,
+                momentum=wl.momentum, weight_decay=wl.weight_decay)
+    args.update(kw)
+    return nss.hyper(**args)
+
+
+def _check(nss, wl, method, ns_dtype, faithful, gaussian_exact_gate=None, subspace=False,
+           shadow=False):
+    params, grads, mom = W.host_inputs(wl)
+    tab = wl.table()
+    print(f"[case] {wl.title} method={method} ns_dtype={ns_dtype} shapes="
+          f"{[(e.rows, e.cols, e.split_rows) for e in wl.entries]}", flush=True)
+    gpu = run_step(nss, params, grads, mom, tab, _hyper(nss, wl, method, ns_dtype), shadow=shadow)
+    g64 = W.grad_as_f64(wl, grads)
+    kw = dict(lr=wl.lr, mu=wl.momentum, weight_decay=wl.weight_decay, method=method)
+    exact = oracle.muon_step(params, g64, mom, tab, **kw)
+    ref = oracle.muon_step(params, g64, mom, tab, store_fmt=ns_dtype, **kw) if faithful else exact
+    gate = LP_GATE if faithful else FP32_GATE
+    for i, sl in enumerate(entry_slices(tab)):
+        e = wl.entries[i]
+        eo = rel(gpu["update"][sl], ref["update"][sl])
+        em = rel(gpu["momentum"][sl], exact["momentum"][sl])
+        dp = rel(gpu["params"][sl] - params[sl], ref["params"][sl] - params[sl])
+        print(f"  entry {i} {e.rows}x{e.cols}/{e.split_rows}: O {eo:.2e} M {em:.2e} dp {dp:.2e}")
+        assert eo <= gate and dp <= gate and em <= MOM_GATE, (i, eo, dp, em)
+        if gaussian_exact_gate is not None:
+            assert rel(gpu["update"][sl], exact["update"][sl]) <= gaussian_exact_gate
+        if subspace:
+            blocks = [(0, e.rows)] if e.split_rows == 0 else \
+                [(r, e.split_rows) for r in range(0, e.rows, e.split_rows)]
+            Mm = exact["momentum"][sl].reshape(e.rows, e.cols)
+            Og = gpu["update"][sl].reshape(e.rows, e.cols).astype(np.float64)
+            Oe = exact["update"][sl].reshape(e.rows, e.cols)
+            for r0, nr in blocks:
+                Mb, Ogb, Oeb = Mm[r0:r0 + nr], Og[r0:r0 + nr], Oe[r0:r0 + nr]
+                if nr > e.cols:     # left singular vectors of the short side
+                    Mb, Ogb, Oeb = Mb.T, Ogb.T, Oeb.T
+                es = top_subspace_err(Ogb, Oeb, Mb)
+                assert es <= LP_GATE, (i, r0, es)
+    mask = outside_mask(tab, len(params))
+    assert np.array_equal(gpu["params"][mask], params[mask])
+    assert np.array_equal(gpu["momentum"][mask], mom[mask])
+    assert not np.any(gpu["update"][mask])
+    return gpu, params
+
+
+# --------------------------------------------------------------------------- fp32 iteration
+
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_tiny_fp32_workload(lib, method):
+    _check(lib, W.workload(1), method, "f32", faithful=False)
+
+
+RAGGED = [(300, 200, 0), (130, 700, 0), (1, 1, 0), (5, 77, 0), (700, 130, 0), (256, 96, 64),
+          (520, 600, 0), (64, 2000, 0), (3, 1, 0)]
+
+
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_ragged_fp32(lib, method):
+    wl = W.custom_workload(RAGGED, grad_dtype="f32", ns_dtype="f32", wid=101)
+    _check(lib, wl, method, "f32", faithful=False)
+
+
+# --------------------------------------------------------------------------- half precision
+
+LOWRANK = [(256, 640, 0), (640, 256, 0), (600, 900, 0), (512, 768, 128)]
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16"),
+                                             ("standard", "f16")])
+def test_half_precision_gaussian(lib, method, ns_dtype):
+    wl = W.custom_workload([(128, 128, 0), (128, 512, 0), (512, 128, 0), (200, 333, 0)],
+                           grad_dtype="bf16", wid=102, grad_kind="gaussian")
+    _check(lib, wl, method, ns_dtype, faithful=True, gaussian_exact_gate=LP_GATE)
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16"),
+                                             ("standard", "f16")])
+def test_half_precision_lowrank(lib, method, ns_dtype):
+    wl = W.custom_workload(LOWRANK, grad_dtype="bf16", wid=103)
+    _check(lib, wl, method, ns_dtype, faithful=True, subspace=True)
+
+
+def test_fp32_grads_half_iteration(lib):
+    wl = W.custom_workload([(192, 320, 0), (320, 192, 0)], grad_dtype="f32", wid=104,
+                           grad_kind="lowrank")
+    _check(lib, wl, "standard", "bf16", faithful=True, subspace=True)
+
+
+def test_bf16_shadow_is_rne_of_new_params(lib):
+    wl = W.custom_workload([(128, 256, 0), (300, 140, 0)], grad_dtype="bf16", wid=105)
+    gpu, _ = _check(lib, wl, "standard", "bf16", faithful=True, shadow=True)
+    for sl in entry_slices(wl.table()):
+        assert np.array_equal(gpu["shadow"][sl], W.f32_to_bf16_bits(gpu["params"][sl]))
+    assert not np.any(gpu["shadow"][outside_mask(wl.table(), wl.numel)])
+
+
+# --------------------------------------------------------------------------- exact properties
+
+def _dev_step(nss, params, grads, mom, tab, h, dev="cuda:0"):
+    import torch
+    p, g, m = (to_device(a, dev, torch) for a in (params, grads, mom))
+    u = torch.zeros_like(p)
+    nss.step(p, g, m, tab, h, update_out=u)
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), m.cpu().numpy(), u.cpu().numpy()
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_split_equals_separate_entries(lib, method, ns_dtype):
+    rows, cols, k = 512, 384, 128
+    wl = W.custom_workload([(rows, cols, k)], wid=106)
+    params, grads, mom = W.host_inputs(wl)
+    h = _hyper(lib, wl, method, ns_dtype)
+    a = _dev_step(lib, params, grads, mom, [(0, rows, cols, k)], h)
+    b = _dev_step(lib, params, grads, mom, [(i * k * cols, k, cols, 0) for i in range(rows // k)], h)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16"),
+                                             ("standard", "f32")])
+def test_batch_invariance_and_determinism(lib, method, ns_dtype):
+    shapes = [(256, 384, 0), (256, 384, 0), (384, 256, 0), (100, 50, 0), (256, 384, 0)]
+    wl = W.custom_workload(shapes, wid=107)
+    params, grads, mom = W.host_inputs(wl)
+    tab = wl.table()
+    h = _hyper(lib, wl, method, ns_dtype)
+    full1 = _dev_step(lib, params, grads, mom, tab, h)
+    full2 = _dev_step(lib, params, grads, mom, tab, h)
+    for x, y in zip(full1, full2):
+        assert np.array_equal(x, y)                    # run to run
+    for i in (1, 2):
+        alone = _dev_step(lib, params, grads, mom, [tab[i]], h)
+        sl = entry_slices(tab)[i]
+        for x, y in zip(alone, full1):
+            assert np.array_equal(x[sl], y[sl])        # alone == in a batch
+
+
+def test_special_cases_bit_exact(lib):
+    wl = W.custom_workload([(64, 200, 0), (300, 64, 0)], grad_dtype="bf16", wid=108)
+    params, grads, mom = W.host_inputs(wl)
+    tab = wl.table()
+    sl = entry_slices(tab)
+    # lr = 0: parameters unchanged
+    p, _, _ = _dev_step(lib, params, grads, mom, tab, _hyper(lib, wl, "standard", "bf16", lr=0.0))
+    assert np.array_equal(p, params)
+    # mu = 0 with a non-zero previous momentum: momentum equals the gradient
+    _, m, _ = _dev_step(lib, params, grads, mom + 3.0, tab, _hyper(lib, wl, "gram", "f16", momentum=0.0))
+    g32 = W.bf16_bits_to_f32(grads)
+    for s in sl:
+        assert np.array_equal(m[s], g32[s])
+    # zero gradient and momentum: zero update, pure decay p * fl(1 - lr wd)
+    lr, wd = 0.5, 0.2
+    p, m, u = _dev_step(lib, params, np.zeros_like(grads), mom, tab,
+                        _hyper(lib, wl, "standard", "bf16", lr=lr, weight_decay=wd))
+    decay = np.float32(1.0 - np.float64(np.float32(lr)) * np.float64(np.float32(wd)))
+    for s in sl:
+        assert not np.any(u[s])
+        assert np.array_equal(p[s], params[s] * decay)
+
+
+def test_nan_gradient_propagates_only_to_its_problem(lib):
+    wl = W.custom_workload([(128, 256, 0), (128, 256, 0)], grad_dtype="bf16", wid=109)
+    params, grads, mom = W.host_inputs(wl)
+    tab = wl.table()
+    h = _hyper(lib, wl, "standard", "bf16")
+    clean = _dev_step(lib, params, grads, mom, tab, h)
+    bad = grads.copy()
+    bad[tab[0][0] + 5] = 0x7FC0                      # a bf16 quiet NaN
+    p, m, u = _dev_step(lib, params, bad, mom, tab, h)
+    s0, s1 = entry_slices(tab)
+    assert np.isnan(u[s0]).all()
+    assert np.array_equal(u[s1], clean[2][s1]) and np.array_equal(p[s1], clean[0][s1])
+
+
+def test_three_steps_and_resume(lib):
+    import torch
+    wl = W.custom_workload([(256, 512, 0), (512, 256, 0)], grad_dtype="bf16", wid=110)
+    params, grads, mom = W.host_inputs(wl)
+    tab = wl.table()
+    h = _hyper(lib, wl, "standard", "bf16")
+    three = run_step(lib, params, grads, mom, tab, h, steps=3)
+    two = run_step(lib, params, grads, mom, tab, h, steps=2)
+    resumed = run_step(lib, two["params"], grads, two["momentum"], tab, h, steps=1)
+    for k in ("params", "momentum", "update"):
+        assert np.array_equal(three[k], resumed[k])
+    # three steps against the oracle, with the same gradient each step
+    g64 = W.grad_as_f64(wl, grads)
+    P, M = params.astype(np.float64), mom.astype(np.float64)
+    for _ in range(3):
+        ref = oracle.muon_step(P, g64, M, tab, lr=wl.lr, mu=wl.momentum,
+                               weight_decay=wl.weight_decay, method="standard", store_fmt="bf16")
+        P, M = ref["params"], ref["momentum"]
+    for s in entry_slices(tab):
+        assert rel(three["momentum"][s], M[s]) <= MOM_GATE
+        assert rel(three["update"][s], ref["update"][s]) <= LP_GATE
+        assert rel(three["params"][s] - params[s], P[s] - params[s]) <= LP_GATE
+
+
+def test_unaligned_offsets_multiple_of_8(lib):
+    for gdt in ("f32", "bf16"):
+        shapes = [(40, 72, 0), (72, 40, 0), (9, 8, 0), (16, 24, 8)]
+        offs, cur = [], 8
+        for r, c, _ in shapes:
+            offs.append(cur)
+            cur += r * c + 8
+        tab = [(o, r, c, s) for o, (r, c, s) in zip(offs, shapes)]
+        rng = np.random.default_rng(5)
+        n = cur + 8
+        params = rng.standard_normal(n).astype(np.float32)
+        g = rng.standard_normal(n).astype(np.float32)
+        grads = g if gdt == "f32" else W.f32_to_bf16_bits(g)
+        mom = rng.standard_normal(n).astype(np.float32)
+        h = lib.hyper(ns_method="standard", ns_dtype="f32", grad_dtype=gdt, weight_decay=0.1)
+        p, m, u = _dev_step(lib, params, grads, mom, tab, h)
+        gd = g.astype(np.float64) if gdt == "f32" else W.bf16_bits_to_f32(grads).astype(np.float64)
+        ref = oracle.muon_step(params, gd, mom, tab, lr=0.02, mu=0.95, weight_decay=0.1,
+                               method="standard")
+        for s in entry_slices(tab):
+            assert rel(u[s], ref["update"][s]) <= FP32_GATE
+            assert rel(m[s], ref["momentum"][s]) <= MOM_GATE
+        mask = outside_mask(tab, n)
+        assert np.array_equal(p[mask], params[mask]) and np.array_equal(m[mask], mom[mask])
+
+
+def test_empty_table_and_small_workspace(lib):
+    import torch
+    dev = "cuda:0"
+    p = torch.randn(4096, device=dev)
+    g = torch.randn(4096, device=dev).to(torch.bfloat16)
+    m = torch.zeros(4096, device=dev)
+    p0 = p.clone()
+    h = lib.hyper(ns_method="standard", ns_dtype="bf16")
+    lib.step(p, g, m, [], h)
+    tab = [(0, 64, 64, 0)]
+    need = lib.workspace_size(tab, h)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device=dev)
+    with pytest.raises(lib.MuonError) as ei:
+        lib.step(p, g, m, tab, h, ws=ws)
+    assert ei.value.status == lib.ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.equal(p, p0) and not torch.any(m)
+
+
+# --------------------------------------------------------------------------- pack / unpack
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_pack_unpack_bit_exact(lib, dtype):
+    import torch
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    dev = "cuda:0"
+    shapes = [(3, 5), (64, 64), (1, 7), (100, 33), (2, 2)]
+    offs, cur = [], 0
+    for r, c in shapes:
+        cur = (cur + 7) // 8 * 8
+        offs.append(cur)
+        cur += r * c
+    n = cur + 13
+    tab = [(o, r, c, 0) for o, (r, c) in zip(offs, shapes)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    mats = [torch.randn(r, c, device=dev, generator=gen).to(tdt) for r, c in shapes]
+    sentinel = torch.full((n,), -7.25, device=dev).to(tdt)
+    packed = sentinel.clone()
+    lib.pack(packed, mats, tab)
+    outs = [torch.zeros_like(t) for t in mats]
+    lib.unpack(outs, packed, tab)
+    torch.cuda.synchronize()
+    for a, b, (o, r, c, _) in zip(outs, mats, tab):
+        assert torch.equal(a.view(torch.int16 if dtype != "f32" else torch.int32),
+                           b.view(torch.int16 if dtype != "f32" else torch.int32))
+        assert torch.equal(packed[o:o + r * c], b.reshape(-1))
+    mask = torch.ones(n, dtype=torch.bool, device=dev)
+    for o, r, c, _ in tab:
+        mask[o:o + r * c] = False
+    assert torch.equal(packed[mask], sentinel[mask])
+
+
+# --------------------------------------------------------------------------- AdamW
+
+@pytest.mark.parametrize("gdt", ["bf16", "f32"])
+def test_adamw_against_oracle(lib, gdt):
+    import torch
+    dev = "cuda:0"
+    n = 1_000_003                                   # ragged tail (n % 8 != 0)
+    p0, gb, m0, v0 = W.adamw_inputs(n, seed=1)
+    g32 = W.bf16_bits_to_f32(gb)
+    grads_host = gb if gdt == "bf16" else g32
+    lr, b1, b2, eps, wd = 3e-4, 0.9, 0.95, 1e-8, 0.1
+    p, m, v = (torch.from_numpy(a.copy()).to(dev) for a in (p0, m0, v0))
+    g = to_device(grads_host, dev, torch)
+    P, M, V = p0.astype(np.float64), m0.astype(np.float64), v0.astype(np.float64)
+    for t in (1, 2, 3):
+        lib.adamw(p, g, m, v, lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, step=t)
+        P, M, V = oracle.adamw_step(P, g32, M, V, lr, b1, b2, eps, wd, t)
+    torch.cuda.synchronize()
+    pg, mg, vg = p.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy()
+    assert rel(mg, M) <= MOM_GATE and rel(vg, V) <= MOM_GATE
+    bound = 2 * np.spacing(np.abs(P).astype(np.float32)).astype(np.float64) + 1e-4 * np.abs(P - p0)
+    assert np.all(np.abs(pg - P) <= bound)
+    assert rel(pg - p0, P - p0) <= 1e-3
+
+
+def test_adamw_first_step_closed_form(lib):
+    import torch
+    dev = "cuda:0"
+    n = 4099
+    rng = np.random.default_rng(3)
+    p0 = rng.standard_normal(n).astype(np.float32)
+    g = rng.standard_normal(n).astype(np.float32)
+    g[:17] = 0.0
+    p = torch.from_numpy(p0.copy()).to(dev)
+    lib.adamw(p, torch.from_numpy(g).to(dev), torch.zeros(n, device=dev), torch.zeros(n, device=dev),
+              lr=3e-4, eps=1e-8, weight_decay=0.1, step=1)
+    torch.cuda.synchronize()
+    out = p.cpu().numpy()
+    decay = np.float32(1.0 - np.float64(np.float32(3e-4)) * np.float64(np.float32(0.1)))
+    assert np.array_equal(out[:17], p0[:17] * decay)            # zero gradient: decay only
+    expect = p0.astype(np.float64) * (1 - 3e-5) - 3e-4 * g / (np.abs(g) + 1e-8)
+    assert np.max(np.abs(out - expect)) < 4e-7

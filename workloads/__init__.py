@@ -56,6 +56,13 @@ class Workload:
     momentum: float = 0.95
     weight_decay: float = 0.1
     adamw_sizes: Tuple[int, ...] = ()   # element counts of the non-2D / AdamW tensors
+    grad_kind: str = ""        # "gaussian" | "lowrank"; "" = gaussian for f32, lowrank otherwise
+
+    @property
+    def kind(self) -> str:
+        if self.grad_kind:
+            return self.grad_kind
+        return "gaussian" if self.grad_dtype == "f32" else "lowrank"
 
     @property
     def offsets(self) -> List[int]:
@@ -136,10 +143,12 @@ def workload(wid: int) -> Workload:
 
 def custom_workload(shapes: Sequence[Tuple[int, int, int]], grad_dtype: str = "bf16",
                     ns_dtype: str = "bf16", wid: int = 100, lr: float = 0.02,
-                    momentum: float = 0.95, weight_decay: float = 0.1) -> Workload:
+                    momentum: float = 0.95, weight_decay: float = 0.1,
+                    grad_kind: str = "") -> Workload:
     """A workload from explicit (rows, cols, split_rows) triples (used for ragged cases)."""
     ents = tuple(Entry(f"m{i}", r, c, s) for i, (r, c, s) in enumerate(shapes))
-    return Workload(wid, "custom", ents, grad_dtype, ns_dtype, lr, momentum, weight_decay)
+    return Workload(wid, "custom", ents, grad_dtype, ns_dtype, lr, momentum, weight_decay,
+                    grad_kind=grad_kind)
 
 
 # ----------------------------------------------------------------------------
@@ -171,17 +180,18 @@ def entry_values(wl: Workload, index: int) -> Tuple[np.ndarray, np.ndarray]:
     uint16), param float32; both shaped (rows, cols)."""
     e = wl.entries[index]
     rng = entry_rng(wl.wid, index)
-    if wl.grad_dtype == "f32":
+    if wl.kind == "gaussian":
         g = rng.standard_normal((e.rows, e.cols)).astype(np.float32)
         p = rng.standard_normal((e.rows, e.cols)).astype(np.float32)
-        return g, p
+        return (g if wl.grad_dtype == "f32" else f32_to_bf16_bits(g)), p
     r = 16
     u = rng.standard_normal((e.rows, r))
     v = rng.standard_normal((e.cols, r))
     noise = rng.standard_normal((e.rows, e.cols))
     g64 = (1e-3 / np.sqrt(r)) * (u @ v.T) + 1e-5 * noise
     p = rng.standard_normal((e.rows, e.cols)).astype(np.float32)
-    return f32_to_bf16_bits(g64.astype(np.float32)), p
+    g32 = g64.astype(np.float32)
+    return (g32 if wl.grad_dtype == "f32" else f32_to_bf16_bits(g32)), p
 
 
 def grad_as_f64(wl: Workload, g: np.ndarray) -> np.ndarray:
