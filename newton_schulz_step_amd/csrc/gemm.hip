@@ -15,7 +15,8 @@
 // from global memory to LDS (global_load_lds_dwordx4) into a double buffer;
 // rows are 128 bytes, with the 16-byte chunk index XOR-swizzled by the row so
 // that the MFMA operand reads (ds_read_b128, 32 rows at one chunk) spread over
-// all banks. One barrier per K slice.
+// all banks. MFMA operands are double-buffered in registers so that reads of
+// the next sub-step overlap the current MFMAs; one barrier per K slice.
 //
 // Epilogue: each wave stages 32 rows of its fp32 accumulators in LDS, applies
 //   v = alpha * acc + beta * D[i][j] + gamma * [i == j]
@@ -24,6 +25,7 @@
 // (on diagonal tiles each element is written exactly once, so the stored matrix
 // is exactly symmetric). The apply epilogue instead finishes the Muon step,
 // p <- p * decay - lr * v, at the matrix's stored (possibly transposed) position.
+// Global loads of the epilogue (D, params) are issued in batches ahead of use.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,18 +34,21 @@ namespace muon {
 template <typename T> struct Mfma;
 template <> struct Mfma<__bf16> {
   using V = bf16x8;
+  static constexpr int kInstr = 1;
   static __device__ __forceinline__ void run(const V& a, const V& b, f32x16& c) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
 };
 template <> struct Mfma<_Float16> {
   using V = f16x8;
+  static constexpr int kInstr = 1;
   static __device__ __forceinline__ void run(const V& a, const V& b, f32x16& c) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
 };
 template <> struct Mfma<float> {
   using V = f32x4;
+  static constexpr int kInstr = 4;
   static __device__ __forceinline__ void run(const V& a, const V& b, f32x16& c) {
     // a 16-byte chunk holds 4 consecutive k; lanes 0-31 and 32-63 hold adjacent chunks
 #pragma unroll
@@ -93,28 +98,23 @@ template <typename T> __device__ __forceinline__ void st8(T* p, const T (&v)[8])
   }
 }
 
-template <typename T, int TILE, bool SYM, int EPI>
-__global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
-  constexpr int ESZ = sizeof(T);
-  constexpr int HALF = TILE / 2;          // wave tile edge
-  constexpr int WB = HALF / 32;           // 32x32 blocks per wave edge
-  constexpr int OPB = TILE * 128;         // bytes of one operand slice
-  constexpr int LOADS = TILE / 32;        // 1-KB direct loads per wave per operand
-  constexpr int SP = HALF + 4;            // staging row pitch (floats)
+// Tile geometry shared by the main loops and the epilogue.
+template <typename T, int TILE> struct Geo {
+  static constexpr int ESZ = sizeof(T);
+  static constexpr int HALF = TILE / 2;          // wave tile edge (2 x 2 waves)
+  static constexpr int WB = HALF / 32;           // 32x32 blocks per wave edge
+  static constexpr int OPB = TILE * 128;         // bytes of one operand slice
+  static constexpr int LOADS = TILE / 32;        // 1-KB direct loads per wave per operand
+  static constexpr int SP = HALF + 4;            // staging row pitch (floats)
   using V = typename Mfma<T>::V;
+};
 
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // ---- tile decode
+// Logical tile (problem, tile row, tile column) of this workgroup.
+template <bool SYM>
+__device__ __forceinline__ void decode_tile(const GemmArgs& a, int& prob, int& ti, int& tj) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int prob = bid / a.tiles_per_problem;
+  prob = bid / a.tiles_per_problem;
   const int t = bid - prob * a.tiles_per_problem;
-  int ti, tj;
   if constexpr (SYM) {
     ti = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
     while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
@@ -130,6 +130,29 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
     ti = first + w % gsz;
     tj = w / gsz;
   }
+}
+
+// Main loop: acc[i][j] += P[tile rows] Q[tile cols]^T over the whole K range.
+//
+// K advances in 128-byte slices through two LDS buffers. Each slice has four
+// sub-steps (one per 16-byte chunk pair); the MFMA operands of sub-step s + 1 are
+// read from LDS while the MFMAs of sub-step s run (two register sets). Every
+// sub-step is its own scheduling region, so no MFMA waits for a read issued in
+// its own region. One barrier per slice, before the last sub-step: it publishes
+// the next slice (every wave has waited for its own direct loads) and frees the
+// current buffer, into which the load of slice min(kt + 2, nk - 1) then starts.
+// On the last two slices those loads are redundant (in bounds, never read), and
+// the loop drains them before the epilogue reuses the LDS.
+template <typename T, int TILE>
+__device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, int tj, char* lds0, char* lds1,
+                                         f32x16 (&acc)[Geo<T, TILE>::WB][Geo<T, TILE>::WB]) {
+  using Gm = Geo<T, TILE>;
+  constexpr int ESZ = Gm::ESZ, HALF = Gm::HALF, WB = Gm::WB, OPB = Gm::OPB, LOADS = Gm::LOADS;
+  constexpr int NMF = WB * WB * Mfma<T>::kInstr;    // MFMA instructions per sub-step
+  using V = typename Gm::V;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
 
   // ---- per-lane direct-load offsets (bytes, relative to the tile's first row)
   const char* Pb = static_cast<const char*>(a.P) +
@@ -144,7 +167,6 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
     poff[it] = static_cast<int64_t>(r) * a.ldp * ESZ + c * 16;
     qoff[it] = static_cast<int64_t>(r) * a.ldq * ESZ + c * 16;
   }
-
   auto issue = [&](char* st, int kt) {
     const int64_t kb = static_cast<int64_t>(kt) * 128;
 #pragma unroll
@@ -171,7 +193,6 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
     }
   }
 
-  f32x16 acc[WB][WB];
 #pragma unroll
   for (int i = 0; i < WB; ++i)
 #pragma unroll
@@ -179,29 +200,149 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = a.K / (128 / ESZ);
-  issue(lds0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = (kt & 1) ? lds1 : lds0;
-    char* nxt = (kt & 1) ? lds0 : lds1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  V fa0[WB], fb0[WB], fa1[WB], fb1[WB];
+  auto rd = [&](V (&xa)[WB], V (&xb)[WB], const char* buf, int ks) {
+#pragma unroll
+    for (int i = 0; i < WB; ++i) xa[i] = *reinterpret_cast<const V*>(buf + aoff[i][ks]);
+#pragma unroll
+    for (int j = 0; j < WB; ++j) xb[j] = *reinterpret_cast<const V*>(buf + OPB + boff[j][ks]);
+  };
+  auto mm = [&](V (&xa)[WB], V (&xb)[WB]) {
+#pragma unroll
+    for (int i = 0; i < WB; ++i)
+#pragma unroll
+      for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], acc[i][j]);
+  };
+  // scheduling: 2 WB operand reads spread over the sub-step's MFMAs, then a fence
+  auto region = [&]() {
+#pragma unroll
+    for (int q = 0; q < 2 * WB; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF / (2 * WB), 0);    // MFMAs
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int nk = a.K / (128 / ESZ);   // even: K is a multiple of the tile edge
+  auto slice = [&](char* cur, char* nxt, int kt) {
+    rd(fa1, fb1, cur, 1);
+    mm(fa0, fb0);
+    region();
+    rd(fa0, fb0, cur, 2);
+    mm(fa1, fb1);
+    region();
+    rd(fa1, fb1, cur, 3);
+    mm(fa0, fb0);
+    region();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 1 < nk) issue(nxt, kt + 1);
+    rd(fa0, fb0, nxt, 0);
+    issue(cur, min(kt + 2, nk - 1));
+    mm(fa1, fb1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      V af[WB], bf[WB];
+    for (int q = 0; q < 2 * WB; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
 #pragma unroll
-      for (int i = 0; i < WB; ++i) af[i] = *reinterpret_cast<const V*>(cur + aoff[i][ks]);
+    for (int q = 0; q < 2 * LOADS; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);                 // one direct load
+      if (q & 1) __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  issue(lds0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  rd(fa0, fb0, lds0, 0);
+  issue(lds1, 1);
+  for (int kt = 0; kt < nk; kt += 2) {
+    slice(lds0, lds1, kt);
+    slice(lds1, lds0, kt + 1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// 8 consecutive elements of T held raw in registers (one or two 16-byte vectors).
+template <typename T> struct Pack8 {
+  u16x8 u;
+  __device__ __forceinline__ void load(const T* p) { u = *reinterpret_cast<const u16x8*>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    return static_cast<float>(__builtin_bit_cast(T, static_cast<unsigned short>(u[e])));
+  }
+};
+template <> struct Pack8<float> {
+  f32x4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+    lo = q[0];
+    hi = q[1];
+  }
+  __device__ __forceinline__ float get(int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
+};
+
+// p <- p * decay - lr * v for 8 consecutive stored elements starting at idx, with
+// optional copies of v (update_out) and of the new p rounded to bf16 (shadow).
+// `cnt` < 8 elements (ragged edge) or an unaligned idx take the scalar path.
+__device__ __forceinline__ void apply8(const GemmArgs& a, int64_t idx, int cnt, const float (&v)[8],
+                                       const f32x4& p0, const f32x4& p1, bool vec) {
+  if (vec) {
+    f32x4 o0, o1;
 #pragma unroll
-      for (int j = 0; j < WB; ++j) bf[j] = *reinterpret_cast<const V*>(cur + OPB + boff[j][ks]);
+    for (int e = 0; e < 4; ++e) {
+      o0[e] = p0[e] * a.decay - a.lr * v[e];
+      o1[e] = p1[e] * a.decay - a.lr * v[e + 4];
+    }
+    f32x4* pp = reinterpret_cast<f32x4*>(a.params + idx);
+    pp[0] = o0;
+    pp[1] = o1;
+    if (a.update_out) {
+      f32x4 u0, u1;
 #pragma unroll
-      for (int i = 0; i < WB; ++i)
+      for (int e = 0; e < 4; ++e) { u0[e] = v[e]; u1[e] = v[e + 4]; }
+      f32x4* up = reinterpret_cast<f32x4*>(a.update_out + idx);
+      up[0] = u0;
+      up[1] = u1;
+    }
+    if (a.shadow) {
+      u16x8 sh;
 #pragma unroll
-        for (int j = 0; j < WB; ++j) Mfma<T>::run(af[i], bf[j], acc[i][j]);
+      for (int e = 0; e < 4; ++e) { sh[e] = bf16_bits(o0[e]); sh[e + 4] = bf16_bits(o1[e]); }
+      *reinterpret_cast<u16x8*>(a.shadow + idx) = sh;
+    }
+  } else {
+    for (int e = 0; e < cnt; ++e) {
+      const float pn = a.params[idx + e] * a.decay - a.lr * v[e];
+      a.params[idx + e] = pn;
+      if (a.update_out) a.update_out[idx + e] = v[e];
+      if (a.shadow) a.shadow[idx + e] = bf16_bits(pn);
     }
   }
+}
 
-  // ---- epilogue
+// Epilogue: v = alpha acc + beta D + gamma I, stored (or applied) as the launch asks.
+// Per wave and per 32-row block i: the accumulators are staged in LDS; a row pass
+// gives each lane 8 consecutive columns of several rows (row-major store, or the
+// apply of a matrix stored as is), a column pass 8 consecutive rows of one column
+// (transposed store, or the apply of a transposed matrix). Every global load of a
+// pass (D, params) is issued before any of them is used, and D of block i + 1 is
+// requested as soon as block i has consumed its own, so each pass waits for memory
+// at most once.
+template <typename T, int TILE, bool SYM, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, int tj, char* lds0, char* lds1,
+                                         f32x16 (&acc)[Geo<T, TILE>::WB][Geo<T, TILE>::WB]) {
+  using Gm = Geo<T, TILE>;
+  constexpr int HALF = Gm::HALF, WB = Gm::WB, SP = Gm::SP;
+  constexpr int CPR = HALF / 8;          // 8-column chunks per staged row
+  constexpr int NR = 32 * CPR / 64;      // row-pass tasks per lane
+  constexpr int NC = HALF * 4 / 64;      // column-pass tasks per lane
+  constexpr int PB = NR < 4 ? NR : 4;    // apply: chunks whose parameters are loaded together
+  static_assert(NR % PB == 0 && NC % PB == 0, "apply batches");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
   float* stg = reinterpret_cast<float*>((wave < 2 ? lds0 : lds1) + (wave & 1) * 32 * SP * 4);
   const int gi_w = ti * TILE + wm * HALF;   // first row of this wave's outputs
   const int gj_w = tj * TILE + wn * HALF;   // first column
@@ -214,11 +355,25 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
     transposed = pd.transposed;
     src = pd.src_off;
   }
+  const int m = a.m_valid, n = a.n_valid;
 
   T* C = static_cast<T*>(a.C);
   T* Ct = static_cast<T*>(a.Ct);
   const T* D = static_cast<const T*>(a.D);
   const bool need_col = (EPI == EPI_APPLY) ? (transposed != 0) : (Ct != nullptr);
+
+  Pack8<T> dq[NR];
+  auto load_d = [&](int i) {
+    if (D == nullptr) return;
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      const int q = lane + 64 * t;
+      const int gi = gi_w + i * 32 + q / CPR;
+      const int gj = gj_w + (q % CPR) * 8;
+      dq[t].load(D + static_cast<int64_t>(prob) * a.d_ps + static_cast<int64_t>(gi) * a.ldd + gj);
+    }
+  };
+  load_d(0);
 
 #pragma unroll
   for (int i = 0; i < WB; ++i) {
@@ -230,72 +385,34 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
         stg[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * SP + j * 32 + (lane & 31)] = acc[i][j][r];
     __syncthreads();
 
-    // row pass: 8 consecutive columns per task
-    constexpr int CPR = HALF / 8;            // chunks per row
-#pragma unroll 2
-    for (int q = lane; q < 32 * CPR; q += 64) {
-      const int rr = q / CPR;
-      const int cc = (q - rr * CPR) * 8;
-      const int gi = gi_w + i * 32 + rr;
-      const int gj = gj_w + cc;
+    constexpr bool APPLY = (EPI == EPI_APPLY);
+
+    // ---- row pass: each lane finishes one 8-column chunk at a time
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      const int q = lane + 64 * t;
+      const int rr = q / CPR, cc = (q % CPR) * 8;
+      const int gi = gi_w + i * 32 + rr, gj = gj_w + cc;
       float v[8];
       const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + rr * SP + cc);
       const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + rr * SP + cc + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) { v[e] = a.alpha * s0[e]; v[e + 4] = a.alpha * s1[e]; }
       if (D != nullptr) {
-        float d[8];
-        ld8<T>(D + static_cast<int64_t>(prob) * a.d_ps + static_cast<int64_t>(gi) * a.ldd + gj, d);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += a.beta * d[e];
+        for (int e = 0; e < 8; ++e) v[e] += a.beta * dq[t].get(e);
       }
       if (a.gamma != 0.0f) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (gi == gj + e) v[e] += a.gamma;
       }
-      if constexpr (EPI == EPI_APPLY) {
-        if (!transposed) {
-          const int m = a.m_valid, n = a.n_valid;
-          if (gi < m && gj < n) {
-            const int64_t idx = src + static_cast<int64_t>(gi) * n + gj;
-            if (gj + 8 <= n && (idx & 7) == 0) {
-              f32x4* pp = reinterpret_cast<f32x4*>(a.params + idx);
-              f32x4 p0 = pp[0], p1 = pp[1];
-              f32x4 o0, o1;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                o0[e] = p0[e] * a.decay - a.lr * v[e];
-                o1[e] = p1[e] * a.decay - a.lr * v[e + 4];
-              }
-              pp[0] = o0; pp[1] = o1;
-              if (a.update_out) {
-                f32x4 u0, u1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { u0[e] = v[e]; u1[e] = v[e + 4]; }
-                f32x4* up = reinterpret_cast<f32x4*>(a.update_out + idx);
-                up[0] = u0; up[1] = u1;
-              }
-              if (a.shadow) {
-                u16x8 sh;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { sh[e] = bf16_bits(o0[e]); sh[e + 4] = bf16_bits(o1[e]); }
-                *reinterpret_cast<u16x8*>(a.shadow + idx) = sh;
-              }
-            } else {
-              for (int e = 0; e < 8 && gj + e < n; ++e) {
-                const float pn = a.params[idx + e] * a.decay - a.lr * v[e];
-                a.params[idx + e] = pn;
-                if (a.update_out) a.update_out[idx + e] = v[e];
-                if (a.shadow) a.shadow[idx + e] = bf16_bits(pn);
-              }
-            }
-          }
-        } else {
-          float4* sp = reinterpret_cast<float4*>(stg + rr * SP + cc);
-          sp[0] = make_float4(v[0], v[1], v[2], v[3]);
-          sp[1] = make_float4(v[4], v[5], v[6], v[7]);
-        }
+      float4* sp = reinterpret_cast<float4*>(stg + rr * SP + cc);
+      if constexpr (APPLY) {
+        // the value itself goes back to the staging area (for the apply below,
+        // or for the column pass of a transposed matrix)
+        sp[0] = make_float4(v[0], v[1], v[2], v[3]);
+        sp[1] = make_float4(v[4], v[5], v[6], v[7]);
       } else {
         T o[8];
 #pragma unroll
@@ -310,66 +427,94 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
           }
         }
         if (need_col) {
-          float4* sp = reinterpret_cast<float4*>(stg + rr * SP + cc);
           sp[0] = make_float4(to_f32(o[0]), to_f32(o[1]), to_f32(o[2]), to_f32(o[3]));
           sp[1] = make_float4(to_f32(o[4]), to_f32(o[5]), to_f32(o[6]), to_f32(o[7]));
         }
       }
     }
+    if (!(APPLY && !transposed) && i + 1 < WB) load_d(i + 1);
 
+    if (APPLY && !transposed) {
+      // stored m x n: canonical (gi, gj) at src + gi * n + gj. Each lane reads back
+      // the chunks it wrote; parameters are loaded PB chunks at a time, all of a
+      // batch before any is used.
+#pragma unroll
+      for (int b = 0; b < NR; b += PB) {
+        f32x4 p0[PB], p1[PB];
+        bool pvec[PB];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+          const int q = lane + 64 * (b + u);
+          const int gi = gi_w + i * 32 + q / CPR, gj = gj_w + (q % CPR) * 8;
+          const int64_t idx = src + static_cast<int64_t>(gi) * n + gj;
+          pvec[u] = gi < m && gj + 8 <= n && (idx & 7) == 0;
+          if (pvec[u]) {
+            const f32x4* pp = reinterpret_cast<const f32x4*>(a.params + idx);
+            p0[u] = pp[0];
+            p1[u] = pp[1];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+          const int q = lane + 64 * (b + u);
+          const int rr = q / CPR, cc = (q % CPR) * 8;
+          const int gi = gi_w + i * 32 + rr, gj = gj_w + cc;
+          if (gi < m && gj < n) {
+            float v[8];
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + rr * SP + cc);
+            const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + rr * SP + cc + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { v[e] = s0[e]; v[e + 4] = s1[e]; }
+            apply8(a, src + static_cast<int64_t>(gi) * n + gj, min(8, n - gj), v, p0[u], p1[u], pvec[u]);
+          }
+        }
+      }
+      if (i + 1 < WB) load_d(i + 1);
+    }
+
+    // ---- column pass
     if (need_col) {
       __syncthreads();
-      // column pass: 8 consecutive rows of one column per task
-#pragma unroll 2
-      for (int q = lane; q < HALF * 4; q += 64) {
-        const int r8 = (q & 3) * 8;
-        const int cc = q >> 2;
-        const int gi = gi_w + i * 32 + r8;
-        const int gj = gj_w + cc;
-        float v[8];
+      if constexpr (APPLY) {
+        // stored n x m: canonical (gi, gj) at src + gj * m + gi
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = stg[(r8 + e) * SP + cc];
-        if constexpr (EPI == EPI_APPLY) {
-          // stored n x m (rows > cols): element (gi, gj) of the canonical matrix is at gj * m + gi
-          const int m = a.m_valid, n = a.n_valid;
-          if (gj < n && gi < m) {
+        for (int b = 0; b < NC; b += PB) {
+          f32x4 c0[PB], c1[PB];
+          bool cvec[PB];
+#pragma unroll
+          for (int u = 0; u < PB; ++u) {
+            const int q = lane + 64 * (b + u);
+            const int gi = gi_w + i * 32 + (q & 3) * 8, gj = gj_w + (q >> 2);
             const int64_t idx = src + static_cast<int64_t>(gj) * m + gi;
-            if (gi + 8 <= m && (idx & 7) == 0) {
-              f32x4* pp = reinterpret_cast<f32x4*>(a.params + idx);
-              f32x4 p0 = pp[0], p1 = pp[1];
-              f32x4 o0, o1;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                o0[e] = p0[e] * a.decay - a.lr * v[e];
-                o1[e] = p1[e] * a.decay - a.lr * v[e + 4];
-              }
-              pp[0] = o0; pp[1] = o1;
-              if (a.update_out) {
-                f32x4 u0, u1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { u0[e] = v[e]; u1[e] = v[e + 4]; }
-                f32x4* up = reinterpret_cast<f32x4*>(a.update_out + idx);
-                up[0] = u0; up[1] = u1;
-              }
-              if (a.shadow) {
-                u16x8 sh;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { sh[e] = bf16_bits(o0[e]); sh[e + 4] = bf16_bits(o1[e]); }
-                *reinterpret_cast<u16x8*>(a.shadow + idx) = sh;
-              }
-            } else {
-              for (int e = 0; e < 8 && gi + e < m; ++e) {
-                const float pn = a.params[idx + e] * a.decay - a.lr * v[e];
-                a.params[idx + e] = pn;
-                if (a.update_out) a.update_out[idx + e] = v[e];
-                if (a.shadow) a.shadow[idx + e] = bf16_bits(pn);
-              }
+            cvec[u] = gj < n && gi + 8 <= m && (idx & 7) == 0;
+            if (cvec[u]) {
+              const f32x4* pp = reinterpret_cast<const f32x4*>(a.params + idx);
+              c0[u] = pp[0];
+              c1[u] = pp[1];
             }
           }
-        } else {
+#pragma unroll
+          for (int u = 0; u < PB; ++u) {
+            const int q = lane + 64 * (b + u);
+            const int r8 = (q & 3) * 8, cc = q >> 2;
+            const int gi = gi_w + i * 32 + r8, gj = gj_w + cc;
+            if (gj < n && gi < m) {
+              float w[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) w[e] = stg[(r8 + e) * SP + cc];
+              apply8(a, src + static_cast<int64_t>(gj) * m + gi, min(8, m - gi), w, c0[u], c1[u], cvec[u]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NC; ++t) {
+          const int q = lane + 64 * t;
+          const int r8 = (q & 3) * 8, cc = q >> 2;
+          const int gi = gi_w + i * 32 + r8, gj = gj_w + cc;
           T o[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(v[e]);
+          for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(stg[(r8 + e) * SP + cc]);
           T* cp = Ct + static_cast<int64_t>(prob) * a.ct_ps + static_cast<int64_t>(gj) * a.ldct + gi;
           if (!diag || gi > gj) {
             st8<T>(cp, o);
@@ -383,12 +528,26 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
   }
 }
 
+template <typename T, int TILE, bool SYM, int EPI>
+__global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
+  using Gm = Geo<T, TILE>;
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * Gm::OPB];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * Gm::OPB];
+  int prob, ti, tj;
+  decode_tile<SYM>(a, prob, ti, tj);
+  f32x16 acc[Gm::WB][Gm::WB];
+  mainloop<T, TILE>(a, prob, ti, tj, lds0, lds1, acc);
+  epilogue<T, TILE, SYM, EPI>(a, prob, ti, tj, lds0, lds1, acc);
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 
 template <typename T, int TILE, bool SYM, int EPI>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
   if (a.total_tiles <= 0) return hipSuccess;
+  // the main loop runs whole pairs of 128-byte K slices
+  if (a.K <= 0 || a.K % (2 * 128 / static_cast<int>(sizeof(T))) != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((ns_gemm<T, TILE, SYM, EPI>), dim3(a.total_tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
