@@ -16,6 +16,7 @@ bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload 3]
                     [--method standard|gram] [--no-cpu-baseline]
+    python bench.py --copy-calibration   # plain copy of known size (counter scale)
 """
 from __future__ import annotations
 
@@ -138,6 +139,58 @@ def cpu_baseline(wl, method, budget_s=25.0):
                        f"by nominal NS FLOPs to {est_step_s:.1f} s")}
 
 
+def copy_calibration(nbytes: int = 1 << 32) -> dict:
+    """One plain device copy of `nbytes` through the library's copy kernel
+    (muon_pack with a single entry): the known-size reference that scales the
+    FETCH_SIZE / WRITE_SIZE counters, and the copy bandwidth of this GPU."""
+    import torch
+    import newton_schulz_step_amd as nss
+    nss.load()
+    dev = torch.device("cuda:0")
+    n = nbytes // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.zeros(n, device=dev)
+    cols = 65536
+    tab = [(0, n // cols, cols, 0)]          # one entry covering the whole buffer
+    for _ in range(2):
+        nss.pack(dst, [src], tab)
+    torch.cuda.synchronize()
+    reps = 5
+    nss.profile_begin()
+    for _ in range(reps):
+        nss.pack(dst, [src], tab)
+    torch.cuda.synchronize()
+    launches, ms = nss.profile_end()["copy_batch"]
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": launches,
+            "avg_launch_ms": ms / launches, "copy_gbs": 2 * nbytes * launches / (ms * 1e-3) / 1e9}
+
+
+def adamw_pass(wl, steps: int = 10) -> dict:
+    """AdamW over the workload's non-2D tensors (one flat buffer), bf16 grads:
+    26 algorithmic bytes per element (p, m, v read and written, g read)."""
+    import torch
+    import newton_schulz_step_amd as nss
+    n = sum(wl.adamw_sizes)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    p = torch.randn(n, device=dev, generator=gen)
+    g = torch.randn(n, device=dev, generator=gen).to(torch.bfloat16)
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    kw = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    nss.adamw(p, g, m, v, step=1, **kw)
+    torch.cuda.synchronize()
+    nss.profile_begin()
+    for t in range(steps):
+        nss.adamw(p, g, m, v, step=t + 2, **kw)
+    torch.cuda.synchronize()
+    launches, ms = nss.profile_end()["adamw"]
+    gbs = 26.0 * n * launches / (ms * 1e-3) / 1e9
+    return {"elements": n, "launches": launches, "avg_launch_ms": ms / launches, "gbs": gbs,
+            "frac_of_hbm": gbs / HBM_PEAK_GBS}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +199,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--method", default="standard", choices=["standard", "gram"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -160,6 +214,9 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     nss.load()
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration()), flush=True)
+        return 0
     dev = torch.device("cuda:0")
     wl = W.workload(args.workload)
     ns_dtype = "bf16" if args.method == "standard" else "f16"
@@ -254,6 +311,8 @@ def main() -> int:
     }
     del params, grads, mom, ws
     torch.cuda.empty_cache()
+    out["adamw_pass"] = adamw_pass(W.workload(5))
+    out["adamw_pass"]["workload"] = "32000x4096 embedding + 65 vectors of 4096 (per-head workload's AdamW part)"
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.method)
     print(json.dumps(out), flush=True)

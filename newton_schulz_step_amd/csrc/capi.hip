@@ -201,6 +201,7 @@ static void set_sym(GemmArgs& g, const Group& G, const void* P, const void* Q, i
   g.total_tiles = g.tiles_per_problem * G.count;
   g.C = C; g.c_ps = G.mp * G.mp; g.ldc = static_cast<int32_t>(G.mp);
   g.Ct = C; g.ct_ps = G.mp * G.mp; g.ldct = static_cast<int32_t>(G.mp);
+  g.group_m = -1;   // tiles column by column, each XCD on every eighth tile row
 }
 
 static void set_full(GemmArgs& g, const Group& G, const void* P, int64_t p_ps, int64_t ldp, const void* Q,
@@ -212,6 +213,7 @@ static void set_full(GemmArgs& g, const Group& G, const void* P, int64_t p_ps, i
   g.tiles_n = static_cast<int32_t>(cols / G.tile);
   g.tiles_per_problem = g.tiles_m * g.tiles_n;
   g.total_tiles = g.tiles_per_problem * G.count;
+  g.group_m = -1;   // tiles column by column, each XCD on every eighth tile row
 }
 
 // X0 (and its transpose) of every problem of the group.

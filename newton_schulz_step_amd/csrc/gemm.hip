@@ -112,6 +112,34 @@ template <typename T, int TILE> struct Geo {
 // Logical tile (problem, tile row, tile column) of this workgroup.
 template <bool SYM>
 __device__ __forceinline__ void decode_tile(const GemmArgs& a, int& prob, int& ti, int& tj) {
+  if (SYM && a.group_m < 0) {
+    // lower triangle column by column (tj = 0: rows 0..T-1, tj = 1: rows 1..T-1,
+    // ...), no XCD remap
+    const int b = blockIdx.x;
+    prob = b / a.tiles_per_problem;
+    int t = b - prob * a.tiles_per_problem;
+    const int T = a.tiles_m;
+    int c = 0;
+    while (t >= T - c) {
+      t -= T - c;
+      ++c;
+    }
+    tj = c;
+    ti = c + t;
+    return;
+  }
+  if (!SYM && a.group_m < 0) {
+    // column-major within a problem, no XCD remap: the workgroups running at
+    // one time cover whole tile columns of one problem; XCD x (workgroups are
+    // dealt round-robin) takes tile rows x, x + 8, ... of every column, so each
+    // Q strip is fetched from HBM once and shared through the last-level cache
+    const int b = blockIdx.x;
+    prob = b / a.tiles_per_problem;
+    const int t = b - prob * a.tiles_per_problem;
+    tj = t / a.tiles_m;
+    ti = t - tj * a.tiles_m;
+    return;
+  }
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   prob = bid / a.tiles_per_problem;
   const int t = bid - prob * a.tiles_per_problem;
@@ -121,7 +149,9 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int& prob, int& t
     while (ti * (ti + 1) / 2 > t) --ti;
     tj = t - ti * (ti + 1) / 2;
   } else {
-    constexpr int G = 4;
+    // groups of G tile rows, walked column by column, so that the P strips of
+    // a group and each Q strip are read while they are still cached
+    const int G = a.group_m > 0 ? a.group_m : 4;
     const int per_group = G * a.tiles_n;
     const int g = t / per_group;
     const int first = g * G;

@@ -17,6 +17,7 @@ struct GemmArgs {
   const void* Q; int64_t q_ps; int32_t ldq;
   int32_t K;
   int32_t tiles_m, tiles_n, tiles_per_problem, total_tiles;
+  int32_t group_m;                               // tile order: > 0 rows per group, 0 = 4, < 0 column-major
   float alpha, beta, gamma;
   const void* D; int64_t d_ps; int32_t ldd;      // optional (beta term)
   void* C; int64_t c_ps; int32_t ldc;            // optional row-major store
