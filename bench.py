@@ -85,16 +85,53 @@ def gemm_source_hash() -> str:
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: int):
+WORKLOAD_SLUG = {1: "tiny_fp32", 2: "one_layer", 3: "owner_share_7b", 4: "moe_experts",
+                 5: "per_head_split"}
+
+
+def traffic_path(workload: int, method: str) -> str:
+    return os.path.join(ROOT, "profiles",
+                        f"traffic_ns_gemm_update_{WORKLOAD_SLUG[workload]}_{method}.json")
+
+
+def measured_traffic(kernel: str, workload: int, method: str):
     """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, or
     None when there are none or the kernel source changed since they were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_ns_gemm_update_w{workload}.json")
+    path = traffic_path(workload, method)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel") != kernel or rec.get("gemm_sha256_16") != gemm_source_hash():
+    if rec.get("kernel_symbol") is None or rec.get("gemm_sha256_16") != gemm_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("hbm_bytes_per_launch")
+
+
+def summarize_counters(fetch_csv, write_csv, fetch_copy_csv, write_copy_csv, copy_bytes,
+                       symbol, workload, method):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of `symbol`, each scaled
+    by what the same counter reads for the plain copy of `copy_bytes` bytes."""
+    import csv
+
+    def per_dispatch(path, name_part):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if name_part in r["Kernel_Name"]]
+        return sum(vals) / len(vals), len(vals)
+
+    fetch_kib, nf = per_dispatch(fetch_csv, symbol)
+    write_kib, nw = per_dispatch(write_csv, symbol)
+    cf, _ = per_dispatch(fetch_copy_csv, "copy_batch_kernel")
+    cw, _ = per_dispatch(write_copy_csv, "copy_batch_kernel")
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    rec = {"kernel_symbol": symbol, "workload": WORKLOAD_SLUG[workload], "method": method,
+           "dispatches": [nf, nw], "fetch_kib_per_dispatch": fetch_kib,
+           "write_kib_per_dispatch": write_kib, "copy_bytes": copy_bytes,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_read_bytes_per_launch": fetch_kib * 1024.0 * f_scale,
+           "hbm_write_bytes_per_launch": write_kib * 1024.0 * w_scale,
+           "gemm_sha256_16": gemm_source_hash()}
+    rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    return rec
 
 
 def cpu_baseline(wl, method, budget_s=25.0):
@@ -200,7 +237,19 @@ def main() -> int:
     ap.add_argument("--method", default="standard", choices=["standard", "gram"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                              "FETCH_COPY_CSV", "WRITE_COPY_CSV"))
     args = ap.parse_args()
+    if args.summarize_counters:
+        ns_dtype = "bf16" if args.method == "standard" else "f16"
+        symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0EEEvNS_8GemmArgsE" if ns_dtype == "bf16"
+                  else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0EEEvNS_8GemmArgsE")
+        rec = summarize_counters(*args.summarize_counters, copy_bytes=1 << 32, symbol=symbol,
+                                 workload=args.workload, method=args.method)
+        with open(traffic_path(args.workload, args.method), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "owner exchange is not part of this library", file=sys.stderr)
@@ -267,7 +316,7 @@ def main() -> int:
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
         dom_flops = sum(2.0 * m * m * n + 18.0 * m ** 3 for m, n in probs) * args.steps
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
-    traffic = measured_traffic(dom_kernel, args.workload)
+    traffic = measured_traffic(dom_kernel, args.workload, args.method)
     mom_launches, mom_ms = kstats.get("momentum_sumsq", (0, 0.0))
     gbytes = elems * (10 if wl.grad_dtype != "f32" else 12) * args.steps / 1e9
 

@@ -163,6 +163,16 @@ static float gram_scale(int64_t m) {
   return static_cast<float>(int64_t(1) << e);
 }
 
+// Contraction length of a product over a dimension of `len` valid elements: the
+// buffers are zero beyond `len` (up to the tile-padded extent), so the K loop
+// stops at the next multiple of two 128-byte slices instead of the padded extent.
+// (Gram's Q carries a on its padded diagonal, but padded and valid indices never
+// meet in one product term: the valid block of every result is unchanged.)
+static int64_t kext(int64_t len, int dtype) {
+  const int64_t q = dtype == MUON_DTYPE_F32 ? 64 : 128;
+  return (len + q - 1) / q * q;
+}
+
 struct StepCtx {
   const Plan* P;
   const muon_hyper_t* h;
@@ -242,12 +252,12 @@ static int run_standard(const StepCtx& c, const Group& G) {
   int cur = 0;
   for (int k = 0; k < c.h->ns_steps; ++k) {
     GemmArgs g1{};
-    set_sym(g1, G, X[cur], X[cur], G.np, G.np, xs, A);
+    set_sym(g1, G, X[cur], X[cur], kext(G.n, dt), G.np, xs, A);
     g1.alpha = 1.0f;
     MUON_LAUNCH("ns_gemm_xxt", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, g1, c.s));
 
     GemmArgs g2{};
-    set_sym(g2, G, A, A, G.mp, G.mp, ss, B);
+    set_sym(g2, G, A, A, kext(G.m, dt), G.mp, ss, B);
     g2.alpha = c.h->ns_c;
     g2.beta = c.h->ns_b;
     g2.D = A; g2.d_ps = ss; g2.ldd = static_cast<int32_t>(G.mp);
@@ -255,7 +265,7 @@ static int run_standard(const StepCtx& c, const Group& G) {
 
     const bool last = (k == c.h->ns_steps - 1);
     GemmArgs g3 = last ? apply_args(c, G) : GemmArgs{};
-    set_full(g3, G, B, ss, G.mp, Y[cur], xs, G.mp, G.mp, G.mp, G.np);
+    set_full(g3, G, B, ss, G.mp, Y[cur], xs, G.mp, kext(G.m, dt), G.mp, G.np);
     g3.alpha = 1.0f;
     g3.beta = c.h->ns_a;
     g3.D = X[cur]; g3.d_ps = xs; g3.ldd = static_cast<int32_t>(G.np);
@@ -292,7 +302,7 @@ static int run_gram(const StepCtx& c, const Group& G) {
   if (st != MUON_OK) return st;
 
   GemmArgs r0{};
-  set_sym(r0, G, X0, X0, G.np, G.np, xs, R[0]);
+  set_sym(r0, G, X0, X0, kext(G.n, dt), G.np, xs, R[0]);
   r0.alpha = s;
   MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, r0, c.s));
 
@@ -302,7 +312,7 @@ static int run_gram(const StepCtx& c, const Group& G) {
     // Q_k (symmetric); on the first step it is also P (and P^T)
     void* Qdst = (k == 0) ? PT[0] : Qb;
     GemmArgs gq{};
-    set_sym(gq, G, R[rc], R[rc], G.mp, G.mp, ss, Qdst);
+    set_sym(gq, G, R[rc], R[rc], kext(G.m, dt), G.mp, ss, Qdst);
     gq.alpha = c.h->ns_c / (s * s);
     gq.beta = c.h->ns_b / s;
     gq.gamma = c.h->ns_a;
@@ -314,7 +324,7 @@ static int run_gram(const StepCtx& c, const Group& G) {
     } else {
       // P <- Q P, with P^T as the second operand; stored transposed, or row-major after the last step
       GemmArgs gp{};
-      set_full(gp, G, Qdst, ss, G.mp, PT[pc], ss, G.mp, G.mp, G.mp, G.mp);
+      set_full(gp, G, Qdst, ss, G.mp, PT[pc], ss, G.mp, kext(G.m, dt), G.mp, G.mp);
       gp.alpha = 1.0f;
       if (k == S - 1) {
         gp.C = Pm; gp.c_ps = ss; gp.ldc = static_cast<int32_t>(G.mp);
@@ -330,13 +340,13 @@ static int run_gram(const StepCtx& c, const Group& G) {
       const void* Qk = Qdst;
       // T = R Q, stored as T^T
       GemmArgs gt{};
-      set_full(gt, G, R[rc], ss, G.mp, Qk, ss, G.mp, G.mp, G.mp, G.mp);
+      set_full(gt, G, R[rc], ss, G.mp, Qk, ss, G.mp, kext(G.m, dt), G.mp, G.mp);
       gt.alpha = 1.0f;
       gt.Ct = Tt; gt.ct_ps = ss; gt.ldct = static_cast<int32_t>(G.mp);
       MUON_LAUNCH("gram_gemm_full", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, gt, c.s));
       // R <- Q T (symmetric: lower tiles, mirrored)
       GemmArgs gr{};
-      set_sym(gr, G, Qk, Tt, G.mp, G.mp, ss, R[rc ^ 1]);
+      set_sym(gr, G, Qk, Tt, kext(G.m, dt), G.mp, ss, R[rc ^ 1]);
       gr.alpha = 1.0f;
       MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, gr, c.s));
       rc ^= 1;
@@ -344,7 +354,7 @@ static int run_gram(const StepCtx& c, const Group& G) {
   }
   if (Pfinal == nullptr) return fail(MUON_ERR_HIP, "internal: gram chain left no final P");
   GemmArgs ga = apply_args(c, G);
-  set_full(ga, G, Pfinal, ss, G.mp, Y0, xs, G.mp, G.mp, G.mp, G.np);
+  set_full(ga, G, Pfinal, ss, G.mp, Y0, xs, G.mp, kext(G.m, dt), G.mp, G.np);
   ga.alpha = 1.0f;
   MUON_LAUNCH("gram_gemm_apply", c.s, launch_ns_gemm(dt, G.tile, false, EPI_APPLY, ga, c.s));
   return MUON_OK;

@@ -18,7 +18,15 @@ int element_size(int dtype) {
   }
 }
 
-int tile_for(int64_t m) { return m >= 512 ? 256 : 128; }
+// 256 x 256 tiles (one workgroup per CU) for short sides from 512 up, unless the
+// group's smallest launch, the symmetric X X^T over the lower tiles, would then
+// fill fewer than 1.5 waves of the 256 CUs: 128 x 128 tiles (two workgroups per
+// CU, four times the tiles) keep small groups from idling most of the chip.
+int tile_for(int64_t m, int64_t count) {
+  if (m < 512) return 128;
+  const int64_t t = (m + 255) / 256;
+  return count * t * (t + 1) / 2 >= 384 ? 256 : 128;
+}
 
 static int64_t round_up(int64_t v, int64_t q) { return (v + q - 1) / q * q; }
 static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -82,8 +90,7 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
       g = static_cast<int>(L.groups.size());
       gid[key] = g;
       Group G;
-      G.m = m; G.n = n; G.tile = tile_for(m);
-      G.mp = round_up(m, G.tile); G.np = round_up(n, G.tile);
+      G.m = m; G.n = n;
       L.groups.push_back(G);
       per_group.emplace_back();
     } else {
@@ -98,6 +105,10 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
     }
   }
   for (size_t g = 0; g < L.groups.size(); ++g) {
+    Group& G = L.groups[g];
+    G.tile = tile_for(G.m, static_cast<int64_t>(per_group[g].size()));
+    G.mp = round_up(G.m, G.tile);
+    G.np = round_up(G.n, G.tile);
     L.groups[g].first = static_cast<int>(L.problems.size());
     L.groups[g].count = static_cast<int>(per_group[g].size());
     L.problems.insert(L.problems.end(), per_group[g].begin(), per_group[g].end());

@@ -55,7 +55,7 @@ int validate(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* 
 // Builds the layout of a validated table.
 Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h);
 
-// Tile edge used for a problem whose short side is m.
-int tile_for(int64_t m);
+// Tile edge used for a group of `count` problems whose short side is m.
+int tile_for(int64_t m, int64_t count);
 
 }  // namespace muon
