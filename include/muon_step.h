@@ -40,10 +40,9 @@
  *     every buffer unchanged. muon_last_error() gives a message for the last
  *     failing call on the calling thread.
  *   - The caller owns all buffers, including the workspace. The library keeps
- *     one small device array of per-problem descriptors (16 bytes per problem
- *     plus 16 bytes per 32768-element chunk) for each distinct shape table it
- *     has seen, created on the first call with that table and reused after;
- *     muon_release_plans() frees them.
+ *     one small device array of per-problem descriptors (16 bytes per problem)
+ *     for each distinct shape table it has seen, created on the first call with
+ *     that table and reused after; muon_release_plans() frees them.
  *   - Calls that share a workspace, or that update the same buffers, must be
  *     ordered by the caller (same stream, or events).
  */

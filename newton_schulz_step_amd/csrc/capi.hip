@@ -54,8 +54,6 @@ static hipError_t timed(const char* kind, hipStream_t s, F&& launch) {
 struct Plan {
   Layout L;
   ProblemDesc* d_problems = nullptr;
-  ChunkDesc* d_chunks = nullptr;
-  int32_t* d_chunk_begin = nullptr;
 };
 
 static std::mutex g_plan_mu;
@@ -64,11 +62,7 @@ static constexpr size_t kMaxPlans = 1024;
 
 static void free_plan(Plan& p) {
   if (p.d_problems) hipFree(p.d_problems);
-  if (p.d_chunks) hipFree(p.d_chunks);
-  if (p.d_chunk_begin) hipFree(p.d_chunk_begin);
   p.d_problems = nullptr;
-  p.d_chunks = nullptr;
-  p.d_chunk_begin = nullptr;
 }
 
 static std::string plan_key(int device, const muon_matrix_t* t, int32_t n, const muon_hyper_t* h) {
@@ -102,27 +96,15 @@ static int get_plan(const muon_matrix_t* t, int32_t n, const muon_hyper_t* h, Pl
     probs[i].transposed = p->L.problems[i].transposed;
     probs[i].pad = 0;
   }
-  std::vector<ChunkDesc> chunks(p->L.chunks.size());
-  for (size_t i = 0; i < chunks.size(); ++i) {
-    chunks[i].start = p->L.chunks[i].start;
-    chunks[i].len = p->L.chunks[i].len;
-    chunks[i].problem = p->L.chunks[i].problem;
-  }
   const size_t pb = std::max<size_t>(probs.size(), 1) * sizeof(ProblemDesc);
-  const size_t cb = std::max<size_t>(chunks.size(), 1) * sizeof(ChunkDesc);
-  const size_t bb = p->L.chunk_begin.size() * sizeof(int32_t);
-  if (hipMalloc(&p->d_problems, pb) != hipSuccess || hipMalloc(&p->d_chunks, cb) != hipSuccess ||
-      hipMalloc(&p->d_chunk_begin, bb) != hipSuccess) {
+  if (hipMalloc(&p->d_problems, pb) != hipSuccess) {
     free_plan(*p);
-    return fail(MUON_ERR_HIP, "hipMalloc of the descriptor arrays failed");
+    return fail(MUON_ERR_HIP, "hipMalloc of the problem descriptors failed");
   }
-  if ((!probs.empty() && hipMemcpy(p->d_problems, probs.data(), probs.size() * sizeof(ProblemDesc),
-                                   hipMemcpyHostToDevice) != hipSuccess) ||
-      (!chunks.empty() && hipMemcpy(p->d_chunks, chunks.data(), chunks.size() * sizeof(ChunkDesc),
-                                    hipMemcpyHostToDevice) != hipSuccess) ||
-      hipMemcpy(p->d_chunk_begin, p->L.chunk_begin.data(), bb, hipMemcpyHostToDevice) != hipSuccess) {
+  if (!probs.empty() &&
+      hipMemcpy(p->d_problems, probs.data(), probs.size() * sizeof(ProblemDesc), hipMemcpyHostToDevice) != hipSuccess) {
     free_plan(*p);
-    return fail(MUON_ERR_HIP, "copying the descriptor arrays failed");
+    return fail(MUON_ERR_HIP, "copying the problem descriptors failed");
   }
   *out = p.get();
   g_plans[key] = std::move(p);
@@ -453,12 +435,13 @@ int muon_step(void* params, const void* grads, float* momentum, int64_t numel, c
   float* partials = reinterpret_cast<float*>(ws + P->L.off_partials);
   float* invn = reinterpret_cast<float*>(ws + P->L.off_invnorm);
   const float mu = h->momentum;
-  MUON_LAUNCH("momentum_sumsq", s,
-              launch_momentum_sumsq(h->grad_dtype, momentum, grads, P->d_chunks, static_cast<int>(P->L.chunks.size()),
-                                    mu, partials, s));
-  MUON_LAUNCH("finalize_norm", s,
-              launch_finalize_norm(partials, P->d_chunk_begin, static_cast<int>(P->L.problems.size()), h->ns_eps,
-                                   invn, s));
+  for (const Group& G : P->L.groups)
+    MUON_LAUNCH("momentum_sumsq", s,
+                launch_momentum_sumsq(h->grad_dtype, momentum, grads, P->d_problems + G.first, G.count, G.m * G.n,
+                                      G.chunks, mu, partials + G.partial_first, s));
+  for (const Group& G : P->L.groups)
+    MUON_LAUNCH("finalize_norm", s,
+                launch_finalize_norm(partials + G.partial_first, G.chunks, G.count, h->ns_eps, invn + G.first, s));
   StepCtx c{P, h, ws, momentum, static_cast<float*>(params), update_out, bf16_shadow,
             static_cast<float>(1.0 - static_cast<double>(h->lr) * static_cast<double>(h->weight_decay)), s};
   for (const Group& G : P->L.groups) {

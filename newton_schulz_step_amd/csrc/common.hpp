@@ -25,14 +25,6 @@ struct ProblemDesc {
   int32_t pad;
 };
 
-// Momentum chunk: a contiguous piece of one problem's elements.
-struct ChunkDesc {
-  int64_t start;       // element offset in the packed buffers
-  int32_t len;         // element count (<= kChunkElems)
-  int32_t problem;     // problem index within its group's problem list (global index)
-};
-
-constexpr int kChunkElems = kChunkElemsHost;
 
 // ---------------------------------------------------------------------------
 // element conversions (round to nearest even, the hardware default)
@@ -69,23 +61,40 @@ template <> __device__ __forceinline__ float grad_to_f32<MUON_DTYPE_F16>(const v
   return f16_bits_to_f32(static_cast<const unsigned short*>(g)[i]);
 }
 
-// 8 consecutive grad elements (16-byte aligned for 16-bit types, 32-byte for f32)
-template <int GDT> __device__ __forceinline__ void load_grad8(const void* g, int64_t i, float (&o)[8]);
-template <> __device__ __forceinline__ void load_grad8<MUON_DTYPE_F32>(const void* g, int64_t i, float (&o)[8]) {
-  const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(g) + i);
-  f32x4 a = p[0], b = p[1];
+// 4 consecutive grad elements (8-byte aligned for 16-bit types, 16-byte for f32).
+// Gradients are read exactly once per step: non-temporal loads keep them from
+// displacing cached data (also in load_grad2).
+template <int GDT> __device__ __forceinline__ void load_grad4(const void* g, int64_t i, float (&o)[4]);
+template <> __device__ __forceinline__ void load_grad4<MUON_DTYPE_F32>(const void* g, int64_t i, float (&o)[4]) {
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(g) + i));
   o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
-  o[4] = b[0]; o[5] = b[1]; o[6] = b[2]; o[7] = b[3];
 }
-template <> __device__ __forceinline__ void load_grad8<MUON_DTYPE_BF16>(const void* g, int64_t i, float (&o)[8]) {
-  u16x8 v = *reinterpret_cast<const u16x8*>(static_cast<const unsigned short*>(g) + i);
+template <> __device__ __forceinline__ void load_grad4<MUON_DTYPE_BF16>(const void* g, int64_t i, float (&o)[4]) {
+  const u16x4 v = __builtin_nontemporal_load(reinterpret_cast<const u16x4*>(static_cast<const unsigned short*>(g) + i));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = bf16_bits_to_f32(v[e]);
+  for (int e = 0; e < 4; ++e) o[e] = bf16_bits_to_f32(v[e]);
 }
-template <> __device__ __forceinline__ void load_grad8<MUON_DTYPE_F16>(const void* g, int64_t i, float (&o)[8]) {
-  u16x8 v = *reinterpret_cast<const u16x8*>(static_cast<const unsigned short*>(g) + i);
+template <> __device__ __forceinline__ void load_grad4<MUON_DTYPE_F16>(const void* g, int64_t i, float (&o)[4]) {
+  const u16x4 v = __builtin_nontemporal_load(reinterpret_cast<const u16x4*>(static_cast<const unsigned short*>(g) + i));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = f16_bits_to_f32(v[e]);
+  for (int e = 0; e < 4; ++e) o[e] = f16_bits_to_f32(v[e]);
+}
+
+// 2 consecutive grad elements (4-byte aligned for 16-bit types, 8-byte for f32)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <int GDT> __device__ __forceinline__ void load_grad2(const void* g, int64_t i, float (&o)[2]);
+template <> __device__ __forceinline__ void load_grad2<MUON_DTYPE_F32>(const void* g, int64_t i, float (&o)[2]) {
+  const f32x2 a = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(static_cast<const float*>(g) + i));
+  o[0] = a[0]; o[1] = a[1];
+}
+template <> __device__ __forceinline__ void load_grad2<MUON_DTYPE_BF16>(const void* g, int64_t i, float (&o)[2]) {
+  const u16x2 v = __builtin_nontemporal_load(reinterpret_cast<const u16x2*>(static_cast<const unsigned short*>(g) + i));
+  o[0] = bf16_bits_to_f32(v[0]); o[1] = bf16_bits_to_f32(v[1]);
+}
+template <> __device__ __forceinline__ void load_grad2<MUON_DTYPE_F16>(const void* g, int64_t i, float (&o)[2]) {
+  const u16x2 v = __builtin_nontemporal_load(reinterpret_cast<const u16x2*>(static_cast<const unsigned short*>(g) + i));
+  o[0] = f16_bits_to_f32(v[0]); o[1] = f16_bits_to_f32(v[1]);
 }
 
 // ---------------------------------------------------------------------------

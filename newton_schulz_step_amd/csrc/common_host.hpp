@@ -2,5 +2,6 @@
 #pragma once
 
 namespace muon {
-constexpr int kChunkElemsHost = 32768;  // elements per momentum chunk
+constexpr int kMomThreads = 256;                 // threads per momentum block
+constexpr int kMomChunk = kMomThreads * 4;       // elements per momentum block (4 per thread)
 }  // namespace muon

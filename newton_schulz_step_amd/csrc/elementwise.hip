@@ -2,10 +2,11 @@
 // squares, the Frobenius normalisation into the iteration's storage type, AdamW,
 // and bit-exact batched copies for packing.
 //
-// All of these are bound by HBM bandwidth; each thread moves 8 elements per
-// access (16/32-byte vector loads and stores), consecutive threads touch
-// consecutive vectors, and reductions run in a fixed order (wave butterflies,
-// then a fixed sum over waves) so results do not depend on scheduling.
+// All of these are bound by HBM bandwidth: consecutive threads touch consecutive
+// vectors, each thread moves a few elements in one pass (no loops), and
+// reductions run in a fixed order (wave butterflies, then a fixed sum over
+// waves, then a fixed-order float64 sum over blocks) so results do not depend on
+// scheduling.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -15,53 +16,37 @@ namespace muon {
 // momentum (DeepSpeed-Muon article, "什么是 Muon 优化器？": momentum first) and the
 // sum of squares that the Frobenius normalisation needs
 
+// One block of kMomThreads threads updates kMomChunk consecutive elements of one
+// problem, four per thread (one 16-byte momentum vector): many small blocks keep
+// the most reads and writes in flight across the HBM channels.
 template <int GDT>
-__device__ __forceinline__ float momentum8(float* M, const void* G, int64_t i, float mu) {
-  float g[8];
-  load_grad8<GDT>(G, i, g);
-  f32x4* mp = reinterpret_cast<f32x4*>(M + i);
-  f32x4 m0 = mp[0], m1 = mp[1];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    m0[e] = mu * m0[e] + g[e];
-    m1[e] = mu * m1[e] + g[e + 4];
-  }
-  mp[0] = m0;
-  mp[1] = m1;
-  float s = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) s += m0[e] * m0[e] + m1[e] * m1[e];
-  return s;
-}
-
-template <int GDT>
-__global__ __launch_bounds__(256) void momentum_sumsq_kernel(float* M, const void* G, const ChunkDesc* chunks,
-                                                             float mu, float* partials) {
-  __shared__ float red[4];
-  const ChunkDesc c = chunks[blockIdx.x];
+__global__ __launch_bounds__(kMomThreads) void momentum_sumsq_kernel(float* M, const void* G, const ProblemDesc* probs,
+                                                                     int64_t per_problem, int64_t chunks, float mu,
+                                                                     float* partials) {
+  __shared__ float red[kMomThreads / 64];
+  const int64_t b = blockIdx.x;
+  const int64_t p = b / chunks;
+  const int64_t c = b - p * chunks;
+  const int64_t first = c * kMomChunk;                      // first element of the block within the problem
+  const int len = static_cast<int>(min<int64_t>(kMomChunk, per_problem - first));
+  const int64_t start = probs[p].src_off + first;           // a multiple of 8 elements
   const int tid = threadIdx.x;
+  const int e0 = tid * 4;
   float ss = 0.0f;
-  if ((c.start & 7) == 0) {
-    const int nv = c.len >> 3;
-    int v = tid;
-    for (; v + 3 * 256 < nv; v += 4 * 256) {
-      // four independent vectors in flight per thread
-      const float s0 = momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v) * 8, mu);
-      const float s1 = momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v + 256) * 8, mu);
-      const float s2 = momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v + 512) * 8, mu);
-      const float s3 = momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v + 768) * 8, mu);
-      ss += (s0 + s1) + (s2 + s3);
+  if (e0 + 4 <= len) {
+    float g[4];
+    load_grad4<GDT>(G, start + e0, g);
+    f32x4* mp = reinterpret_cast<f32x4*>(M + start + e0);
+    f32x4 m = *mp;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[e] = mu * m[e] + g[e];
+      ss += m[e] * m[e];
     }
-    for (; v < nv; v += 256) ss += momentum8<GDT>(M, G, c.start + static_cast<int64_t>(v) * 8, mu);
-    for (int k = nv * 8 + tid; k < c.len; k += 256) {
-      const int64_t i = c.start + k;
-      const float m = mu * M[i] + grad_to_f32<GDT>(G, i);
-      M[i] = m;
-      ss += m * m;
-    }
+    *mp = m;
   } else {
-    for (int k = tid; k < c.len; k += 256) {
-      const int64_t i = c.start + k;
+    for (int e = e0; e < len; ++e) {
+      const int64_t i = start + e;
       const float m = mu * M[i] + grad_to_f32<GDT>(G, i);
       M[i] = m;
       ss += m * m;
@@ -70,21 +55,27 @@ __global__ __launch_bounds__(256) void momentum_sumsq_kernel(float* M, const voi
   ss = wave_sum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  if (tid == 0) partials[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) partials[b] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const ChunkDesc* chunks,
-                                 int n_chunks, float mu, float* partials, hipStream_t s) {
-  if (n_chunks <= 0) return hipSuccess;
+hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const ProblemDesc* probs, int n_problems,
+                                 int64_t per_problem, int64_t chunks, float mu, float* partials, hipStream_t s) {
+  static_assert(kMomThreads == 256, "the block reduction sums four waves");
+  const int64_t blocks = static_cast<int64_t>(n_problems) * chunks;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   switch (grad_dtype) {
     case MUON_DTYPE_BF16:
-      hipLaunchKernelGGL(momentum_sumsq_kernel<MUON_DTYPE_BF16>, dim3(n_chunks), dim3(256), 0, s, M, G, chunks, mu, partials);
+      hipLaunchKernelGGL(momentum_sumsq_kernel<MUON_DTYPE_BF16>, dim3(blocks), dim3(kMomThreads), 0, s, M, G, probs,
+                         per_problem, chunks, mu, partials);
       break;
     case MUON_DTYPE_F16:
-      hipLaunchKernelGGL(momentum_sumsq_kernel<MUON_DTYPE_F16>, dim3(n_chunks), dim3(256), 0, s, M, G, chunks, mu, partials);
+      hipLaunchKernelGGL(momentum_sumsq_kernel<MUON_DTYPE_F16>, dim3(blocks), dim3(kMomThreads), 0, s, M, G, probs,
+                         per_problem, chunks, mu, partials);
       break;
     default:
-      hipLaunchKernelGGL(momentum_sumsq_kernel<MUON_DTYPE_F32>, dim3(n_chunks), dim3(256), 0, s, M, G, chunks, mu, partials);
+      hipLaunchKernelGGL(momentum_sumsq_kernel<MUON_DTYPE_F32>, dim3(blocks), dim3(kMomThreads), 0, s, M, G, probs,
+                         per_problem, chunks, mu, partials);
   }
   return hipGetLastError();
 }
@@ -92,22 +83,34 @@ hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const 
 // ---------------------------------------------------------------------------
 // 1 / (||Y||_F + eps) per problem; partial sums combined in double, fixed order
 
-__global__ __launch_bounds__(256) void finalize_norm_kernel(const float* partials, const int32_t* cb, int n_problems,
-                                                            float eps, float* inv_norm) {
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (p >= n_problems) return;
-  double s = 0.0;
-  for (int k = cb[p] + lane; k < cb[p + 1]; k += 64) s += static_cast<double>(partials[k]);
+// One block per problem: thread t sums partials t, t + 256, ... into four
+// float64 accumulators (k mod 4), combined in a fixed order, then waves and the
+// block in a fixed order; the result depends only on the problem's own partials.
+__global__ __launch_bounds__(256) void finalize_norm_kernel(const float* partials, int64_t chunks, float eps,
+                                                            float* inv_norm) {
+  __shared__ double red[4];
+  const int p = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* part = partials + static_cast<int64_t>(p) * chunks;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t k = tid;
+  for (; k + 3 * 256 < chunks; k += 4 * 256) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += static_cast<double>(part[k + u * 256]);
+  }
+  for (int u = 0; k < chunks; k += 256, ++u) acc[u] += static_cast<double>(part[k]);
+  double s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   s = wave_sum_d(s);
-  if (lane == 0) inv_norm[p] = static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(eps)));
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) inv_norm[p] = static_cast<float>(1.0 / (sqrt((red[0] + red[1]) + (red[2] + red[3])) +
+                                                        static_cast<double>(eps)));
 }
 
-hipError_t launch_finalize_norm(const float* partials, const int32_t* chunk_begin, int n_problems, float eps,
-                                float* inv_norm, hipStream_t s) {
+hipError_t launch_finalize_norm(const float* partials, int64_t chunks, int n_problems, float eps, float* inv_norm,
+                                hipStream_t s) {
   if (n_problems <= 0) return hipSuccess;
-  hipLaunchKernelGGL(finalize_norm_kernel, dim3((n_problems + 3) / 4), dim3(256), 0, s, partials, chunk_begin,
-                     n_problems, eps, inv_norm);
+  hipLaunchKernelGGL(finalize_norm_kernel, dim3(n_problems), dim3(256), 0, s, partials, chunks, eps, inv_norm);
   return hipGetLastError();
 }
 
@@ -229,57 +232,46 @@ hipError_t launch_prep_x0(int ns_dtype, const float* M, const ProblemDesc* probs
 // ---------------------------------------------------------------------------
 // AdamW (the article's Adam fallback for non-2D parameters, AdamW mode)
 
-template <int GDT>
-__device__ __forceinline__ void adamw8(float* p, const void* g, float* m, float* v, int64_t i, float b1, float b2,
-                                       float step_size, float inv_bc2, float eps, float decay) {
-  float gg[8];
-  load_grad8<GDT>(g, i, gg);
-  f32x4* pp = reinterpret_cast<f32x4*>(p + i);
-  f32x4* mp = reinterpret_cast<f32x4*>(m + i);
-  f32x4* vp = reinterpret_cast<f32x4*>(v + i);
-  f32x4 P[2] = {pp[0], pp[1]}, Mv[2] = {mp[0], mp[1]}, Vv[2] = {vp[0], vp[1]};
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float gi = gg[h * 4 + e];
-      const float mn = b1 * Mv[h][e] + (1.0f - b1) * gi;
-      const float vn = b2 * Vv[h][e] + (1.0f - b2) * gi * gi;
-      Mv[h][e] = mn;
-      Vv[h][e] = vn;
-      P[h][e] = P[h][e] * decay - step_size * (mn / (sqrtf(vn * inv_bc2) + eps));
-    }
-  pp[0] = P[0]; pp[1] = P[1];
-  mp[0] = Mv[0]; mp[1] = Mv[1];
-  vp[0] = Vv[0]; vp[1] = Vv[1];
-}
-
+// Two elements per thread, one pass, no loop: with four buffers read and three
+// written per element, small per-thread work keeps the most requests in flight.
 template <int GDT>
 __global__ __launch_bounds__(256) void adamw_kernel(float* p, const void* g, float* m, float* v, int64_t n, float b1,
                                                     float b2, float step_size, float inv_bc2, float eps, float decay) {
-  const int64_t nv = n >> 3;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
-  for (int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; k < nv; k += stride)
-    adamw8<GDT>(p, g, m, v, k * 8, b1, b2, step_size, inv_bc2, eps, decay);
-  if (blockIdx.x == 0) {
-    for (int64_t i = nv * 8 + threadIdx.x; i < n; i += 256) {
-      const float gi = grad_to_f32<GDT>(g, i);
-      const float mn = b1 * m[i] + (1.0f - b1) * gi;
-      const float vn = b2 * v[i] + (1.0f - b2) * gi * gi;
-      m[i] = mn;
-      v[i] = vn;
-      p[i] = p[i] * decay - step_size * (mn / (sqrtf(vn * inv_bc2) + eps));
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 2;
+  if (i >= n) return;
+  auto one = [&](float gi, float& pi, float& mi, float& vi) {
+    const float mn = b1 * mi + (1.0f - b1) * gi;
+    const float vn = b2 * vi + (1.0f - b2) * gi * gi;
+    mi = mn;
+    vi = vn;
+    pi = pi * decay - step_size * (mn / (sqrtf(vn * inv_bc2) + eps));
+  };
+  if (i + 2 <= n) {
+    float gg[2];
+    load_grad2<GDT>(g, i, gg);
+    f32x2* pp = reinterpret_cast<f32x2*>(p + i);
+    f32x2* mp = reinterpret_cast<f32x2*>(m + i);
+    f32x2* vp = reinterpret_cast<f32x2*>(v + i);
+    f32x2 P = *pp, Mv = *mp, Vv = *vp;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float pe = P[e], me = Mv[e], ve = Vv[e];
+      one(gg[e], pe, me, ve);
+      P[e] = pe; Mv[e] = me; Vv[e] = ve;
     }
+    *pp = P;
+    *mp = Mv;
+    *vp = Vv;
+  } else {
+    one(grad_to_f32<GDT>(g, i), p[i], m[i], v[i]);
   }
 }
 
 hipError_t launch_adamw(int grad_dtype, float* p, const void* g, float* m, float* v, int64_t n, float beta1,
                         float beta2, float step_size, float inv_bc2, float eps, float decay, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const int64_t nv = n >> 3;
-  int64_t blocks = (nv + 255) / 256;
-  if (blocks < 1) blocks = 1;
-  if (blocks > 16384) blocks = 16384;
+  const int64_t blocks = (n + 511) / 512;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   switch (grad_dtype) {
     case MUON_DTYPE_BF16:
       hipLaunchKernelGGL(adamw_kernel<MUON_DTYPE_BF16>, dim3(blocks), dim3(256), 0, s, p, g, m, v, n, beta1, beta2,

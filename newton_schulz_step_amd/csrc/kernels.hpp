@@ -30,13 +30,15 @@ struct GemmArgs {
 
 hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmArgs& a, hipStream_t s);
 
-// M <- mu M + G over each chunk; partial[c] = sum of squares of the new M in chunk c.
-hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const ChunkDesc* chunks,
-                                 int n_chunks, float mu, float* partials, hipStream_t s);
+// M <- mu M + G over every problem of a group (each m n contiguous elements at
+// its src_off), kMomChunk elements per block; partials[b] = sum of squares of the
+// new M in block b (problem b / chunks, block b % chunks of that problem).
+hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const ProblemDesc* probs, int n_problems,
+                                 int64_t per_problem, int64_t chunks, float mu, float* partials, hipStream_t s);
 
-// inv_norm[p] = 1 / (sqrt(sum of partials of p) + eps), partials summed in a fixed order.
-hipError_t launch_finalize_norm(const float* partials, const int32_t* chunk_begin, int n_problems,
-                                float eps, float* inv_norm, hipStream_t s);
+// inv_norm[p] = 1 / (sqrt(sum of the `chunks` partials of p) + eps), summed in a fixed order.
+hipError_t launch_finalize_norm(const float* partials, int64_t chunks, int n_problems, float eps, float* inv_norm,
+                                hipStream_t s);
 
 // X0 (canonical m x n, padded mp x np) and Y0 = X0^T (np x mp) of every problem of a group,
 // X0 = round(M * inv_norm); padding zero.

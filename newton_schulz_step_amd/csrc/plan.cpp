@@ -113,28 +113,19 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
     L.groups[g].count = static_cast<int>(per_group[g].size());
     L.problems.insert(L.problems.end(), per_group[g].begin(), per_group[g].end());
   }
-  // momentum chunks, by problem
-  L.chunk_begin.resize(L.problems.size() + 1);
-  for (const Group& G : L.groups) {
-    const int64_t total = G.m * G.n;
-    for (int p = G.first; p < G.first + G.count; ++p) {
-      L.chunk_begin[p] = static_cast<int32_t>(L.chunks.size());
-      for (int64_t s = 0; s < total; s += kChunkElemsHost) {
-        HostChunk c;
-        c.start = L.problems[p].src_off + s;
-        c.len = static_cast<int32_t>(std::min<int64_t>(kChunkElemsHost, total - s));
-        c.problem = p;
-        L.chunks.push_back(c);
-      }
-    }
+  // momentum blocks: each problem is cut into blocks of kMomChunk elements; the
+  // per-block partial sums of squares are laid out group by group, problem by problem
+  for (Group& G : L.groups) {
+    G.chunks = (G.m * G.n + kMomChunk - 1) / kMomChunk;
+    G.partial_first = L.n_partials;
+    L.n_partials += static_cast<size_t>(G.count) * static_cast<size_t>(G.chunks);
   }
-  L.chunk_begin[L.problems.size()] = static_cast<int32_t>(L.chunks.size());
 
   // workspace
   const size_t esz = static_cast<size_t>(element_size(h->ns_dtype));
   size_t off = 0;
   L.off_partials = off;
-  off = align256(off + L.chunks.size() * sizeof(float));
+  off = align256(off + L.n_partials * sizeof(float));
   L.off_invnorm = off;
   off = align256(off + L.problems.size() * sizeof(float));
   for (Group& G : L.groups) {

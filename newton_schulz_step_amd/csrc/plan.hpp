@@ -19,18 +19,14 @@ struct HostProblem {
   int32_t entry;
 };
 
-struct HostChunk {
-  int64_t start;
-  int32_t len;
-  int32_t problem;
-};
-
 // All problems of one canonical shape (m <= n). Buffers are tile-padded
 // (mp x np), one slice per problem, consecutive.
 struct Group {
   int64_t m = 0, n = 0, mp = 0, np = 0;
   int tile = 0;
   int first = 0, count = 0;          // problems [first, first + count) of the plan
+  int64_t chunks = 0;                // momentum blocks per problem (ceil(m n / kMomChunk))
+  size_t partial_first = 0;          // index of the group's first per-block partial sum
   // workspace byte offsets
   size_t x[2] = {0, 0}, y[2] = {0, 0};   // X and X^T, ping-pong (standard); X0 / Y0 in [0] (gram)
   size_t a = 0, b = 0;                   // standard: A, B; gram: R, Q
@@ -40,8 +36,7 @@ struct Group {
 struct Layout {
   std::vector<HostProblem> problems;   // ordered by group
   std::vector<Group> groups;
-  std::vector<HostChunk> chunks;       // ordered by problem
-  std::vector<int32_t> chunk_begin;    // size problems + 1
+  size_t n_partials = 0;               // per-block partial sums of squares, all groups
   size_t off_partials = 0, off_invnorm = 0;
   size_t ws_bytes = 0;
 };
