@@ -11,8 +11,8 @@
 //
 // Tile: TILE x TILE outputs per workgroup (256 or 128), 4 waves in a 2x2 grid,
 // each wave owning (TILE/2)^2 outputs as 32x32 MFMA blocks. K advances in
-// 128-byte slices (64 bf16/f16 or 32 f32 elements). Operand slices go straight
-// from global memory to LDS (global_load_lds_dwordx4) into a double buffer;
+// 128-byte slices (64 bf16/f16 or 32 f32 elements). Operand slices are staged
+// through registers into a double buffer in LDS;
 // rows are 128 bytes, with the 16-byte chunk index XOR-swizzled by the row so
 // that the MFMA operand reads (ds_read_b128, 32 rows at one chunk) spread over
 // all banks. MFMA operands are double-buffered in registers so that reads of
@@ -165,48 +165,58 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int& prob, int& t
 // Main loop: acc[i][j] += P[tile rows] Q[tile cols]^T over the whole K range.
 //
 // K advances in 128-byte slices through two LDS buffers. Each slice has four
-// sub-steps (one per 16-byte chunk pair); the MFMA operands of sub-step s + 1 are
-// read from LDS while the MFMAs of sub-step s run (two register sets). Every
-// sub-step is its own scheduling region, so no MFMA waits for a read issued in
-// its own region. One barrier per slice, before the last sub-step: it publishes
-// the next slice (every wave has waited for its own direct loads) and frees the
-// current buffer, into which the load of slice min(kt + 2, nk - 1) then starts.
-// On the last two slices those loads are redundant (in bounds, never read), and
-// the loop drains them before the epilogue reuses the LDS.
+// sub-steps (one per 16-byte chunk pair); the MFMA operands of sub-step s + 1
+// are read from LDS while the MFMAs of sub-step s run (two register sets), and
+// every sub-step is its own scheduling region, so no MFMA waits for a read
+// issued in its own region.
+//
+// Operand slices are staged through registers: during slice kt, sub-steps 0..2
+// each write a third of slice kt + 1 (loaded into registers during slice kt - 1)
+// into the other LDS buffer and immediately reload those registers with the same
+// part of slice kt + 2. Spreading the global loads over the slice keeps the load
+// path busy steadily; issued in one burst per slice (as direct-to-LDS loads must
+// be, once the barrier frees their buffer) they stalled the MFMAs for about a
+// sixth of the time. One barrier per slice, before the last sub-step, publishes
+// slice kt + 1. The last slices reload slice nk - 1 (in bounds, never used).
 template <typename T, int TILE>
 __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, int tj, char* lds0, char* lds1,
                                          f32x16 (&acc)[Geo<T, TILE>::WB][Geo<T, TILE>::WB]) {
   using Gm = Geo<T, TILE>;
   constexpr int ESZ = Gm::ESZ, HALF = Gm::HALF, WB = Gm::WB, OPB = Gm::OPB, LOADS = Gm::LOADS;
-  constexpr int NMF = WB * WB * Mfma<T>::kInstr;    // MFMA instructions per sub-step
+  constexpr int NV = 2 * LOADS;                       // 16-byte vectors per lane per slice (P, then Q)
+  constexpr int NMF = WB * WB * Mfma<T>::kInstr;      // MFMA instructions per sub-step
   using V = typename Gm::V;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- per-lane direct-load offsets (bytes, relative to the tile's first row)
+  // ---- per-lane global source and LDS destination of each 16-byte vector: lane l
+  // of load `it` covers row (wave * LOADS + it) * 8 + l / 8, chunk l % 8; the chunk
+  // is stored at position chunk ^ swz(row) of its 128-byte LDS row
   const char* Pb = static_cast<const char*>(a.P) +
                    (static_cast<int64_t>(prob) * a.p_ps + static_cast<int64_t>(ti) * TILE * a.ldp) * ESZ;
   const char* Qb = static_cast<const char*>(a.Q) +
                    (static_cast<int64_t>(prob) * a.q_ps + static_cast<int64_t>(tj) * TILE * a.ldq) * ESZ;
-  int64_t poff[LOADS], qoff[LOADS];
+  const char* gp[NV];
+  int wofs[NV];
 #pragma unroll
-  for (int it = 0; it < LOADS; ++it) {
+  for (int v = 0; v < NV; ++v) {
+    const int it = v % LOADS;
     const int r = (wave * LOADS + it) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    poff[it] = static_cast<int64_t>(r) * a.ldp * ESZ + c * 16;
-    qoff[it] = static_cast<int64_t>(r) * a.ldq * ESZ + c * 16;
+    const int c = lane & 7;
+    if (v < LOADS) gp[v] = Pb + static_cast<int64_t>(r) * a.ldp * ESZ + c * 16;
+    else gp[v] = Qb + static_cast<int64_t>(r) * a.ldq * ESZ + c * 16;
+    wofs[v] = (v < LOADS ? 0 : OPB) + r * 128 + ((c ^ swz(r)) << 4);
   }
-  auto issue = [&](char* st, int kt) {
+  u16x8 rv[NV];
+  auto gload = [&](int v0, int v1, int kt) {
     const int64_t kb = static_cast<int64_t>(kt) * 128;
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Pb + poff[it] + kb),
-                                       (MUON_LDS void*)(st + (wave * LOADS + it) * 1024), 16, 0, 0);
+    for (int v = v0; v < v1; ++v) rv[v] = *reinterpret_cast<const u16x8*>(gp[v] + kb);
+  };
+  auto lwrite = [&](int v0, int v1, char* st) {
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Qb + qoff[it] + kb),
-                                       (MUON_LDS void*)(st + OPB + (wave * LOADS + it) * 1024), 16, 0, 0);
+    for (int v = v0; v < v1; ++v) *reinterpret_cast<u16x8*>(st + wofs[v]) = rv[v];
   };
 
   // ---- per-lane MFMA operand read offsets (bytes within an operand slice)
@@ -243,55 +253,62 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
 #pragma unroll
       for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], acc[i][j]);
   };
-  // scheduling: 2 WB operand reads spread over the sub-step's MFMAs, then a fence
-  auto region = [&]() {
+  // scheduling of one sub-step: its nw LDS writes and global loads, then its 2 WB
+  // operand reads, each paired with MFMAs; then a fence
+  auto region = [&](int nw) {
+#pragma unroll
+    for (int q = 0; q < nw; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);    // LDS write
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // global load
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+    }
 #pragma unroll
     for (int q = 0; q < 2 * WB; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, NMF / (2 * WB), 0);    // MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF / (2 * WB) > 1 ? NMF / (2 * WB) - 1 : 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int nk = a.K / (128 / ESZ);   // even: K is a multiple of the tile edge
+  const int nk = a.K / (128 / ESZ);                   // even: K is a multiple of two slices
+  constexpr int B1 = (NV + 2) / 3, B2 = (2 * NV + 2) / 3;
   auto slice = [&](char* cur, char* nxt, int kt) {
+    const int kl = min(kt + 2, nk - 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // slice kt + 1 is in registers
+    lwrite(0, B1, nxt);
+    gload(0, B1, kl);
     rd(fa1, fb1, cur, 1);
     mm(fa0, fb0);
-    region();
+    region(B1);
+    lwrite(B1, B2, nxt);
+    gload(B1, B2, kl);
     rd(fa0, fb0, cur, 2);
     mm(fa1, fb1);
-    region();
+    region(B2 - B1);
+    lwrite(B2, NV, nxt);
+    gload(B2, NV, kl);
     rd(fa1, fb1, cur, 3);
     mm(fa0, fb0);
-    region();
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    region(NV - B2);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own LDS writes and reads done
     __syncthreads();
     rd(fa0, fb0, nxt, 0);
-    issue(cur, min(kt + 2, nk - 1));
     mm(fa1, fb1);
-#pragma unroll
-    for (int q = 0; q < 2 * WB; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    }
-#pragma unroll
-    for (int q = 0; q < 2 * LOADS; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);                 // one direct load
-      if (q & 1) __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    region(0);
   };
 
-  issue(lds0, 0);
+  gload(0, NV, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lwrite(0, NV, lds0);
+  gload(0, NV, 1);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __syncthreads();
   rd(fa0, fb0, lds0, 0);
-  issue(lds1, 1);
   for (int kt = 0; kt < nk; kt += 2) {
     slice(lds0, lds1, kt);
     slice(lds1, lds0, kt + 1);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
 // 8 consecutive elements of T held raw in registers (one or two 16-byte vectors).
