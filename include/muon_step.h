@@ -40,7 +40,7 @@
  *     every buffer unchanged. muon_last_error() gives a message for the last
  *     failing call on the calling thread.
  *   - The caller owns all buffers, including the workspace. The library keeps
- *     one small device array of per-problem descriptors (16 bytes per problem)
+ *     one small device array of per-problem descriptors (48 bytes per problem)
  *     for each distinct shape table it has seen, created on the first call with
  *     that table and reused after; muon_release_plans() frees them.
  *   - Calls that share a workspace, or that update the same buffers, must be
@@ -161,6 +161,49 @@ int muon_step(void* params, const void* grads, float* momentum, int64_t numel,
               const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h,
               void* workspace, size_t workspace_bytes,
               float* update_out, uint16_t* bf16_shadow, void* stream);
+
+/* The part of one table entry that a parameter partition holds: elements
+ * [lo, hi) of the matrix flattened in stored row-major order, found in the
+ * partition from index param_offset on (element e at param_offset + e - lo).
+ * lo == hi holds nothing (its param_offset is then ignored). */
+typedef struct {
+  int64_t lo;
+  int64_t hi;
+  int64_t param_offset;
+} muon_window_t;
+
+/* One Muon step for a holder of one flat parameter partition, whose matrices
+ * may straddle the partition's boundaries. The DeepSpeed-Muon article (ZeRO
+ * stage support section, on partition boundaries) gives every rank that holds
+ * part of such a matrix the whole reduced gradient before the nonlinear
+ * update: here the holder keeps the whole momentum of each listed matrix,
+ * runs momentum and Newton-Schulz on the whole matrix, and updates only the
+ * elements of its own window. Every holder of a matrix, given the same
+ * gradient and momentum, computes the same momentum and the same update, so
+ * the holders' windows together equal a muon_step of the whole matrix, bit
+ * for bit.
+ *   partition       device float32[partition_numel], updated in place
+ *                   (window elements only).
+ *   grads, momentum, numel, table, h, workspace: as in muon_step (the table
+ *                   describes the full-matrix layout of grads and momentum;
+ *                   momentum is updated for every listed matrix in full).
+ *   windows         host, one per table entry; windows must lie inside the
+ *                   partition and must not share a partition element.
+ *   update_out      optional device float32[numel] in the table's layout:
+ *                   receives O for every element of every listed matrix.
+ *   bf16_shadow     optional device bf16[partition_numel]: the bf16 copy of
+ *                   the new partition elements (window elements only).
+ * Workspace size: muon_workspace_size() of the same table. Errors as in
+ * muon_step, plus MUON_ERR_RANGE for a window outside its matrix or the
+ * partition, MUON_ERR_OVERLAP for windows sharing a partition element or a
+ * partition that overlaps another buffer. Windows may start and end at any
+ * element; runs of 8 elements whose partition index is a multiple of 8 take
+ * the vector path, the rest a scalar one. */
+int muon_step_window(float* partition, int64_t partition_numel, const void* grads, float* momentum,
+                     int64_t numel, const muon_matrix_t* table, const muon_window_t* windows,
+                     int32_t n_entries, const muon_hyper_t* h, void* workspace,
+                     size_t workspace_bytes, float* update_out, uint16_t* bf16_shadow,
+                     void* stream);
 
 /* AdamW step over a flat buffer of non-2D parameters (the article's Adam
  * fallback, AdamW mode):

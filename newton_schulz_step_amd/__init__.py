@@ -8,8 +8,8 @@ binding; torch supplies device memory and streams.
 """
 from ._binding import (  # noqa: F401
     DTYPES, EXPORTED, LIB_PATH, NS_METHODS, STATUS_NAMES, AdamWHyper, KernelStat, MuonError,
-    MuonHyper, MuonMatrix, adamw, hyper, load, pack, profile_begin, profile_end, release_plans,
-    step, table, unpack, version, workspace, workspace_size)
+    MuonHyper, MuonMatrix, MuonWindow, adamw, hyper, load, pack, profile_begin, profile_end,
+    release_plans, step, step_window, table, unpack, version, windows, workspace, workspace_size)
 from ._binding import (  # noqa: F401
     ERR_ALIGN, ERR_BAD_HYPER, ERR_BAD_METHOD, ERR_BAD_SHAPE, ERR_HIP, ERR_NULL, ERR_OVERLAP,
     ERR_RANGE, ERR_UNSUPPORTED, ERR_WORKSPACE, OK)

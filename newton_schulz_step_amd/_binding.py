@@ -28,7 +28,7 @@ NS_METHODS = {"standard": 0, "gram": 1}
 
 EXPORTED = (
     "muon_default_hyper", "muon_default_adamw_hyper", "muon_workspace_size", "muon_step",
-    "adamw_step", "muon_pack", "muon_unpack", "muon_last_error", "muon_release_plans",
+    "muon_step_window", "adamw_step", "muon_pack", "muon_unpack", "muon_last_error", "muon_release_plans",
     "muon_profile_begin", "muon_profile_end", "muon_version",
 )
 
@@ -54,6 +54,10 @@ class MuonHyper(ctypes.Structure):
                 ("ns_steps", ctypes.c_int32), ("ns_eps", ctypes.c_float),
                 ("ns_method", ctypes.c_int32), ("param_dtype", ctypes.c_int32),
                 ("grad_dtype", ctypes.c_int32), ("ns_dtype", ctypes.c_int32)]
+
+
+class MuonWindow(ctypes.Structure):
+    _fields_ = [("lo", ctypes.c_int64), ("hi", ctypes.c_int64), ("param_offset", ctypes.c_int64)]
 
 
 class AdamWHyper(ctypes.Structure):
@@ -90,13 +94,15 @@ def load() -> ctypes.CDLL:
         lib.muon_workspace_size.argtypes = [pm, i32, ctypes.POINTER(MuonHyper), ctypes.POINTER(sz)]
         lib.muon_step.argtypes = [vp, vp, vp, i64, pm, i32, ctypes.POINTER(MuonHyper), vp, sz,
                                   vp, vp, vp]
+        lib.muon_step_window.argtypes = [vp, i64, vp, vp, i64, pm, ctypes.POINTER(MuonWindow), i32,
+                                         ctypes.POINTER(MuonHyper), vp, sz, vp, vp, vp]
         lib.adamw_step.argtypes = [vp, vp, vp, vp, i64, ctypes.POINTER(AdamWHyper), vp]
         lib.muon_pack.argtypes = [vp, i64, ctypes.POINTER(vp), pm, i32, i32, vp]
         lib.muon_unpack.argtypes = [ctypes.POINTER(vp), vp, i64, pm, i32, i32, vp]
         lib.muon_last_error.restype = ctypes.c_char_p
         lib.muon_version.restype = ctypes.c_char_p
         lib.muon_profile_end.argtypes = [ctypes.POINTER(KernelStat), i32, ctypes.POINTER(i32)]
-        for name in ("muon_workspace_size", "muon_step", "adamw_step", "muon_pack", "muon_unpack",
+        for name in ("muon_workspace_size", "muon_step", "muon_step_window", "adamw_step", "muon_pack", "muon_unpack",
                      "muon_release_plans", "muon_profile_begin", "muon_profile_end"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
@@ -228,6 +234,47 @@ def step(params, grads, momentum, entries, h: MuonHyper, ws=None, update_out=Non
     _check(load().muon_step(_ptr(params), _ptr(grads), _ptr(momentum), numel, arr, n,
                             ctypes.byref(h), _ptr(ws), ws.numel() * ws.element_size(),
                             _ptr(update_out), _ptr(bf16_shadow), _stream(params, stream)))
+
+
+def windows(ws: Iterable[Sequence[int]], n: int):
+    """ctypes array of muon_window_t from (lo, hi, param_offset) tuples, one per entry."""
+    rows = [tuple(w) for w in ws]
+    if len(rows) != n:
+        raise ValueError("one window per table entry")
+    arr = (MuonWindow * max(n, 1))()
+    for i, (lo, hi, po) in enumerate(rows):
+        arr[i] = MuonWindow(lo, hi, po)
+    return arr
+
+
+def step_window(partition, grads, momentum, entries, wins, h: MuonHyper, ws=None,
+                update_out=None, bf16_shadow=None, stream=None) -> None:
+    """One Muon step for the holder of a parameter partition (muon_step_window):
+    momentum and Newton-Schulz on every listed matrix in full, the update
+    applied to the window (lo, hi, param_offset) of each entry in `partition`."""
+    torch = _torch()
+    if partition.dtype != torch.float32 or momentum.dtype != torch.float32:
+        raise TypeError("partition and momentum must be float32")
+    if _dtype_code(grads) != h.grad_dtype:
+        raise TypeError("grads dtype does not match hyper.grad_dtype")
+    numel = momentum.numel()
+    if grads.numel() != numel:
+        raise ValueError("grads and momentum must have the same numel")
+    arr, n = table(entries)
+    warr = windows(wins, n)
+    need = ctypes.c_size_t(0)
+    _check(load().muon_workspace_size(arr, n, ctypes.byref(h), ctypes.byref(need)))
+    if ws is None:
+        ws = workspace(need.value, momentum.device)
+    if update_out is not None and (update_out.dtype != torch.float32 or update_out.numel() != numel):
+        raise ValueError("update_out must be float32 with momentum's numel")
+    if bf16_shadow is not None and (bf16_shadow.element_size() != 2 or
+                                    bf16_shadow.numel() != partition.numel()):
+        raise ValueError("bf16_shadow must be a 16-bit tensor with the partition's numel")
+    _check(load().muon_step_window(_ptr(partition), partition.numel(), _ptr(grads), _ptr(momentum),
+                                   numel, arr, warr, n, ctypes.byref(h), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _ptr(update_out),
+                                   _ptr(bf16_shadow), _stream(momentum, stream)))
 
 
 def adamw(params, grads, m, v, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-10, weight_decay=0.0,

@@ -65,18 +65,20 @@ static void free_plan(Plan& p) {
   p.d_problems = nullptr;
 }
 
-static std::string plan_key(int device, const muon_matrix_t* t, int32_t n, const muon_hyper_t* h) {
+static std::string plan_key(int device, const muon_matrix_t* t, const muon_window_t* w, int32_t n,
+                            const muon_hyper_t* h) {
   std::string k;
-  const int32_t hdr[5] = {device, n, h->ns_method, h->ns_dtype, h->grad_dtype};
+  const int32_t hdr[6] = {device, n, h->ns_method, h->ns_dtype, h->grad_dtype, w != nullptr};
   k.append(reinterpret_cast<const char*>(hdr), sizeof(hdr));
   if (n > 0) k.append(reinterpret_cast<const char*>(t), sizeof(muon_matrix_t) * static_cast<size_t>(n));
+  if (n > 0 && w) k.append(reinterpret_cast<const char*>(w), sizeof(muon_window_t) * static_cast<size_t>(n));
   return k;
 }
 
-static int get_plan(const muon_matrix_t* t, int32_t n, const muon_hyper_t* h, Plan** out) {
+static int get_plan(const muon_matrix_t* t, const muon_window_t* w, int32_t n, const muon_hyper_t* h, Plan** out) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
-  const std::string key = plan_key(device, t, n, h);
+  const std::string key = plan_key(device, t, w, n, h);
   std::lock_guard<std::mutex> lk(g_plan_mu);
   auto it = g_plans.find(key);
   if (it != g_plans.end()) {
@@ -89,12 +91,11 @@ static int get_plan(const muon_matrix_t* t, int32_t n, const muon_hyper_t* h, Pl
     g_plans.clear();
   }
   std::unique_ptr<Plan> p(new Plan);
-  p->L = build_layout(t, n, h);
+  p->L = build_layout(t, n, h, w);
   std::vector<ProblemDesc> probs(p->L.problems.size());
   for (size_t i = 0; i < probs.size(); ++i) {
-    probs[i].src_off = p->L.problems[i].src_off;
-    probs[i].transposed = p->L.problems[i].transposed;
-    probs[i].pad = 0;
+    const HostProblem& hp = p->L.problems[i];
+    probs[i] = ProblemDesc{hp.src_off, hp.p_base, hp.lo, hp.hi, hp.transposed, {0, 0, 0}};
   }
   const size_t pb = std::max<size_t>(probs.size(), 1) * sizeof(ProblemDesc);
   if (hipMalloc(&p->d_problems, pb) != hipSuccess) {
@@ -389,9 +390,12 @@ int muon_workspace_size(const muon_matrix_t* table, int32_t n_entries, const muo
   return MUON_OK;
 }
 
-int muon_step(void* params, const void* grads, float* momentum, int64_t numel, const muon_matrix_t* table,
-              int32_t n_entries, const muon_hyper_t* h, void* workspace, size_t workspace_bytes, float* update_out,
-              uint16_t* bf16_shadow, void* stream) {
+// The shared body of muon_step and muon_step_window. `windows` NULL: params and
+// the shadow share the table's layout (params_numel == numel).
+static int step_impl(float* params, int64_t params_numel, const void* grads, float* momentum, int64_t numel,
+                     const muon_matrix_t* table, const muon_window_t* windows, int32_t n_entries,
+                     const muon_hyper_t* h, void* workspace, size_t workspace_bytes, float* update_out,
+                     uint16_t* bf16_shadow, void* stream) {
   g_err.clear();
   std::string err;
   int st = validate(table, n_entries, h, err);
@@ -402,6 +406,10 @@ int muon_step(void* params, const void* grads, float* momentum, int64_t numel, c
   for (int32_t i = 0; i < n_entries; ++i)
     if (table[i].offset + table[i].rows * table[i].cols > numel)
       return fail(MUON_ERR_RANGE, "entry " + std::to_string(i) + " ends beyond numel");
+  if (windows) {
+    st = validate_windows(table, windows, n_entries, params_numel, err);
+    if (st != MUON_OK) return fail(st, err);
+  }
   if (n_entries == 0 || numel == 0) return MUON_OK;
   if (workspace == nullptr) return fail(MUON_ERR_NULL, "workspace is NULL");
   if (misaligned(params, 16) || misaligned(grads, 16) || misaligned(momentum, 16) ||
@@ -409,9 +417,10 @@ int muon_step(void* params, const void* grads, float* momentum, int64_t numel, c
     return fail(MUON_ERR_ALIGN, "a buffer pointer is not 16-byte aligned");
   if (misaligned(workspace, 256)) return fail(MUON_ERR_ALIGN, "workspace is not 256-byte aligned");
   const size_t gsz = static_cast<size_t>(element_size(h->grad_dtype));
-  const size_t ne = static_cast<size_t>(numel);
+  const size_t ne = static_cast<size_t>(numel), pe = static_cast<size_t>(params_numel);
+  const char* pname = windows ? "partition" : "params";
   std::vector<Span> spans = {
-      {static_cast<const char*>(params), static_cast<const char*>(params) + ne * 4, "params"},
+      {reinterpret_cast<const char*>(params), reinterpret_cast<const char*>(params) + pe * 4, pname},
       {static_cast<const char*>(grads), static_cast<const char*>(grads) + ne * gsz, "grads"},
       {reinterpret_cast<const char*>(momentum), reinterpret_cast<const char*>(momentum) + ne * 4, "momentum"},
       {static_cast<const char*>(workspace), static_cast<const char*>(workspace) + workspace_bytes, "workspace"}};
@@ -419,13 +428,13 @@ int muon_step(void* params, const void* grads, float* momentum, int64_t numel, c
     spans.push_back({reinterpret_cast<const char*>(update_out), reinterpret_cast<const char*>(update_out) + ne * 4,
                      "update_out"});
   if (bf16_shadow)
-    spans.push_back({reinterpret_cast<const char*>(bf16_shadow), reinterpret_cast<const char*>(bf16_shadow) + ne * 2,
+    spans.push_back({reinterpret_cast<const char*>(bf16_shadow), reinterpret_cast<const char*>(bf16_shadow) + pe * 2,
                      "bf16_shadow"});
   std::string which;
   if (overlapping(spans, which)) return fail(MUON_ERR_OVERLAP, "buffers overlap: " + which);
 
   Plan* P = nullptr;
-  st = get_plan(table, n_entries, h, &P);
+  st = get_plan(table, windows, n_entries, h, &P);
   if (st != MUON_OK) return st;
   if (workspace_bytes < P->L.ws_bytes)
     return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(P->L.ws_bytes) + " bytes");
@@ -442,13 +451,32 @@ int muon_step(void* params, const void* grads, float* momentum, int64_t numel, c
   for (const Group& G : P->L.groups)
     MUON_LAUNCH("finalize_norm", s,
                 launch_finalize_norm(partials + G.partial_first, G.chunks, G.count, h->ns_eps, invn + G.first, s));
-  StepCtx c{P, h, ws, momentum, static_cast<float*>(params), update_out, bf16_shadow,
+  StepCtx c{P, h, ws, momentum, params, update_out, bf16_shadow,
             static_cast<float>(1.0 - static_cast<double>(h->lr) * static_cast<double>(h->weight_decay)), s};
   for (const Group& G : P->L.groups) {
     st = (h->ns_method == MUON_NS_STANDARD) ? run_standard(c, G) : run_gram(c, G);
     if (st != MUON_OK) return st;
   }
   return MUON_OK;
+}
+
+int muon_step(void* params, const void* grads, float* momentum, int64_t numel, const muon_matrix_t* table,
+              int32_t n_entries, const muon_hyper_t* h, void* workspace, size_t workspace_bytes, float* update_out,
+              uint16_t* bf16_shadow, void* stream) {
+  return step_impl(static_cast<float*>(params), numel, grads, momentum, numel, table, nullptr, n_entries, h,
+                   workspace, workspace_bytes, update_out, bf16_shadow, stream);
+}
+
+int muon_step_window(float* partition, int64_t partition_numel, const void* grads, float* momentum, int64_t numel,
+                     const muon_matrix_t* table, const muon_window_t* windows, int32_t n_entries,
+                     const muon_hyper_t* h, void* workspace, size_t workspace_bytes, float* update_out,
+                     uint16_t* bf16_shadow, void* stream) {
+  if (n_entries > 0 && windows == nullptr) {
+    g_err.clear();
+    return fail(MUON_ERR_NULL, "windows is NULL");
+  }
+  return step_impl(partition, partition_numel, grads, momentum, numel, table, windows,
+                   n_entries, h, workspace, workspace_bytes, update_out, bf16_shadow, stream);
 }
 
 int adamw_step(float* params, const void* grads, float* m, float* v, int64_t numel, const muon_adamw_hyper_t* h,

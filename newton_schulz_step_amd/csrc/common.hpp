@@ -19,12 +19,18 @@ typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 namespace muon {
 
 // Per-problem descriptor (one Newton-Schulz problem = a matrix or a split block).
+// A problem's elements, in stored (row-major) order, have local flat indices
+// e in [0, rows * cols). Momentum, gradient and update_out element e sits at
+// src_off + e; the step applies its update to e in [lo, hi) only, at params
+// index p_base + e (the whole problem at src_off + e for an ordinary step; a
+// window of a matrix that straddles a parameter partition otherwise).
 struct ProblemDesc {
-  int64_t src_off;     // element offset of the block in the packed buffers
+  int64_t src_off;
+  int64_t p_base;
+  int64_t lo, hi;
   int32_t transposed;  // 1: stored rows x cols with rows > cols, canonical = stored^T
-  int32_t pad;
+  int32_t pad[3];
 };
-
 
 // ---------------------------------------------------------------------------
 // element conversions (round to nearest even, the hardware default)

@@ -24,7 +24,8 @@
 // to Ct; a symmetric launch computes only tiles with ti >= tj and mirrors them
 // (on diagonal tiles each element is written exactly once, so the stored matrix
 // is exactly symmetric). The apply epilogue instead finishes the Muon step,
-// p <- p * decay - lr * v, at the matrix's stored (possibly transposed) position.
+// p <- p * decay - lr * v, at the matrix's stored (possibly transposed) position,
+// for the elements of the problem's window (the whole problem in an ordinary step).
 // Global loads of the epilogue (D, params) are issued in batches ahead of use.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -329,11 +330,15 @@ template <> struct Pack8<float> {
   __device__ __forceinline__ float get(int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
 };
 
-// p <- p * decay - lr * v for 8 consecutive stored elements starting at idx, with
-// optional copies of v (update_out) and of the new p rounded to bf16 (shadow).
-// `cnt` < 8 elements (ragged edge) or an unaligned idx take the scalar path.
-__device__ __forceinline__ void apply8(const GemmArgs& a, int64_t idx, int cnt, const float (&v)[8],
-                                       const f32x4& p0, const f32x4& p1, bool vec) {
+// One run of up to 8 consecutive stored elements e0 .. e0 + cnt - 1 of a problem:
+// v goes to update_out at uidx (every element), and p <- p * decay - lr * v, with
+// the optional bf16 copy of the new p (shadow), to the params at pidx for the
+// elements inside the problem's window [lo, hi). `vec`: a whole run inside the
+// window with pidx a multiple of 8 and uidx of 4, whose params the caller has
+// loaded into p0, p1; anything else takes the scalar path.
+__device__ __forceinline__ void apply8(const GemmArgs& a, int64_t pidx, int64_t uidx, int64_t e0, int cnt,
+                                       int64_t lo, int64_t hi, const float (&v)[8], const f32x4& p0,
+                                       const f32x4& p1, bool vec) {
   if (vec) {
     f32x4 o0, o1;
 #pragma unroll
@@ -341,14 +346,14 @@ __device__ __forceinline__ void apply8(const GemmArgs& a, int64_t idx, int cnt, 
       o0[e] = p0[e] * a.decay - a.lr * v[e];
       o1[e] = p1[e] * a.decay - a.lr * v[e + 4];
     }
-    f32x4* pp = reinterpret_cast<f32x4*>(a.params + idx);
+    f32x4* pp = reinterpret_cast<f32x4*>(a.params + pidx);
     pp[0] = o0;
     pp[1] = o1;
     if (a.update_out) {
       f32x4 u0, u1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) { u0[e] = v[e]; u1[e] = v[e + 4]; }
-      f32x4* up = reinterpret_cast<f32x4*>(a.update_out + idx);
+      f32x4* up = reinterpret_cast<f32x4*>(a.update_out + uidx);
       up[0] = u0;
       up[1] = u1;
     }
@@ -356,14 +361,16 @@ __device__ __forceinline__ void apply8(const GemmArgs& a, int64_t idx, int cnt, 
       u16x8 sh;
 #pragma unroll
       for (int e = 0; e < 4; ++e) { sh[e] = bf16_bits(o0[e]); sh[e + 4] = bf16_bits(o1[e]); }
-      *reinterpret_cast<u16x8*>(a.shadow + idx) = sh;
+      *reinterpret_cast<u16x8*>(a.shadow + pidx) = sh;
     }
   } else {
     for (int e = 0; e < cnt; ++e) {
-      const float pn = a.params[idx + e] * a.decay - a.lr * v[e];
-      a.params[idx + e] = pn;
-      if (a.update_out) a.update_out[idx + e] = v[e];
-      if (a.shadow) a.shadow[idx + e] = bf16_bits(pn);
+      if (a.update_out) a.update_out[uidx + e] = v[e];
+      if (e0 + e >= lo && e0 + e < hi) {
+        const float pn = a.params[pidx + e] * a.decay - a.lr * v[e];
+        a.params[pidx + e] = pn;
+        if (a.shadow) a.shadow[pidx + e] = bf16_bits(pn);
+      }
     }
   }
 }
@@ -391,16 +398,23 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   const int wm = wave >> 1, wn = wave & 1;
 
   float* stg = reinterpret_cast<float*>((wave < 2 ? lds0 : lds1) + (wave & 1) * 32 * SP * 4);
+  // staged element (row r, column c) of the 32-row block: the column is XORed with
+  // 8 * (bits 3-4 of r), which keeps 8-column chunks contiguous and puts the rows
+  // r, r + 8, r + 16, r + 24 that one column-pass read gathers in different banks
+  auto srow = [&](int r, int c) { return r * SP + (c ^ (((r >> 3) & 3) << 3)); };
   const int gi_w = ti * TILE + wm * HALF;   // first row of this wave's outputs
   const int gj_w = tj * TILE + wn * HALF;   // first column
   const bool diag = SYM && (ti == tj);
 
   int transposed = 0;
-  int64_t src = 0;
+  int64_t src = 0, pb = 0, wlo = 0, whi = 0;
   if constexpr (EPI == EPI_APPLY) {
     const ProblemDesc pd = a.probs[prob];
     transposed = pd.transposed;
     src = pd.src_off;
+    pb = pd.p_base;
+    wlo = pd.lo;
+    whi = pd.hi;
   }
   const int m = a.m_valid, n = a.n_valid;
 
@@ -429,7 +443,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
     for (int j = 0; j < WB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        stg[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * SP + j * 32 + (lane & 31)] = acc[i][j][r];
+        stg[srow((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), j * 32 + (lane & 31))] = acc[i][j][r];
     __syncthreads();
 
     constexpr bool APPLY = (EPI == EPI_APPLY);
@@ -441,8 +455,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       const int rr = q / CPR, cc = (q % CPR) * 8;
       const int gi = gi_w + i * 32 + rr, gj = gj_w + cc;
       float v[8];
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + rr * SP + cc);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + rr * SP + cc + 4);
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) { v[e] = a.alpha * s0[e]; v[e + 4] = a.alpha * s1[e]; }
       if (D != nullptr) {
@@ -454,7 +468,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
         for (int e = 0; e < 8; ++e)
           if (gi == gj + e) v[e] += a.gamma;
       }
-      float4* sp = reinterpret_cast<float4*>(stg + rr * SP + cc);
+      float4* sp = reinterpret_cast<float4*>(stg + srow(rr, cc));
       if constexpr (APPLY) {
         // the value itself goes back to the staging area (for the apply below,
         // or for the column pass of a transposed matrix)
@@ -482,9 +496,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
     if (!(APPLY && !transposed) && i + 1 < WB) load_d(i + 1);
 
     if (APPLY && !transposed) {
-      // stored m x n: canonical (gi, gj) at src + gi * n + gj. Each lane reads back
-      // the chunks it wrote; parameters are loaded PB chunks at a time, all of a
-      // batch before any is used.
+      // stored m x n: canonical (gi, gj) is stored element gi * n + gj. Each lane
+      // reads back the chunks it wrote; parameters are loaded PB chunks at a time,
+      // all of a batch before any is used.
 #pragma unroll
       for (int b = 0; b < NR; b += PB) {
         f32x4 p0[PB], p1[PB];
@@ -493,10 +507,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
         for (int u = 0; u < PB; ++u) {
           const int q = lane + 64 * (b + u);
           const int gi = gi_w + i * 32 + q / CPR, gj = gj_w + (q % CPR) * 8;
-          const int64_t idx = src + static_cast<int64_t>(gi) * n + gj;
-          pvec[u] = gi < m && gj + 8 <= n && (idx & 7) == 0;
+          const int64_t e = static_cast<int64_t>(gi) * n + gj;
+          pvec[u] = gi < m && gj + 8 <= n && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
           if (pvec[u]) {
-            const f32x4* pp = reinterpret_cast<const f32x4*>(a.params + idx);
+            const f32x4* pp = reinterpret_cast<const f32x4*>(a.params + pb + e);
             p0[u] = pp[0];
             p1[u] = pp[1];
           }
@@ -508,11 +522,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
           const int gi = gi_w + i * 32 + rr, gj = gj_w + cc;
           if (gi < m && gj < n) {
             float v[8];
-            const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + rr * SP + cc);
-            const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + rr * SP + cc + 4);
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
+            const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) { v[e] = s0[e]; v[e + 4] = s1[e]; }
-            apply8(a, src + static_cast<int64_t>(gi) * n + gj, min(8, n - gj), v, p0[u], p1[u], pvec[u]);
+            const int64_t e = static_cast<int64_t>(gi) * n + gj;
+            apply8(a, pb + e, src + e, e, min(8, n - gj), wlo, whi, v, p0[u], p1[u], pvec[u]);
           }
         }
       }
@@ -523,7 +538,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
     if (need_col) {
       __syncthreads();
       if constexpr (APPLY) {
-        // stored n x m: canonical (gi, gj) at src + gj * m + gi
+        // stored n x m: canonical (gi, gj) is stored element gj * m + gi
 #pragma unroll
         for (int b = 0; b < NC; b += PB) {
           f32x4 c0[PB], c1[PB];
@@ -532,10 +547,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
           for (int u = 0; u < PB; ++u) {
             const int q = lane + 64 * (b + u);
             const int gi = gi_w + i * 32 + (q & 3) * 8, gj = gj_w + (q >> 2);
-            const int64_t idx = src + static_cast<int64_t>(gj) * m + gi;
-            cvec[u] = gj < n && gi + 8 <= m && (idx & 7) == 0;
+            const int64_t e = static_cast<int64_t>(gj) * m + gi;
+            cvec[u] = gj < n && gi + 8 <= m && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
             if (cvec[u]) {
-              const f32x4* pp = reinterpret_cast<const f32x4*>(a.params + idx);
+              const f32x4* pp = reinterpret_cast<const f32x4*>(a.params + pb + e);
               c0[u] = pp[0];
               c1[u] = pp[1];
             }
@@ -548,8 +563,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
             if (gj < n && gi < m) {
               float w[8];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) w[e] = stg[(r8 + e) * SP + cc];
-              apply8(a, src + static_cast<int64_t>(gj) * m + gi, min(8, m - gi), w, c0[u], c1[u], cvec[u]);
+              for (int e = 0; e < 8; ++e) w[e] = stg[srow(r8 + e, cc)];
+              const int64_t e = static_cast<int64_t>(gj) * m + gi;
+              apply8(a, pb + e, src + e, e, min(8, m - gi), wlo, whi, w, c0[u], c1[u], cvec[u]);
             }
           }
         }
@@ -561,7 +577,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
           const int gi = gi_w + i * 32 + r8, gj = gj_w + cc;
           T o[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(stg[(r8 + e) * SP + cc]);
+          for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(stg[srow(r8 + e, cc)]);
           T* cp = Ct + static_cast<int64_t>(prob) * a.ct_ps + static_cast<int64_t>(gj) * a.ldct + gi;
           if (!diag || gi > gj) {
             st8<T>(cp, o);

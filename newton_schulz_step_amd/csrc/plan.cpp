@@ -73,7 +73,30 @@ int validate(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* 
   return MUON_OK;
 }
 
-Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h) {
+int validate_windows(const muon_matrix_t* table, const muon_window_t* windows, int32_t n_entries,
+                     int64_t partition_numel, std::string& err) {
+  if (n_entries > 0 && windows == nullptr) { err = "windows is NULL"; return MUON_ERR_NULL; }
+  if (partition_numel < 0) { err = "partition_numel < 0"; return MUON_ERR_RANGE; }
+  std::vector<std::pair<int64_t, int64_t>> spans;
+  for (int32_t i = 0; i < n_entries; ++i) {
+    const muon_window_t& w = windows[i];
+    const std::string at = " (window " + std::to_string(i) + ")";
+    const int64_t total = table[i].rows * table[i].cols;
+    if (w.lo < 0 || w.lo > w.hi || w.hi > total) { err = "window outside [0, rows * cols] or lo > hi" + at; return MUON_ERR_RANGE; }
+    if (w.hi > w.lo && (w.param_offset < 0 || w.param_offset + (w.hi - w.lo) > partition_numel)) {
+      err = "window does not fit in the partition" + at;
+      return MUON_ERR_RANGE;
+    }
+    if (w.hi > w.lo) spans.emplace_back(w.param_offset, w.hi - w.lo);
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i - 1].first + spans[i - 1].second > spans[i].first) { err = "windows overlap in the partition"; return MUON_ERR_OVERLAP; }
+  return MUON_OK;
+}
+
+Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h,
+                    const muon_window_t* windows) {
   Layout L;
   // canonical shape -> group, in order of first appearance
   std::map<std::pair<int64_t, int64_t>, int> gid;
@@ -98,9 +121,21 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
     }
     for (int64_t b = 0; b < nblk; ++b) {
       HostProblem p;
-      p.src_off = e.offset + b * pr * e.cols;
+      const int64_t first = b * pr * e.cols;       // entry flat index of the block's element 0
+      const int64_t size = pr * e.cols;
+      p.src_off = e.offset + first;
       p.transposed = pr > e.cols ? 1 : 0;
       p.entry = i;
+      if (windows == nullptr) {
+        p.lo = 0;
+        p.hi = size;
+        p.p_base = p.src_off;
+      } else {
+        const muon_window_t& w = windows[i];
+        p.lo = std::min(std::max(w.lo - first, int64_t(0)), size);
+        p.hi = std::min(std::max(w.hi - first, int64_t(0)), size);
+        p.p_base = w.param_offset - w.lo + first;
+      }
       per_group[g].push_back(p);
     }
   }

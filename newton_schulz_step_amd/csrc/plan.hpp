@@ -15,6 +15,8 @@ namespace muon {
 
 struct HostProblem {
   int64_t src_off;
+  int64_t p_base;      // params index of local flat element 0
+  int64_t lo, hi;      // local flat elements whose update is applied
   int32_t transposed;
   int32_t entry;
 };
@@ -47,8 +49,16 @@ int element_size(int dtype);
 // overlap). Returns a MUON_* status and fills `err`.
 int validate(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h, std::string& err);
 
-// Builds the layout of a validated table.
-Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h);
+// Checks the windows of a windowed step against the table and a partition of
+// `partition_numel` elements (bounds, lo <= hi, no two windows sharing a
+// partition element).
+int validate_windows(const muon_matrix_t* table, const muon_window_t* windows, int32_t n_entries,
+                     int64_t partition_numel, std::string& err);
+
+// Builds the layout of a validated table; `windows` may be NULL (every element
+// applied in place at its own offset).
+Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h,
+                    const muon_window_t* windows = nullptr);
 
 // Tile edge used for a group of `count` problems whose short side is m.
 int tile_for(int64_t m, int64_t count);

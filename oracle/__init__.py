@@ -8,5 +8,5 @@ from .muon_oracle import (  # noqa: F401
     ADAM_DEFAULTS, DEFAULT_NS_METHOD, MUON_DEFAULTS, NS_A, NS_B, NS_C, NS_EPS,
     NS_METHODS, NS_STEPS, adamw_step, gram_scale, momentum_update, muon_step,
     newton_schulz_gram, newton_schulz_standard, normalise, orthogonalise, pack,
-    problem_blocks, unpack)
+    partition_windows, problem_blocks, unpack, window_step)
 from .rounding import round_to, storer  # noqa: F401

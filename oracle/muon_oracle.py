@@ -51,7 +51,7 @@ The exact mode evaluates the products as they are.
 """
 from __future__ import annotations
 
-from typing import Callable, Dict, Optional, Sequence, Tuple
+from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -204,6 +204,47 @@ def muon_step(params: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
         p[span] = p[span] * (1.0 - lr * weight_decay)
         p[span] = p[span] - lr * O_all[span]
     return {"params": p, "momentum": M, "update": O_all}
+
+
+def partition_windows(table: Sequence[Tuple[int, int, int, int]], start: int,
+                      stop: int) -> List[Tuple[int, int, int]]:
+    """(lo, hi, param_offset) per entry for the holder of the flat partition
+    [start, stop) of the full layout: the part of each matrix (flattened in
+    stored row-major order) that falls in the partition, and where it sits in
+    the partition. (0, 0, 0) for a matrix the partition does not touch."""
+    out = []
+    for off, rows, cols, _s in table:
+        a, b = max(start, off), min(stop, off + rows * cols)
+        out.append((a - off, b - off, a - start) if a < b else (0, 0, 0))
+    return out
+
+
+def window_step(partition: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
+                table: Sequence[Tuple[int, int, int, int]],
+                windows: Sequence[Tuple[int, int, int]], lr: float = 0.02,
+                weight_decay: float = 0.0, **kw) -> Dict[str, np.ndarray]:
+    """One Muon step for the holder of a flat parameter partition.
+
+    [DS] ZeRO stage support, partition boundaries: when a Muon matrix straddles a
+    ZeRO partition boundary, every rank that holds part of it receives the whole
+    reduced gradient before the nonlinear update. Reading: the holder keeps the
+    whole momentum of the matrix, forms the whole update O as muon_step does,
+    and applies p <- p (1 - lr wd) - lr O to the elements of its own window only.
+    windows[i] = (lo, hi, param_offset): elements [lo, hi) of entry i, flat in
+    stored order, at partition[param_offset:param_offset + hi - lo].
+    grads/momentum are in the table's full layout; `kw` goes to muon_step.
+    Returns float64 copies of the new partition, the new momentum and O.
+    """
+    full = muon_step(np.zeros(len(momentum)), grads, momentum, table, lr=0.0, **kw)
+    part = np.asarray(partition, dtype=np.float64).copy()
+    O = full["update"]
+    for (off, _r, _c, _s), (lo, hi, po) in zip(table, windows):
+        if hi <= lo:
+            continue
+        span = slice(po, po + hi - lo)
+        part[span] = part[span] * (1.0 - lr * weight_decay)
+        part[span] = part[span] - lr * O[off + lo:off + hi]
+    return {"partition": part, "momentum": full["momentum"], "update": O}
 
 
 def adamw_step(p: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, lr: float,

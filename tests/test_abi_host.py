@@ -116,6 +116,42 @@ def test_step_rejects_before_any_device_work(lib):
     assert st == nss.ERR_RANGE and "entry 1" in msg
 
 
+def _raw_window(lib, entries, wins, numel, pnumel, h, part=FAKE + (4 << 36), grads=FAKE + (1 << 36),
+                mom=FAKE + (2 << 36), ws=FAKE + (3 << 36), upd=None, shadow=None, null_windows=False):
+    arr, n = nss.table(entries)
+    warr = None if null_windows else nss.windows(wins, n)
+    st = lib.muon_step_window(part, pnumel, grads, mom, numel, arr, warr, n, ctypes.byref(h), ws,
+                              1 << 40, upd, shadow, None)
+    return st, lib.muon_last_error().decode()
+
+
+def test_step_window_rejects_before_any_device_work(lib):
+    h = nss.hyper(ns_method="standard", ns_dtype="bf16")
+    ent = [(0, 64, 64, 0), (4096, 32, 64, 0)]
+    ok_w = [(1000, 4096, 0), (0, 100, 3096)]
+    # a matrix straddling both ends of the partition, another starting inside it
+    assert _raw_window(lib, ent, ok_w, 6144, 4096, h, null_windows=True)[0] == nss.ERR_NULL
+    assert _raw_window(lib, ent, ok_w, 6144, 4096, h, part=None)[0] == nss.ERR_NULL
+    assert _raw_window(lib, ent, [(10, 5, 0), (0, 0, 0)], 6144, 4096, h)[0] == nss.ERR_RANGE
+    assert _raw_window(lib, ent, [(-1, 5, 0), (0, 0, 0)], 6144, 4096, h)[0] == nss.ERR_RANGE
+    assert _raw_window(lib, ent, [(0, 4097, 0), (0, 0, 0)], 6144, 8192, h)[0] == nss.ERR_RANGE
+    st, msg = _raw_window(lib, ent, [(0, 4096, 1), (0, 0, 0)], 6144, 4096, h)
+    assert st == nss.ERR_RANGE and "window 0" in msg
+    assert _raw_window(lib, ent, [(0, 4096, -8), (0, 0, 0)], 6144, 8192, h)[0] == nss.ERR_RANGE
+    st, msg = _raw_window(lib, ent, [(0, 64, 0), (0, 64, 63)], 6144, 4096, h)
+    assert st == nss.ERR_OVERLAP and "windows overlap" in msg
+    # adjacent windows and empty windows anywhere are fine as far as validation goes
+    assert _raw_window(lib, ent, [(0, 64, 0), (0, 64, 64)], 6144, 128, h, ws=None)[0] == nss.ERR_NULL
+    assert _raw_window(lib, ent, [(7, 7, 0), (0, 0, 99)], 6144, 0, h, ws=None)[0] == nss.ERR_NULL
+    # the partition and the shadow are sized by partition_numel
+    assert _raw_window(lib, ent, ok_w, 6144, 4096, h, part=FAKE + (2 << 36) - 4096)[0] == nss.ERR_OVERLAP
+    st = _raw_window(lib, ent, ok_w, 6144, 4096, h, shadow=FAKE + (4 << 36) + 4096 * 4 - 16)[0]
+    assert st == nss.ERR_OVERLAP
+    assert _raw_window(lib, ent, ok_w, 6144, 4096, h, upd=FAKE + (4 << 36) - 6144 * 4 + 16)[0] == nss.ERR_OVERLAP
+    assert _raw_window(lib, ent, ok_w, 6143, 4096, h)[0] == nss.ERR_RANGE
+    assert _raw_window(lib, [(0, 64, 64, 0)], [(0, 1, 0)], 4096, 4096, h, part=FAKE + (4 << 36) + 8)[0] == nss.ERR_ALIGN
+
+
 def test_adamw_rejects_before_any_device_work(lib):
     h = nss.AdamWHyper()
     lib.muon_default_adamw_hyper(ctypes.byref(h))

@@ -417,6 +417,77 @@ def test_pack_unpack_roundtrip():
     assert np.count_nonzero(packed) <= used
 
 
+# --------------------------------------------------------------------------- partitions
+
+def _holders(n, cuts):
+    edges = [0] + list(cuts) + [n]
+    return list(zip(edges[:-1], edges[1:]))
+
+
+def test_partition_windows_tile_the_layout():
+    # every element of every matrix falls in exactly one holder's window, at the
+    # partition index that the flat layout gives it
+    tab, n = _table([(6, 10, 0), (12, 4, 0), (8, 8, 4)])
+    for cuts in ([], [30], [7, 61, 100], [60, 108], [1, 2, 3]):
+        seen = np.zeros(n, int)
+        for a, b in _holders(n, cuts):
+            for (off, r, c, _s), (lo, hi, po) in zip(tab, oracle.partition_windows(tab, a, b)):
+                assert 0 <= lo <= hi <= r * c
+                if hi > lo:
+                    assert a + po == off + lo and a + po + (hi - lo) <= b
+                    seen[off + lo:off + hi] += 1
+        for off, r, c, _s in tab:
+            assert np.all(seen[off:off + r * c] == 1)
+
+
+def test_window_union_equals_whole_step():
+    # [DS] partition boundaries: each holder gets the whole reduced gradient, so the
+    # holders' windows together carry exactly the update of the unpartitioned step
+    rng = np.random.default_rng(17)
+    tab, n = _table([(6, 10, 0), (12, 4, 0), (8, 8, 4), (5, 5, 0)])
+    p0, g, m0 = rng.standard_normal(n), rng.standard_normal(n), rng.standard_normal(n)
+    kw = dict(lr=0.03, weight_decay=0.1, mu=0.9, method="standard")
+    whole = oracle.muon_step(p0, g, m0, tab, **kw)
+    for cuts in ([33], [7, 61, 100], [60, 108, 120, 150]):
+        got = p0.copy()
+        for a, b in _holders(n, cuts):
+            out = oracle.window_step(p0[a:b], g, m0, tab, oracle.partition_windows(tab, a, b), **kw)
+            got[a:b] = out["partition"]
+            assert np.array_equal(out["momentum"], whole["momentum"])
+            assert np.array_equal(out["update"], whole["update"])
+        assert np.array_equal(got, whole["params"])
+
+
+def test_window_step_needs_the_whole_gradient():
+    # the rule matters: orthogonalising only the rows a holder owns gives another
+    # update, because the map from momentum to O is not elementwise
+    rng = np.random.default_rng(18)
+    rows, cols = 8, 12
+    M = rng.standard_normal((rows, cols))
+    O = oracle.orthogonalise(M, "standard")
+    O_top = oracle.orthogonalise(M[:4], "standard")
+    assert rel(O_top, O[:4]) > 0.1
+
+
+def test_window_step_special_cases():
+    rng = np.random.default_rng(19)
+    tab, n = _table([(6, 10, 0), (12, 4, 0)])
+    p0, g, m0 = rng.standard_normal(n), rng.standard_normal(n), rng.standard_normal(n)
+    whole = oracle.muon_step(p0, g, m0, tab, lr=0.02, weight_decay=0.1)
+    # one holder of everything: windows cover each matrix at its own offset
+    wins = [(0, r * c, off) for off, r, c, _s in tab]
+    out = oracle.window_step(p0, g, m0, tab, wins, lr=0.02, weight_decay=0.1)
+    assert np.array_equal(out["partition"], whole["params"])
+    # empty windows: the partition is untouched, the momentum still moves
+    part = rng.standard_normal(17)
+    out = oracle.window_step(part, g, m0, tab, [(0, 0, 0), (5, 5, 3)], lr=0.02)
+    assert np.array_equal(out["partition"], part)
+    assert np.array_equal(out["momentum"], whole["momentum"])
+    # lr = 0 leaves the window as it was
+    out = oracle.window_step(part, g, m0, tab, [(3, 10, 2), (0, 0, 0)], lr=0.0, weight_decay=0.3)
+    assert np.array_equal(out["partition"], part)
+
+
 # --------------------------------------------------------------------------- AdamW
 
 def test_adamw_first_step_closed_form():
