@@ -131,6 +131,18 @@ def summarize_counters(fetch_csv, write_csv, fetch_copy_csv, write_copy_csv, cop
            "hbm_write_bytes_per_launch": write_kib * 1024.0 * w_scale,
            "gemm_sha256_16": gemm_source_hash()}
     rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    run = f"python3 $REPO/bench.py --workload {workload} --method {method} --steps 2 --warmup 1 --no-cpu-baseline"
+    cal = "python3 $REPO/bench.py --copy-calibration"
+    rec["commands"] = [
+        "cd /tmp && export TMPDIR=/tmp",
+        f"rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- {run}",
+        f"rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- {run}",
+        f"rocprofv3 --pmc FETCH_SIZE -d <fetch_copy> -o run --output-format csv -- {cal}",
+        f"rocprofv3 --pmc WRITE_SIZE -d <write_copy> -o run --output-format csv -- {cal}",
+        "python3 bench.py --summarize-counters <fetch>/run_counter_collection.csv "
+        "<write>/run_counter_collection.csv <fetch_copy>/run_counter_collection.csv "
+        "<write_copy>/run_counter_collection.csv",
+    ]
     return rec
 
 

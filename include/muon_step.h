@@ -226,6 +226,82 @@ int muon_pack(void* packed, int64_t numel, const void* const* srcs, const muon_m
 int muon_unpack(void* const* dsts, const void* packed, int64_t numel, const muon_matrix_t* table,
                 int32_t n_entries, int32_t dtype, void* stream);
 
+/* ---- Owner planning (host only, no device work) --------------------------
+ * DMuon ("Z2 与 Z3 模式") gives every Muon-target matrix one owner, which alone
+ * runs its Newton-Schulz and keeps the authoritative copy; an owner packs all
+ * of its matrices into one contiguous buffer for the broadcast, and under
+ * DMuon-Z3 one layer's packed buffer at a time is resident. The pages do not
+ * say how owners are chosen. muon_plan_owners balances the nominal
+ * Newton-Schulz FLOPs of the owners greedily, largest first (LPT), and lays
+ * each owner's matrices out in its packed buffer, layer by layer. */
+
+/* One Muon-target matrix of the model: stored rows x cols (row-major),
+ * split_rows as in muon_matrix_t, and the index of the layer it belongs to. */
+typedef struct {
+  int64_t rows;
+  int64_t cols;
+  int64_t split_rows;
+  int32_t layer;
+  int32_t reserved;  /* set to 0 */
+} muon_param_t;
+
+/* Where a matrix went: its owner and its element offset in that owner's
+ * packed buffer (a multiple of the planning alignment). */
+typedef struct {
+  int32_t owner;
+  int32_t reserved;
+  int64_t offset;
+} muon_assign_t;
+
+/* What one owner holds. */
+typedef struct {
+  int64_t numel;            /* packed buffer length in elements (gaps included):
+                               what DMuon-Z2 keeps resident on this rank */
+  int64_t max_layer_numel;  /* longest single-layer span of the packed buffer:
+                               the DMuon-Z3 transient */
+  int64_t ns_flops;         /* nominal Newton-Schulz FLOPs of the owned problems */
+  int32_t n_matrices;
+  int32_t reserved;
+} muon_owner_t;
+
+/* Nominal Newton-Schulz FLOPs of one problem with short side m and long side
+ * n, counting 2 m k n per m x k by k x n product of the iteration as this
+ * library runs it, for `steps` steps. Standard: per step X X^T, A A and B X,
+ * i.e. steps (4 m^2 n + 2 m^3). Gram: R0 = X X^T and the final P X0
+ * (4 m^2 n), per step Q = a I + b R + c R R (2 m^3), and for every step but
+ * the first P <- Q P (2 m^3), for every step but the last R <- Q R Q
+ * (4 m^3): 4 m^2 n + (8 steps - 6) m^3. Returns -1 for invalid input or on
+ * int64 overflow. */
+int64_t muon_ns_flops(int64_t m, int64_t n, int32_t ns_method, int32_t steps);
+
+/* Assign n_params matrices to n_owners owners and lay out each owner's packed
+ * buffer.
+ *   Assignment: problems' FLOPs summed per matrix (muon_ns_flops over its
+ *   split blocks); matrices taken in order of decreasing FLOPs (ties: more
+ *   elements first, then lower index), each given to the owner with the
+ *   least FLOPs so far (ties: lower owner index).
+ *   Layout: each owner's matrices in order of (layer, index), each at the
+ *   next multiple of `align` elements (align >= 8 and a multiple of 8), so
+ *   each layer's matrices form one contiguous span.
+ *   assign   host, n_params records (out).
+ *   owners   host, n_owners records (out).
+ * Errors: MUON_ERR_NULL, MUON_ERR_BAD_SHAPE (a shape muon_step would reject,
+ * n_params < 0, n_owners < 1, layer < 0), MUON_ERR_ALIGN (bad align),
+ * MUON_ERR_BAD_METHOD, MUON_ERR_BAD_HYPER (steps outside [1, 64]),
+ * MUON_ERR_RANGE (int64 overflow). Nothing is written on error. */
+int muon_plan_owners(const muon_param_t* params, int32_t n_params, int32_t n_owners,
+                     int32_t ns_method, int32_t ns_steps, int64_t align,
+                     muon_assign_t* assign, muon_owner_t* owners);
+
+/* Elements sent per step on the shard group of n_ranks ranks, for P_M
+ * Muon-target elements ("Z2 与 Z3 模式", section on per-step communication):
+ * k (n_ranks - 1) / n_ranks * P_M with k = 2 for DMuon-Z2, 3 for DMuon-Z3,
+ * 3 for Muon on FSDP2-Z2 without dedicated owners, 4 on FSDP2-Z3.
+ *   zero_stage  2 or 3; dedicated 1 (DMuon) or 0 (no owners).
+ * Multiply by the element size of the wire format for bytes. Returns a
+ * negative value for invalid input. */
+double muon_comm_elements(int64_t p_m, int32_t n_ranks, int32_t zero_stage, int32_t dedicated);
+
 /* Message for the last failing call on this thread ("" if none). Valid until the
  * next call on this thread. */
 const char* muon_last_error(void);

@@ -8,8 +8,9 @@ binding; torch supplies device memory and streams.
 """
 from ._binding import (  # noqa: F401
     DTYPES, EXPORTED, LIB_PATH, NS_METHODS, STATUS_NAMES, AdamWHyper, KernelStat, MuonError,
-    MuonHyper, MuonMatrix, MuonWindow, adamw, hyper, load, pack, profile_begin, profile_end,
-    release_plans, step, step_window, table, unpack, version, windows, workspace, workspace_size)
+    MuonAssign, MuonHyper, MuonMatrix, MuonOwner, MuonParam, MuonWindow, adamw, comm_elements,
+    hyper, load, ns_flops, pack, plan_owners, profile_begin, profile_end, release_plans, step,
+    step_window, table, unpack, version, windows, workspace, workspace_size)
 from ._binding import (  # noqa: F401
     ERR_ALIGN, ERR_BAD_HYPER, ERR_BAD_METHOD, ERR_BAD_SHAPE, ERR_HIP, ERR_NULL, ERR_OVERLAP,
     ERR_RANGE, ERR_UNSUPPORTED, ERR_WORKSPACE, OK)

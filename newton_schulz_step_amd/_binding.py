@@ -29,7 +29,8 @@ NS_METHODS = {"standard": 0, "gram": 1}
 EXPORTED = (
     "muon_default_hyper", "muon_default_adamw_hyper", "muon_workspace_size", "muon_step",
     "muon_step_window", "adamw_step", "muon_pack", "muon_unpack", "muon_last_error", "muon_release_plans",
-    "muon_profile_begin", "muon_profile_end", "muon_version",
+    "muon_profile_begin", "muon_profile_end", "muon_version", "muon_ns_flops",
+    "muon_plan_owners", "muon_comm_elements",
 )
 
 
@@ -58,6 +59,21 @@ class MuonHyper(ctypes.Structure):
 
 class MuonWindow(ctypes.Structure):
     _fields_ = [("lo", ctypes.c_int64), ("hi", ctypes.c_int64), ("param_offset", ctypes.c_int64)]
+
+
+class MuonParam(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("split_rows", ctypes.c_int64),
+                ("layer", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class MuonAssign(ctypes.Structure):
+    _fields_ = [("owner", ctypes.c_int32), ("reserved", ctypes.c_int32), ("offset", ctypes.c_int64)]
+
+
+class MuonOwner(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("max_layer_numel", ctypes.c_int64),
+                ("ns_flops", ctypes.c_int64), ("n_matrices", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class AdamWHyper(ctypes.Structure):
@@ -99,10 +115,17 @@ def load() -> ctypes.CDLL:
         lib.adamw_step.argtypes = [vp, vp, vp, vp, i64, ctypes.POINTER(AdamWHyper), vp]
         lib.muon_pack.argtypes = [vp, i64, ctypes.POINTER(vp), pm, i32, i32, vp]
         lib.muon_unpack.argtypes = [ctypes.POINTER(vp), vp, i64, pm, i32, i32, vp]
+        lib.muon_ns_flops.argtypes = [i64, i64, i32, i32]
+        lib.muon_ns_flops.restype = i64
+        lib.muon_plan_owners.argtypes = [ctypes.POINTER(MuonParam), i32, i32, i32, i32, i64,
+                                         ctypes.POINTER(MuonAssign), ctypes.POINTER(MuonOwner)]
+        lib.muon_comm_elements.argtypes = [i64, i32, i32, i32]
+        lib.muon_comm_elements.restype = ctypes.c_double
         lib.muon_last_error.restype = ctypes.c_char_p
         lib.muon_version.restype = ctypes.c_char_p
         lib.muon_profile_end.argtypes = [ctypes.POINTER(KernelStat), i32, ctypes.POINTER(i32)]
-        for name in ("muon_workspace_size", "muon_step", "muon_step_window", "adamw_step", "muon_pack", "muon_unpack",
+        for name in ("muon_workspace_size", "muon_step", "muon_step_window", "muon_plan_owners",
+                     "adamw_step", "muon_pack", "muon_unpack",
                      "muon_release_plans", "muon_profile_begin", "muon_profile_end"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
@@ -275,6 +298,53 @@ def step_window(partition, grads, momentum, entries, wins, h: MuonHyper, ws=None
                                    numel, arr, warr, n, ctypes.byref(h), _ptr(ws),
                                    ws.numel() * ws.element_size(), _ptr(update_out),
                                    _ptr(bf16_shadow), _stream(momentum, stream)))
+
+
+def _method_code(method) -> int:
+    return NS_METHODS[method] if isinstance(method, str) else int(method)
+
+
+def ns_flops(m: int, n: int, method="standard", steps: int = 5) -> int:
+    """Nominal Newton-Schulz FLOPs of one problem with short side m, long side n."""
+    f = load().muon_ns_flops(m, n, _method_code(method), steps)
+    if f < 0:
+        raise ValueError("invalid problem for the FLOP model")
+    return int(f)
+
+
+def plan_owners(params: Sequence[Sequence[int]], n_owners: int, method="standard",
+                steps: int = 5, align: int = 64):
+    """Owner plan (muon_plan_owners) for matrices given as (rows, cols, split_rows,
+    layer). Returns (assign, owners): assign[i] = (owner, offset); owners[o] =
+    dict(numel, max_layer_numel, ns_flops, n_matrices, table), where `table` is
+    the owner's muon_step table [(offset, rows, cols, split_rows), ...] in
+    packed order, and `index` the matching input indices."""
+    rows = [tuple(p) for p in params]
+    n = len(rows)
+    arr = (MuonParam * max(n, 1))()
+    for i, (r, c, s, layer) in enumerate(rows):
+        arr[i] = MuonParam(r, c, s, layer, 0)
+    out_a = (MuonAssign * max(n, 1))()
+    out_o = (MuonOwner * max(n_owners, 1))()
+    _check(load().muon_plan_owners(arr, n, n_owners, _method_code(method), steps, align, out_a,
+                                   out_o))
+    assign = [(out_a[i].owner, out_a[i].offset) for i in range(n)]
+    owners = []
+    for o in range(n_owners):
+        idx = sorted((i for i in range(n) if assign[i][0] == o), key=lambda i: assign[i][1])
+        owners.append({"numel": out_o[o].numel, "max_layer_numel": out_o[o].max_layer_numel,
+                       "ns_flops": out_o[o].ns_flops, "n_matrices": out_o[o].n_matrices,
+                       "index": idx,
+                       "table": [(assign[i][1], rows[i][0], rows[i][1], rows[i][2]) for i in idx]})
+    return assign, owners
+
+
+def comm_elements(p_m: int, n_ranks: int, zero_stage: int = 2, dedicated: bool = True) -> float:
+    """Elements sent per step on the shard group (muon_comm_elements)."""
+    v = load().muon_comm_elements(p_m, n_ranks, zero_stage, int(bool(dedicated)))
+    if v < 0:
+        raise ValueError("invalid arguments for the communication model")
+    return v
 
 
 def adamw(params, grads, m, v, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-10, weight_decay=0.0,

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmuonstep.so")
 
-SOURCES = ["capi.hip", "plan.cpp", "gemm.hip", "elementwise.hip"]
+SOURCES = ["capi.hip", "plan.cpp", "planner.cpp", "gemm.hip", "elementwise.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -13,6 +13,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "planner.hpp"
 
 namespace muon {
 
@@ -570,6 +571,22 @@ int muon_unpack(void* const* dsts, const void* packed, int64_t numel, const muon
                      static_cast<int64_t>(table[i].rows * table[i].cols * esz)});
   }
   return run_copies(items, static_cast<hipStream_t>(stream));
+}
+
+int64_t muon_ns_flops(int64_t m, int64_t n, int32_t ns_method, int32_t steps) {
+  return ns_flops(m, n, ns_method, steps);
+}
+
+int muon_plan_owners(const muon_param_t* params, int32_t n_params, int32_t n_owners, int32_t ns_method,
+                     int32_t ns_steps, int64_t align, muon_assign_t* assign, muon_owner_t* owners) {
+  g_err.clear();
+  std::string err;
+  const int st = plan_owners(params, n_params, n_owners, ns_method, ns_steps, align, assign, owners, err);
+  return st == MUON_OK ? MUON_OK : fail(st, err);
+}
+
+double muon_comm_elements(int64_t p_m, int32_t n_ranks, int32_t zero_stage, int32_t dedicated) {
+  return comm_elements(p_m, n_ranks, zero_stage, dedicated);
 }
 
 int muon_release_plans(void) {

@@ -10,3 +10,4 @@ from .muon_oracle import (  # noqa: F401
     newton_schulz_gram, newton_schulz_standard, normalise, orthogonalise, pack,
     partition_windows, problem_blocks, unpack, window_step)
 from .rounding import round_to, storer  # noqa: F401
+from . import planner  # noqa: F401,E402
