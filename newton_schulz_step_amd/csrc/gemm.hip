@@ -177,8 +177,10 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int& prob, int& t
 // part of slice kt + 2. Spreading the global loads over the slice keeps the load
 // path busy steadily; issued in one burst per slice (as direct-to-LDS loads must
 // be, once the barrier frees their buffer) they stalled the MFMAs for about a
-// sixth of the time. One barrier per slice, before the last sub-step, publishes
-// slice kt + 1. The last slices reload slice nk - 1 (in bounds, never used).
+// sixth of the time. Each register waits only for its own load (vmcnt counts
+// loads in issue order), so a load has a whole slice of latency to hide. One
+// barrier per slice, before the last sub-step, publishes slice kt + 1. The last
+// slices reload slice nk - 1 (in bounds, never used).
 template <typename T, int TILE>
 __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, int tj, char* lds0, char* lds1,
                                          f32x16 (&acc)[Geo<T, TILE>::WB][Geo<T, TILE>::WB]) {
@@ -275,7 +277,8 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
   constexpr int B1 = (NV + 2) / 3, B2 = (2 * NV + 2) / 3;
   auto slice = [&](char* cur, char* nxt, int kt) {
     const int kl = min(kt + 2, nk - 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // slice kt + 1 is in registers
+    // no explicit vmcnt wait: the compiler waits for each register's own load
+    // right before its LDS write, so every load has a whole slice to arrive
     lwrite(0, B1, nxt);
     gload(0, B1, kl);
     rd(fa1, fb1, cur, 1);
@@ -436,15 +439,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   };
   load_d(0);
 
+  // Each wave stages into its own part of LDS, and one wave's LDS accesses are
+  // performed in program order, so after the first block (whose staging area the
+  // other waves may still be reading operands from) only the compiler has to be
+  // kept from reordering them: lds_order().
+  auto lds_order = []() { asm volatile("" ::: "memory"); };
 #pragma unroll
   for (int i = 0; i < WB; ++i) {
-    __syncthreads();   // every wave is past its last LDS read (main loop or previous block)
+    if (i == 0) __syncthreads();   // every wave is past its last main-loop LDS read
+    else lds_order();
 #pragma unroll
     for (int j = 0; j < WB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         stg[srow((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), j * 32 + (lane & 31))] = acc[i][j][r];
-    __syncthreads();
+    lds_order();
 
     constexpr bool APPLY = (EPI == EPI_APPLY);
 
@@ -536,7 +545,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
 
     // ---- column pass
     if (need_col) {
-      __syncthreads();
+      lds_order();
       if constexpr (APPLY) {
         // stored n x m: canonical (gi, gj) is stored element gj * m + gi
 #pragma unroll
