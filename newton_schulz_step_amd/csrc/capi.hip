@@ -210,13 +210,13 @@ static void set_full(GemmArgs& g, const Group& G, const void* P, int64_t p_ps, i
   g.group_m = -1;   // tiles column by column, each XCD on every eighth tile row
 }
 
-// X0 (and its transpose) of every problem of the group.
+// X0 of every problem of the group (canonical m x n, row-major).
 static int run_prep(const StepCtx& c, const Group& G) {
   const float* invn = reinterpret_cast<const float*>(c.ws + c.P->L.off_invnorm) + G.first;
   MUON_LAUNCH("prep_x0", c.s,
               launch_prep_x0(c.h->ns_dtype, c.M, c.P->d_problems + G.first, invn, G.count, static_cast<int>(G.m),
                              static_cast<int>(G.n), static_cast<int>(G.mp), static_cast<int>(G.np), c.ws + G.x[0],
-                             c.ws + G.y[0], c.s));
+                             c.s));
   return MUON_OK;
 }
 
@@ -227,7 +227,6 @@ static int run_standard(const StepCtx& c, const Group& G) {
   const int dt = c.h->ns_dtype;
   char* ws = c.ws;
   void* X[2] = {ws + G.x[0], ws + G.x[1]};
-  void* Y[2] = {ws + G.y[0], ws + G.y[1]};
   void* A = ws + G.a;
   void* B = ws + G.b;
   const int64_t xs = G.mp * G.np, ss = G.mp * G.mp;
@@ -248,14 +247,14 @@ static int run_standard(const StepCtx& c, const Group& G) {
     MUON_LAUNCH("ns_gemm_poly", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, g2, c.s));
 
     const bool last = (k == c.h->ns_steps - 1);
+    // B X with X itself as the K x N operand; X is also the a X term
     GemmArgs g3 = last ? apply_args(c, G) : GemmArgs{};
-    set_full(g3, G, B, ss, G.mp, Y[cur], xs, G.mp, kext(G.m, dt), G.mp, G.np);
+    set_full(g3, G, B, ss, G.mp, X[cur], xs, G.np, kext(G.m, dt), G.mp, G.np);
     g3.alpha = 1.0f;
     g3.beta = c.h->ns_a;
     g3.D = X[cur]; g3.d_ps = xs; g3.ldd = static_cast<int32_t>(G.np);
     if (!last) {
       g3.C = X[cur ^ 1]; g3.c_ps = xs; g3.ldc = static_cast<int32_t>(G.np);
-      g3.Ct = Y[cur ^ 1]; g3.ct_ps = xs; g3.ldct = static_cast<int32_t>(G.mp);
       MUON_LAUNCH("ns_gemm_update", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, g3, c.s));
       cur ^= 1;
     } else {
@@ -273,11 +272,9 @@ static int run_gram(const StepCtx& c, const Group& G) {
   const int dt = c.h->ns_dtype;
   char* ws = c.ws;
   void* X0 = ws + G.x[0];
-  void* Y0 = ws + G.y[0];
   void* R[2] = {ws + G.a, ws + G.r2};
   void* Qb = ws + G.b;
-  void* PT[2] = {ws + G.pt[0], ws + G.pt[1]};
-  void* Pm = ws + G.p;
+  void* Pb[2] = {ws + G.p[0], ws + G.p[1]};
   void* Tt = ws + G.t;
   const int64_t xs = G.mp * G.np, ss = G.mp * G.mp;
   const float s = (dt == MUON_DTYPE_F16) ? gram_scale(G.m) : 1.0f;
@@ -291,10 +288,9 @@ static int run_gram(const StepCtx& c, const Group& G) {
   MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, r0, c.s));
 
   int rc = 0, pc = 0;
-  const void* Pfinal = nullptr;
   for (int k = 0; k < S; ++k) {
-    // Q_k (symmetric); on the first step it is also P (and P^T)
-    void* Qdst = (k == 0) ? PT[0] : Qb;
+    // Q_k (symmetric); on the first step it is also P
+    void* Qdst = (k == 0) ? Pb[0] : Qb;
     GemmArgs gq{};
     set_sym(gq, G, R[rc], R[rc], kext(G.m, dt), G.mp, ss, Qdst);
     gq.alpha = c.h->ns_c / (s * s);
@@ -302,43 +298,33 @@ static int run_gram(const StepCtx& c, const Group& G) {
     gq.gamma = c.h->ns_a;
     gq.D = R[rc]; gq.d_ps = ss; gq.ldd = static_cast<int32_t>(G.mp);
     MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, gq, c.s));
-    if (k == 0) {
-      pc = 0;
-      Pfinal = PT[0];
-    } else {
-      // P <- Q P, with P^T as the second operand; stored transposed, or row-major after the last step
+    if (k > 0) {
+      // P <- Q P, P row-major as the K x N operand
       GemmArgs gp{};
-      set_full(gp, G, Qdst, ss, G.mp, PT[pc], ss, G.mp, kext(G.m, dt), G.mp, G.mp);
+      set_full(gp, G, Qdst, ss, G.mp, Pb[pc], ss, G.mp, kext(G.m, dt), G.mp, G.mp);
       gp.alpha = 1.0f;
-      if (k == S - 1) {
-        gp.C = Pm; gp.c_ps = ss; gp.ldc = static_cast<int32_t>(G.mp);
-        Pfinal = Pm;
-      } else {
-        gp.Ct = PT[pc ^ 1]; gp.ct_ps = ss; gp.ldct = static_cast<int32_t>(G.mp);
-        pc ^= 1;
-        Pfinal = nullptr;
-      }
+      gp.C = Pb[pc ^ 1]; gp.c_ps = ss; gp.ldc = static_cast<int32_t>(G.mp);
       MUON_LAUNCH("gram_gemm_full", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, gp, c.s));
+      pc ^= 1;
     }
     if (k < S - 1) {
-      const void* Qk = Qdst;
-      // T = R Q, stored as T^T
+      // T = R Q, stored as T^T (the second operand of the symmetric launch below)
       GemmArgs gt{};
-      set_full(gt, G, R[rc], ss, G.mp, Qk, ss, G.mp, kext(G.m, dt), G.mp, G.mp);
+      set_full(gt, G, R[rc], ss, G.mp, Qdst, ss, G.mp, kext(G.m, dt), G.mp, G.mp);
       gt.alpha = 1.0f;
       gt.Ct = Tt; gt.ct_ps = ss; gt.ldct = static_cast<int32_t>(G.mp);
       MUON_LAUNCH("gram_gemm_full", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, gt, c.s));
       // R <- Q T (symmetric: lower tiles, mirrored)
       GemmArgs gr{};
-      set_sym(gr, G, Qk, Tt, kext(G.m, dt), G.mp, ss, R[rc ^ 1]);
+      set_sym(gr, G, Qdst, Tt, kext(G.m, dt), G.mp, ss, R[rc ^ 1]);
       gr.alpha = 1.0f;
       MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, gr, c.s));
       rc ^= 1;
     }
   }
-  if (Pfinal == nullptr) return fail(MUON_ERR_HIP, "internal: gram chain left no final P");
+  // X = P X0, X0 row-major as the K x N operand, with the apply fused
   GemmArgs ga = apply_args(c, G);
-  set_full(ga, G, Pfinal, ss, G.mp, Y0, xs, G.mp, kext(G.m, dt), G.mp, G.np);
+  set_full(ga, G, Pb[pc], ss, G.mp, X0, xs, G.np, kext(G.m, dt), G.mp, G.np);
   ga.alpha = 1.0f;
   MUON_LAUNCH("gram_gemm_apply", c.s, launch_ns_gemm(dt, G.tile, false, EPI_APPLY, ga, c.s));
   return MUON_OK;

@@ -116,9 +116,10 @@ hipError_t launch_finalize_norm(const float* partials, int64_t chunks, int n_pro
 
 // ---------------------------------------------------------------------------
 // X0 = round(M / (||M||_F + eps)) in canonical orientation (short side = rows),
-// written twice: X (mp x np, row-major) and Y = X^T (np x mp). A 64x64 tile is
-// read in the stored orientation (coalesced), turned in LDS, and written in both
-// orientations (coalesced). Padding rows/columns are written as zeros.
+// written as X (mp x np, row-major). Each block covers a 64x64 tile. A matrix
+// stored as is goes straight through; one stored transposed is read in its
+// stored orientation (coalesced) and turned in LDS. Padding rows/columns are
+// written as zeros.
 
 template <typename T>
 __device__ __forceinline__ void store16(T* dst, const float (&v)[16]) {
@@ -146,7 +147,7 @@ __device__ __forceinline__ void store16(T* dst, const float (&v)[16]) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const ProblemDesc* probs, const float* inv_norm,
-                                                      int m, int n, int mp, int np, T* X, T* Y) {
+                                                      int m, int n, int mp, int np, T* X) {
   __shared__ float tile[64][65];
   const int tiles_j = np >> 6;
   const int per = (mp >> 6) * tiles_j;
@@ -156,75 +157,73 @@ __global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const Prob
   const ProblemDesc pd = probs[p];
   const float inv = inv_norm[p];
   const int r = threadIdx.x >> 2, c16 = (threadIdx.x & 3) * 16;
+  T* dst = X + p * static_cast<int64_t>(mp) * np + static_cast<int64_t>(i0 + r) * np + j0 + c16;
+  float v[16];
 
   if (!pd.transposed) {
-    // stored m x n: element (i, j) at src + i * n + j; this thread reads row i0 + r
+    // stored m x n: element (i, j) at src + i * n + j; this thread covers row i0 + r
     const int gi = i0 + r;
     const int64_t base = pd.src_off + static_cast<int64_t>(gi) * n + j0 + c16;
     if (gi < m && j0 + c16 + 16 <= n && (base & 3) == 0) {
-      const f32x4* s = reinterpret_cast<const f32x4*>(M + base);
+      const f32x4* src = reinterpret_cast<const f32x4*>(M + base);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 w = s[q];
+        const f32x4 w = src[q];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tile[r][c16 + q * 4 + e] = w[e];
+        for (int e = 0; e < 4; ++e) v[q * 4 + e] = w[e] * inv;
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int gj = j0 + c16 + e;
-        tile[r][c16 + e] = (gi < m && gj < n) ? M[base + e] : 0.0f;
+        v[e] = (gi < m && gj < n) ? M[base + e] * inv : 0.0f;
       }
+    }
+    store16<T>(dst, v);
+    return;
+  }
+
+  // stored n x m: element (i, j) at src + j * m + i; this thread reads stored row j0 + r
+  const int gj = j0 + r;
+  const int64_t base = pd.src_off + static_cast<int64_t>(gj) * m + i0 + c16;
+  if (gj < n && i0 + c16 + 16 <= m && (base & 3) == 0) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(M + base);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 w = src[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[c16 + q * 4 + e][r] = w[e];
     }
   } else {
-    // stored n x m: element (i, j) at src + j * m + i; this thread reads stored row j0 + r
-    const int gj = j0 + r;
-    const int64_t base = pd.src_off + static_cast<int64_t>(gj) * m + i0 + c16;
-    if (gj < n && i0 + c16 + 16 <= m && (base & 3) == 0) {
-      const f32x4* s = reinterpret_cast<const f32x4*>(M + base);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 w = s[q];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) tile[c16 + q * 4 + e][r] = w[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int gi = i0 + c16 + e;
-        tile[c16 + e][r] = (gj < n && gi < m) ? M[base + e] : 0.0f;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int gi = i0 + c16 + e;
+      tile[c16 + e][r] = (gj < n && gi < m) ? M[base + e] : 0.0f;
     }
   }
-  __syncthreads();
-
-  const int64_t xs = static_cast<int64_t>(mp) * np;
-  float v[16];
+  __syncthreads();   // the transposed flag is the same for the whole block
 #pragma unroll
   for (int e = 0; e < 16; ++e) v[e] = tile[r][c16 + e] * inv;
-  store16<T>(X + p * xs + static_cast<int64_t>(i0 + r) * np + j0 + c16, v);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = tile[c16 + e][r] * inv;
-  store16<T>(Y + p * xs + static_cast<int64_t>(j0 + r) * mp + i0 + c16, v);
+  store16<T>(dst, v);
 }
 
 hipError_t launch_prep_x0(int ns_dtype, const float* M, const ProblemDesc* probs, const float* inv_norm,
-                          int n_problems, int m, int n, int mp, int np, void* X, void* Y, hipStream_t s) {
+                          int n_problems, int m, int n, int mp, int np, void* X, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(n_problems) * (mp / 64) * (np / 64);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   switch (ns_dtype) {
     case MUON_DTYPE_BF16:
       hipLaunchKernelGGL(prep_x0_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, M, probs, inv_norm, m, n, mp, np,
-                         static_cast<__bf16*>(X), static_cast<__bf16*>(Y));
+                         static_cast<__bf16*>(X));
       break;
     case MUON_DTYPE_F16:
       hipLaunchKernelGGL(prep_x0_kernel<_Float16>, dim3(blocks), dim3(256), 0, s, M, probs, inv_norm, m, n, mp, np,
-                         static_cast<_Float16*>(X), static_cast<_Float16*>(Y));
+                         static_cast<_Float16*>(X));
       break;
     default:
       hipLaunchKernelGGL(prep_x0_kernel<float>, dim3(blocks), dim3(256), 0, s, M, probs, inv_norm, m, n, mp, np,
-                         static_cast<float*>(X), static_cast<float*>(Y));
+                         static_cast<float*>(X));
   }
   return hipGetLastError();
 }

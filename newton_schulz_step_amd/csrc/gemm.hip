@@ -1,21 +1,27 @@
 // Batched MFMA GEMM of the Newton-Schulz iteration (gfx950).
 //
-// Every product of the iteration is written in "NT" form, C = P * Q^T, where
-// both operands are row-major with the contraction index contiguous:
-//   A = X X^T          P = X,  Q = X                 (symmetric output)
-//   A A  (A symmetric) P = A,  Q = A                 (symmetric output)
-//   B X                P = B,  Q = Y = X^T           (Y is kept alongside X)
-//   Gram: R0 = X0 X0^T, R R, R Q, Q (R Q), Q P, P X0 likewise.
-// Keeping both X and X^T (the update's epilogue writes both) removes every
-// transposed operand load from the main loop.
+// The first operand P is always row-major with the contraction index K
+// contiguous. The second operand comes in two layouts:
+//   NT (symmetric launches): Q is N x K, K contiguous, C = P Q^T
+//     A = X X^T          P = X,  Q = X
+//     A A  (A symmetric) P = A,  Q = A
+//     Gram: R0 = X0 X0^T, Q = a I + b R + c R R, R <- Q T (T stored as T^T)
+//   NN (full launches): Q is K x N, N contiguous, C = P Q
+//     B X                P = B,  Q = X
+//     Gram: Q P, R Q, P X0
+// The NN operand is staged in LDS as K rows and read with the transposed LDS
+// read of gfx950, so X is stored only once, row-major, and no product needs a
+// transposed copy of its operand.
 //
 // Tile: TILE x TILE outputs per workgroup (256 or 128), 4 waves in a 2x2 grid,
 // each wave owning (TILE/2)^2 outputs as 32x32 MFMA blocks. K advances in
 // 128-byte slices (64 bf16/f16 or 32 f32 elements). Operand slices are staged
-// through registers into a double buffer in LDS;
-// rows are 128 bytes, with the 16-byte chunk index XOR-swizzled by the row so
-// that the MFMA operand reads (ds_read_b128, 32 rows at one chunk) spread over
-// all banks. MFMA operands are double-buffered in registers so that reads of
+// through registers into a double buffer in LDS. K-contiguous operands use
+// 128-byte rows, with the 16-byte chunk index XOR-swizzled by the row so that
+// the MFMA operand reads (ds_read_b128, 32 rows at one chunk) spread over all
+// banks; an NN operand uses rows of TILE elements with the 32-byte pair index
+// XOR-swizzled by the row, so the four rows of a transposed read fall in
+// different banks. MFMA operands are double-buffered in registers so that reads of
 // the next sub-step overlap the current MFMAs; one barrier per K slice.
 //
 // Epilogue: each wave stages 32 rows of its fp32 accumulators in LDS, applies
@@ -58,6 +64,26 @@ template <> struct Mfma<float> {
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Transposed LDS read of 16-bit elements (gfx950 ds_read_b64_tr_b16). In each
+// group of 16 lanes, lane s supplies the address of 4 consecutive elements;
+// lane l of the group receives element l % 4 of the rows addressed by lanes
+// l / 4, l / 4 + 4, l / 4 + 8 and l / 4 + 12. With lane s pointing at row
+// s / 4, columns 4 (s % 4) .. + 3 of a 4 x 16 block, lane l receives column l of
+// the block, rows 0..3: one MFMA operand quarter read across rows.
+template <typename T> struct TrRead;
+template <> struct TrRead<__bf16> {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4;
+  static __device__ __forceinline__ v4 get(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4*)(p));
+  }
+};
+template <> struct TrRead<_Float16> {
+  typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 v4;
+  static __device__ __forceinline__ v4 get(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) v4*)(p));
+  }
+};
 
 // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
 // contiguous range of logical tiles so that neighbours share its L2.
@@ -181,41 +207,62 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int& prob, int& t
 // loads in issue order), so a load has a whole slice of latency to hide. One
 // barrier per slice, before the last sub-step, publishes slice kt + 1. The last
 // slices reload slice nk - 1 (in bounds, never used).
-template <typename T, int TILE>
+template <typename T, int TILE, bool NN>
 __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, int tj, char* lds0, char* lds1,
                                          f32x16 (&acc)[Geo<T, TILE>::WB][Geo<T, TILE>::WB]) {
   using Gm = Geo<T, TILE>;
   constexpr int ESZ = Gm::ESZ, HALF = Gm::HALF, WB = Gm::WB, OPB = Gm::OPB, LOADS = Gm::LOADS;
   constexpr int NV = 2 * LOADS;                       // 16-byte vectors per lane per slice (P, then Q)
   constexpr int NMF = WB * WB * Mfma<T>::kInstr;      // MFMA instructions per sub-step
+  constexpr int KS = 128 / ESZ;                       // K elements per slice
+  constexpr int RB = TILE * ESZ;                      // NN: bytes of one K row of the Q slice
+  constexpr int CPRQ = RB / 16;                       // NN: 16-byte chunks per K row
+  // LDS reads per sub-step: A, then B (NN: two transposed quarter reads per 16-bit
+  // operand, four element reads per fp32 operand)
+  constexpr int BRD = !NN ? 1 : (ESZ == 2 ? 2 : 4);
+  constexpr int NRD = WB + WB * BRD;
   using V = typename Gm::V;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- per-lane global source and LDS destination of each 16-byte vector: lane l
-  // of load `it` covers row (wave * LOADS + it) * 8 + l / 8, chunk l % 8; the chunk
-  // is stored at position chunk ^ swz(row) of its 128-byte LDS row
+  // ---- per-lane global source and LDS destination of each 16-byte vector.
+  // P (and Q unless NN): lane l of load `it` covers row (wave * LOADS + it) * 8 +
+  // l / 8, chunk l % 8 of a 128-byte K slice; the chunk is stored at position
+  // chunk ^ swz(row) of its 128-byte LDS row.
+  // NN Q (stored K x N, N contiguous): the slice is KS rows of TILE columns; load
+  // `it` of thread t covers chunk (it * 256 + t) of the row-major slice, stored in
+  // an RB-byte LDS row with its 32-byte pair index XORed with (row & 7).
   const char* Pb = static_cast<const char*>(a.P) +
                    (static_cast<int64_t>(prob) * a.p_ps + static_cast<int64_t>(ti) * TILE * a.ldp) * ESZ;
   const char* Qb = static_cast<const char*>(a.Q) +
-                   (static_cast<int64_t>(prob) * a.q_ps + static_cast<int64_t>(tj) * TILE * a.ldq) * ESZ;
+                   (static_cast<int64_t>(prob) * a.q_ps +
+                    (NN ? static_cast<int64_t>(tj) * TILE : static_cast<int64_t>(tj) * TILE * a.ldq)) * ESZ;
   const char* gp[NV];
   int wofs[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int it = v % LOADS;
-    const int r = (wave * LOADS + it) * 8 + (lane >> 3);
-    const int c = lane & 7;
-    if (v < LOADS) gp[v] = Pb + static_cast<int64_t>(r) * a.ldp * ESZ + c * 16;
-    else gp[v] = Qb + static_cast<int64_t>(r) * a.ldq * ESZ + c * 16;
-    wofs[v] = (v < LOADS ? 0 : OPB) + r * 128 + ((c ^ swz(r)) << 4);
+    if (NN && v >= LOADS) {
+      const int id = it * 256 + static_cast<int>(threadIdx.x);
+      const int kr = id / CPRQ, c = id % CPRQ;
+      gp[v] = Qb + static_cast<int64_t>(kr) * a.ldq * ESZ + c * 16;
+      wofs[v] = OPB + kr * RB + (((c >> 1) ^ (kr & 7)) << 5) + ((c & 1) << 4);
+    } else {
+      const int r = (wave * LOADS + it) * 8 + (lane >> 3);
+      const int c = lane & 7;
+      if (v < LOADS) gp[v] = Pb + static_cast<int64_t>(r) * a.ldp * ESZ + c * 16;
+      else gp[v] = Qb + static_cast<int64_t>(r) * a.ldq * ESZ + c * 16;
+      wofs[v] = (v < LOADS ? 0 : OPB) + r * 128 + ((c ^ swz(r)) << 4);
+    }
   }
+  // byte step of one K slice: 128 bytes along a row, or KS rows of Q for NN
+  const int64_t qstep = NN ? static_cast<int64_t>(KS) * a.ldq * ESZ : 128;
   u16x8 rv[NV];
   auto gload = [&](int v0, int v1, int kt) {
-    const int64_t kb = static_cast<int64_t>(kt) * 128;
+    const int64_t kp = static_cast<int64_t>(kt) * 128, kq = static_cast<int64_t>(kt) * qstep;
 #pragma unroll
-    for (int v = v0; v < v1; ++v) rv[v] = *reinterpret_cast<const u16x8*>(gp[v] + kb);
+    for (int v = v0; v < v1; ++v) rv[v] = *reinterpret_cast<const u16x8*>(gp[v] + (v < LOADS ? kp : kq));
   };
   auto lwrite = [&](int v0, int v1, char* st) {
 #pragma unroll
@@ -235,6 +282,31 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
       boff[i][ks] = rb * 128 + ((c ^ swz(rb)) << 4);
     }
   }
+  // NN B operand, offsets at sub-step 0 (sub-step ks adds ks * (KS / 4) rows).
+  // 16-bit: lane l (group g = l / 16, s = l % 16) reads quarter h from row
+  // 8 (g / 2) + 4 h + s / 4, columns 16 (g % 2) + 4 (s % 4) .. + 3 of block j.
+  // fp32: element e of lane l is row 4 (l / 32) + e, column l % 32 of block j.
+  int bnn[WB][BRD];
+  if constexpr (NN) {
+#pragma unroll
+    for (int j = 0; j < WB; ++j) {
+      const int nb = wn * HALF + j * 32;
+#pragma unroll
+      for (int h = 0; h < BRD; ++h) {
+        int kr, col;
+        if constexpr (ESZ == 2) {
+          const int g = lane >> 4, sl = lane & 15;
+          kr = 8 * (g >> 1) + 4 * h + (sl >> 2);
+          col = nb + 16 * (g & 1) + 4 * (sl & 3);
+        } else {
+          kr = 4 * (lane >> 5) + h;
+          col = nb + (lane & 31);
+        }
+        const int cb = col * ESZ;   // byte column
+        bnn[j][h] = OPB + kr * RB + ((((cb >> 5) ^ (kr & 7))) << 5) + (cb & 31);
+      }
+    }
+  }
 
 #pragma unroll
   for (int i = 0; i < WB; ++i)
@@ -247,8 +319,24 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
   auto rd = [&](V (&xa)[WB], V (&xb)[WB], const char* buf, int ks) {
 #pragma unroll
     for (int i = 0; i < WB; ++i) xa[i] = *reinterpret_cast<const V*>(buf + aoff[i][ks]);
+    if constexpr (!NN) {
 #pragma unroll
-    for (int j = 0; j < WB; ++j) xb[j] = *reinterpret_cast<const V*>(buf + OPB + boff[j][ks]);
+      for (int j = 0; j < WB; ++j) xb[j] = *reinterpret_cast<const V*>(buf + OPB + boff[j][ks]);
+    } else if constexpr (ESZ == 2) {
+      const int kofs = ks * (KS / 4) * RB;
+#pragma unroll
+      for (int j = 0; j < WB; ++j) {
+        const auto lo = TrRead<T>::get(buf + bnn[j][0] + kofs);
+        const auto hi = TrRead<T>::get(buf + bnn[j][1] + kofs);
+        xb[j] = __builtin_bit_cast(V, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    } else {
+      const int kofs = ks * (KS / 4) * RB;
+#pragma unroll
+      for (int j = 0; j < WB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xb[j][e] = *reinterpret_cast<const float*>(buf + bnn[j][e] + kofs);
+    }
   };
   auto mm = [&](V (&xa)[WB], V (&xb)[WB]) {
 #pragma unroll
@@ -256,7 +344,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
 #pragma unroll
       for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], acc[i][j]);
   };
-  // scheduling of one sub-step: its nw LDS writes and global loads, then its 2 WB
+  // scheduling of one sub-step: its nw LDS writes and global loads, then its NRD
   // operand reads, each paired with MFMAs; then a fence
   auto region = [&](int nw) {
 #pragma unroll
@@ -266,9 +354,9 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
     }
 #pragma unroll
-    for (int q = 0; q < 2 * WB; ++q) {
+    for (int q = 0; q < NRD; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, NMF / (2 * WB) > 1 ? NMF / (2 * WB) - 1 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF / NRD > 1 ? NMF / NRD - 1 : 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -600,7 +688,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   }
 }
 
-template <typename T, int TILE, bool SYM, int EPI>
+template <typename T, int TILE, bool SYM, int EPI, bool NN>
 __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
   using Gm = Geo<T, TILE>;
   __shared__ __attribute__((aligned(1024))) char lds0[2 * Gm::OPB];
@@ -608,26 +696,29 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
   int prob, ti, tj;
   decode_tile<SYM>(a, prob, ti, tj);
   f32x16 acc[Gm::WB][Gm::WB];
-  mainloop<T, TILE>(a, prob, ti, tj, lds0, lds1, acc);
+  mainloop<T, TILE, NN>(a, prob, ti, tj, lds0, lds1, acc);
   epilogue<T, TILE, SYM, EPI>(a, prob, ti, tj, lds0, lds1, acc);
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 
-template <typename T, int TILE, bool SYM, int EPI>
+template <typename T, int TILE, bool SYM, int EPI, bool NN>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
   if (a.total_tiles <= 0) return hipSuccess;
   // the main loop runs whole pairs of 128-byte K slices
   if (a.K <= 0 || a.K % (2 * 128 / static_cast<int>(sizeof(T))) != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ns_gemm<T, TILE, SYM, EPI>), dim3(a.total_tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((ns_gemm<T, TILE, SYM, EPI, NN>), dim3(a.total_tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+// Symmetric launches take both operands K-contiguous (NT); full launches take the
+// second operand stored K x N (NN).
 template <typename T, int TILE>
 static hipError_t launch_tile(bool sym, int epi, const GemmArgs& a, hipStream_t s) {
-  if (epi == EPI_APPLY) return launch_t<T, TILE, false, EPI_APPLY>(a, s);
-  return sym ? launch_t<T, TILE, true, EPI_STORE>(a, s) : launch_t<T, TILE, false, EPI_STORE>(a, s);
+  if (sym) return epi == EPI_STORE ? launch_t<T, TILE, true, EPI_STORE, false>(a, s) : hipErrorInvalidValue;
+  if (epi == EPI_APPLY) return launch_t<T, TILE, false, EPI_APPLY, true>(a, s);
+  return launch_t<T, TILE, false, EPI_STORE, true>(a, s);
 }
 
 template <typename T>

@@ -7,11 +7,14 @@ namespace muon {
 
 enum { EPI_STORE = 0, EPI_APPLY = 1 };
 
-// One batched NT GEMM launch: for every problem p of a shape group,
-//   C_p = epilogue(alpha * P_p Q_p^T + beta * D_p + gamma * I).
-// Strides (_ps) are elements between consecutive problems; ld* are row pitches
-// in elements. K, and the tile-padded extents, are multiples of the tile sizes,
-// so the main loop needs no bounds checks (padding holds zeros).
+// One batched GEMM launch: for every problem p of a shape group,
+//   C_p = epilogue(alpha * P_p op(Q_p) + beta * D_p + gamma * I),
+// where P_p is rows x K, K contiguous. Symmetric launches take Q_p as N x K, K
+// contiguous (op = transpose, "NT"); full launches take it as K x N, N
+// contiguous (op = identity, "NN"). Strides (_ps) are elements between
+// consecutive problems; ld* are row pitches in elements. K, and the
+// tile-padded extents, are multiples of the tile sizes, so the main loop needs
+// no bounds checks (padding holds zeros).
 struct GemmArgs {
   const void* P; int64_t p_ps; int32_t ldp;
   const void* Q; int64_t q_ps; int32_t ldq;
@@ -40,10 +43,10 @@ hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const 
 hipError_t launch_finalize_norm(const float* partials, int64_t chunks, int n_problems, float eps, float* inv_norm,
                                 hipStream_t s);
 
-// X0 (canonical m x n, padded mp x np) and Y0 = X0^T (np x mp) of every problem of a group,
+// X0 (canonical m x n, padded mp x np, row-major) of every problem of a group,
 // X0 = round(M * inv_norm); padding zero.
 hipError_t launch_prep_x0(int ns_dtype, const float* M, const ProblemDesc* probs, const float* inv_norm,
-                          int n_problems, int m, int n, int mp, int np, void* X, void* Y, hipStream_t s);
+                          int n_problems, int m, int n, int mp, int np, void* X, hipStream_t s);
 
 hipError_t launch_adamw(int grad_dtype, float* p, const void* g, float* m, float* v, int64_t n,
                         float beta1, float beta2, float step_size, float inv_bc2, float eps,

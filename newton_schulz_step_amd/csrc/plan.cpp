@@ -168,19 +168,16 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
     const size_t xbytes = cnt * static_cast<size_t>(G.mp * G.np) * esz;
     const size_t sbytes = cnt * static_cast<size_t>(G.mp * G.mp) * esz;
     G.x[0] = off; off = align256(off + xbytes);
-    G.y[0] = off; off = align256(off + xbytes);
     if (h->ns_method == MUON_NS_STANDARD) {
       G.x[1] = off; off = align256(off + xbytes);
-      G.y[1] = off; off = align256(off + xbytes);
       G.a = off; off = align256(off + sbytes);
       G.b = off; off = align256(off + sbytes);
     } else {
       G.a = off; off = align256(off + sbytes);      // R
       G.r2 = off; off = align256(off + sbytes);     // next R
       G.b = off; off = align256(off + sbytes);      // Q
-      G.pt[0] = off; off = align256(off + sbytes);  // P^T
-      G.pt[1] = off; off = align256(off + sbytes);  // P^T (next)
-      G.p = off; off = align256(off + sbytes);      // P, row-major, after the last step
+      G.p[0] = off; off = align256(off + sbytes);   // P
+      G.p[1] = off; off = align256(off + sbytes);   // next P
       G.t = off; off = align256(off + sbytes);      // (R Q)^T
     }
   }

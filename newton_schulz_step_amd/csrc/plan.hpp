@@ -30,9 +30,9 @@ struct Group {
   int64_t chunks = 0;                // momentum blocks per problem (ceil(m n / kMomChunk))
   size_t partial_first = 0;          // index of the group's first per-block partial sum
   // workspace byte offsets
-  size_t x[2] = {0, 0}, y[2] = {0, 0};   // X and X^T, ping-pong (standard); X0 / Y0 in [0] (gram)
+  size_t x[2] = {0, 0};                  // X, ping-pong (standard); X0 in [0] (gram)
   size_t a = 0, b = 0;                   // standard: A, B; gram: R, Q
-  size_t r2 = 0, pt[2] = {0, 0}, p = 0, t = 0;   // gram: next R, P^T (ping-pong), P, (R Q)^T
+  size_t r2 = 0, p[2] = {0, 0}, t = 0;   // gram: next R, P (ping-pong), (R Q)^T
 };
 
 struct Layout {
