@@ -254,8 +254,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize_counters:
         ns_dtype = "bf16" if args.method == "standard" else "f16"
-        symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0EEEvNS_8GemmArgsE" if ns_dtype == "bf16"
-                  else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0EEEvNS_8GemmArgsE")
+        symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0ELb1EEEvNS_9GemmBatchE" if ns_dtype == "bf16"
+                  else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0ELb0EEEvNS_9GemmBatchE")
         rec = summarize_counters(*args.summarize_counters, copy_bytes=1 << 32, symbol=symbol,
                                  workload=args.workload, method=args.method)
         with open(traffic_path(args.workload, args.method), "w") as f:
@@ -317,14 +317,14 @@ def main() -> int:
         dom_kind = "ns_gemm_update"
         tile = 256 if probs and probs[0][0] >= 512 else 128
         dt_name = {"bf16": "__bf16", "f16": "_Float16", "f32": "float"}[ns_dtype]
-        dom_kernel = f"muon::ns_gemm<{dt_name}, {tile}, false, 0>"
+        dom_kernel = f"muon::ns_gemm<{dt_name}, {tile}, false, 0, true>"
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
         dom_flops = sum(2.0 * m * m * n for m, n in probs) * (h.ns_steps - 1) * args.steps
     else:
         # symmetric launches: R0 = X0 X0^T, five Q = aI + bR + cRR, four R <- Q (R Q)
         dom_kind = "gram_gemm_sym"
         tile = 256 if probs and probs[0][0] >= 512 else 128
-        dom_kernel = f"muon::ns_gemm<{'_Float16' if ns_dtype == 'f16' else 'float'}, {tile}, true, 0>"
+        dom_kernel = f"muon::ns_gemm<{'_Float16' if ns_dtype == 'f16' else 'float'}, {tile}, true, 0, false>"
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
         dom_flops = sum(2.0 * m * m * n + 18.0 * m ** 3 for m, n in probs) * args.steps
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None

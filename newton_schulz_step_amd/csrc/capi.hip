@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -183,7 +184,7 @@ static GemmArgs apply_args(const StepCtx& c, const Group& G) {
 }
 
 // C = alpha * P Q^T (+ beta D + gamma I) over the problems of a group, symmetric
-// (lower tiles, mirrored) when `sym`.
+// (lower tiles, mirrored); both operands K-contiguous.
 static void set_sym(GemmArgs& g, const Group& G, const void* P, const void* Q, int64_t K, int64_t ldpq, int64_t pq_ps,
                     void* C) {
   const int T = static_cast<int>(G.mp / G.tile);
@@ -195,9 +196,10 @@ static void set_sym(GemmArgs& g, const Group& G, const void* P, const void* Q, i
   g.total_tiles = g.tiles_per_problem * G.count;
   g.C = C; g.c_ps = G.mp * G.mp; g.ldc = static_cast<int32_t>(G.mp);
   g.Ct = C; g.ct_ps = G.mp * G.mp; g.ldct = static_cast<int32_t>(G.mp);
-  g.group_m = -1;   // tiles column by column, each XCD on every eighth tile row
 }
 
+// C = alpha * P Q (+ beta D) over the problems of a group: P rows x K
+// (K-contiguous), Q K x cols (cols contiguous).
 static void set_full(GemmArgs& g, const Group& G, const void* P, int64_t p_ps, int64_t ldp, const void* Q,
                      int64_t q_ps, int64_t ldq, int64_t K, int64_t rows, int64_t cols) {
   g.P = P; g.p_ps = p_ps; g.ldp = static_cast<int32_t>(ldp);
@@ -207,7 +209,38 @@ static void set_full(GemmArgs& g, const Group& G, const void* P, int64_t p_ps, i
   g.tiles_n = static_cast<int32_t>(cols / G.tile);
   g.tiles_per_problem = g.tiles_m * g.tiles_n;
   g.total_tiles = g.tiles_per_problem * G.count;
-  g.group_m = -1;   // tiles column by column, each XCD on every eighth tile row
+}
+
+// A set of shape groups that share the tile edge; each NS product is one launch
+// over all of them. Groups are ordered by decreasing n, so the tiles with the
+// longest K (X X^T) are dispatched first and the short ones fill the tail.
+using GroupSet = std::vector<const Group*>;
+
+static std::vector<GroupSet> group_sets(const Layout& L) {
+  std::vector<GroupSet> sets;
+  for (int tile : {256, 128}) {
+    GroupSet all;
+    for (const Group& G : L.groups)
+      if (G.tile == tile) all.push_back(&G);
+    std::stable_sort(all.begin(), all.end(), [](const Group* x, const Group* y) { return x->n > y->n; });
+    for (size_t i = 0; i < all.size(); i += kBatchGroups)
+      sets.emplace_back(all.begin() + i, all.begin() + std::min(all.size(), i + kBatchGroups));
+  }
+  return sets;
+}
+
+// One launch of `kind` over the per-group arguments `v` (at most kBatchGroups).
+static int launch_batch(const char* kind, const StepCtx& c, int tile, bool sym, int epi,
+                        const std::vector<GemmArgs>& v) {
+  GemmBatch b{};
+  b.n = static_cast<int32_t>(v.size());
+  b.start[0] = 0;
+  for (size_t g = 0; g < v.size(); ++g) {
+    b.g[g] = v[g];
+    b.start[g + 1] = b.start[g] + v[g].total_tiles;
+  }
+  MUON_LAUNCH(kind, c.s, launch_ns_gemm(c.h->ns_dtype, tile, sym, epi, b, c.s));
+  return MUON_OK;
 }
 
 // X0 of every problem of the group (canonical m x n, row-major).
@@ -223,42 +256,51 @@ static int run_prep(const StepCtx& c, const Group& G) {
 // Standard quintic (DeepSpeed-Muon article, section 核心算子): per step
 //   A = X X^T;  B = b A + c A A;  X <- a X + B X,
 // the last step's epilogue applying p <- p * decay - lr * X.
-static int run_standard(const StepCtx& c, const Group& G) {
+static int run_standard(const StepCtx& c, const GroupSet& set) {
   const int dt = c.h->ns_dtype;
+  const int tile = set.front()->tile;
   char* ws = c.ws;
-  void* X[2] = {ws + G.x[0], ws + G.x[1]};
-  void* A = ws + G.a;
-  void* B = ws + G.b;
-  const int64_t xs = G.mp * G.np, ss = G.mp * G.mp;
-  int st = run_prep(c, G);
-  if (st != MUON_OK) return st;
+  int st;
+  for (const Group* G : set)
+    if ((st = run_prep(c, *G)) != MUON_OK) return st;
   int cur = 0;
   for (int k = 0; k < c.h->ns_steps; ++k) {
-    GemmArgs g1{};
-    set_sym(g1, G, X[cur], X[cur], kext(G.n, dt), G.np, xs, A);
-    g1.alpha = 1.0f;
-    MUON_LAUNCH("ns_gemm_xxt", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, g1, c.s));
-
-    GemmArgs g2{};
-    set_sym(g2, G, A, A, kext(G.m, dt), G.mp, ss, B);
-    g2.alpha = c.h->ns_c;
-    g2.beta = c.h->ns_b;
-    g2.D = A; g2.d_ps = ss; g2.ldd = static_cast<int32_t>(G.mp);
-    MUON_LAUNCH("ns_gemm_poly", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, g2, c.s));
-
     const bool last = (k == c.h->ns_steps - 1);
-    // B X with X itself as the K x N operand; X is also the a X term
-    GemmArgs g3 = last ? apply_args(c, G) : GemmArgs{};
-    set_full(g3, G, B, ss, G.mp, X[cur], xs, G.np, kext(G.m, dt), G.mp, G.np);
-    g3.alpha = 1.0f;
-    g3.beta = c.h->ns_a;
-    g3.D = X[cur]; g3.d_ps = xs; g3.ldd = static_cast<int32_t>(G.np);
+    std::vector<GemmArgs> v1, v2, v3;
+    for (const Group* Gp : set) {
+      const Group& G = *Gp;
+      void* X[2] = {ws + G.x[0], ws + G.x[1]};
+      void* A = ws + G.a;
+      void* B = ws + G.b;
+      const int64_t xs = G.mp * G.np, ss = G.mp * G.mp;
+      GemmArgs g1{};
+      set_sym(g1, G, X[cur], X[cur], kext(G.n, dt), G.np, xs, A);
+      g1.alpha = 1.0f;
+      v1.push_back(g1);
+
+      GemmArgs g2{};
+      set_sym(g2, G, A, A, kext(G.m, dt), G.mp, ss, B);
+      g2.alpha = c.h->ns_c;
+      g2.beta = c.h->ns_b;
+      g2.D = A; g2.d_ps = ss; g2.ldd = static_cast<int32_t>(G.mp);
+      v2.push_back(g2);
+
+      // B X with X itself as the K x N operand; X is also the a X term
+      GemmArgs g3 = last ? apply_args(c, G) : GemmArgs{};
+      set_full(g3, G, B, ss, G.mp, X[cur], xs, G.np, kext(G.m, dt), G.mp, G.np);
+      g3.alpha = 1.0f;
+      g3.beta = c.h->ns_a;
+      g3.D = X[cur]; g3.d_ps = xs; g3.ldd = static_cast<int32_t>(G.np);
+      if (!last) { g3.C = X[cur ^ 1]; g3.c_ps = xs; g3.ldc = static_cast<int32_t>(G.np); }
+      v3.push_back(g3);
+    }
+    if ((st = launch_batch("ns_gemm_xxt", c, tile, true, EPI_STORE, v1)) != MUON_OK) return st;
+    if ((st = launch_batch("ns_gemm_poly", c, tile, true, EPI_STORE, v2)) != MUON_OK) return st;
     if (!last) {
-      g3.C = X[cur ^ 1]; g3.c_ps = xs; g3.ldc = static_cast<int32_t>(G.np);
-      MUON_LAUNCH("ns_gemm_update", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, g3, c.s));
+      if ((st = launch_batch("ns_gemm_update", c, tile, false, EPI_STORE, v3)) != MUON_OK) return st;
       cur ^= 1;
     } else {
-      MUON_LAUNCH("ns_gemm_apply", c.s, launch_ns_gemm(dt, G.tile, false, EPI_APPLY, g3, c.s));
+      if ((st = launch_batch("ns_gemm_apply", c, tile, false, EPI_APPLY, v3)) != MUON_OK) return st;
     }
   }
   return MUON_OK;
@@ -268,66 +310,97 @@ static int run_standard(const StepCtx& c, const Group& G) {
 // R's entries in fp16's normal range; b and c are rescaled to match); per step
 //   Q = a I + (b/s) R + (c/s^2) R R;  P <- Q P (P = Q first);  R <- Q (R Q)
 // (not after the last step); finally X = P X0 with the apply fused.
-static int run_gram(const StepCtx& c, const Group& G) {
+static int run_gram(const StepCtx& c, const GroupSet& set) {
   const int dt = c.h->ns_dtype;
-  char* ws = c.ws;
-  void* X0 = ws + G.x[0];
-  void* R[2] = {ws + G.a, ws + G.r2};
-  void* Qb = ws + G.b;
-  void* Pb[2] = {ws + G.p[0], ws + G.p[1]};
-  void* Tt = ws + G.t;
-  const int64_t xs = G.mp * G.np, ss = G.mp * G.mp;
-  const float s = (dt == MUON_DTYPE_F16) ? gram_scale(G.m) : 1.0f;
+  const int tile = set.front()->tile;
   const int S = c.h->ns_steps;
-  int st = run_prep(c, G);
-  if (st != MUON_OK) return st;
+  char* ws = c.ws;
+  int st;
+  for (const Group* G : set)
+    if ((st = run_prep(c, *G)) != MUON_OK) return st;
+  auto scale = [&](const Group& G) { return (dt == MUON_DTYPE_F16) ? gram_scale(G.m) : 1.0f; };
+  auto R = [&](const Group& G, int i) -> void* { return ws + (i == 0 ? G.a : G.r2); };
+  auto Pb = [&](const Group& G, int i) -> void* { return ws + G.p[i]; };
 
-  GemmArgs r0{};
-  set_sym(r0, G, X0, X0, kext(G.n, dt), G.np, xs, R[0]);
-  r0.alpha = s;
-  MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, r0, c.s));
+  std::vector<GemmArgs> v;
+  for (const Group* Gp : set) {
+    const Group& G = *Gp;
+    GemmArgs r0{};
+    set_sym(r0, G, ws + G.x[0], ws + G.x[0], kext(G.n, dt), G.np, G.mp * G.np, R(G, 0));
+    r0.alpha = scale(G);
+    v.push_back(r0);
+  }
+  if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
 
   int rc = 0, pc = 0;
   for (int k = 0; k < S; ++k) {
     // Q_k (symmetric); on the first step it is also P
-    void* Qdst = (k == 0) ? Pb[0] : Qb;
-    GemmArgs gq{};
-    set_sym(gq, G, R[rc], R[rc], kext(G.m, dt), G.mp, ss, Qdst);
-    gq.alpha = c.h->ns_c / (s * s);
-    gq.beta = c.h->ns_b / s;
-    gq.gamma = c.h->ns_a;
-    gq.D = R[rc]; gq.d_ps = ss; gq.ldd = static_cast<int32_t>(G.mp);
-    MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, gq, c.s));
+    auto Qdst = [&](const Group& G) -> void* { return k == 0 ? Pb(G, 0) : ws + G.b; };
+    v.clear();
+    for (const Group* Gp : set) {
+      const Group& G = *Gp;
+      const int64_t ss = G.mp * G.mp;
+      const float s = scale(G);
+      GemmArgs gq{};
+      set_sym(gq, G, R(G, rc), R(G, rc), kext(G.m, dt), G.mp, ss, Qdst(G));
+      gq.alpha = c.h->ns_c / (s * s);
+      gq.beta = c.h->ns_b / s;
+      gq.gamma = c.h->ns_a;
+      gq.D = R(G, rc); gq.d_ps = ss; gq.ldd = static_cast<int32_t>(G.mp);
+      v.push_back(gq);
+    }
+    if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
     if (k > 0) {
       // P <- Q P, P row-major as the K x N operand
-      GemmArgs gp{};
-      set_full(gp, G, Qdst, ss, G.mp, Pb[pc], ss, G.mp, kext(G.m, dt), G.mp, G.mp);
-      gp.alpha = 1.0f;
-      gp.C = Pb[pc ^ 1]; gp.c_ps = ss; gp.ldc = static_cast<int32_t>(G.mp);
-      MUON_LAUNCH("gram_gemm_full", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, gp, c.s));
+      v.clear();
+      for (const Group* Gp : set) {
+        const Group& G = *Gp;
+        const int64_t ss = G.mp * G.mp;
+        GemmArgs gp{};
+        set_full(gp, G, Qdst(G), ss, G.mp, Pb(G, pc), ss, G.mp, kext(G.m, dt), G.mp, G.mp);
+        gp.alpha = 1.0f;
+        gp.C = Pb(G, pc ^ 1); gp.c_ps = ss; gp.ldc = static_cast<int32_t>(G.mp);
+        v.push_back(gp);
+      }
+      if ((st = launch_batch("gram_gemm_full", c, tile, false, EPI_STORE, v)) != MUON_OK) return st;
       pc ^= 1;
     }
     if (k < S - 1) {
       // T = R Q, stored as T^T (the second operand of the symmetric launch below)
-      GemmArgs gt{};
-      set_full(gt, G, R[rc], ss, G.mp, Qdst, ss, G.mp, kext(G.m, dt), G.mp, G.mp);
-      gt.alpha = 1.0f;
-      gt.Ct = Tt; gt.ct_ps = ss; gt.ldct = static_cast<int32_t>(G.mp);
-      MUON_LAUNCH("gram_gemm_full", c.s, launch_ns_gemm(dt, G.tile, false, EPI_STORE, gt, c.s));
+      v.clear();
+      for (const Group* Gp : set) {
+        const Group& G = *Gp;
+        const int64_t ss = G.mp * G.mp;
+        GemmArgs gt{};
+        set_full(gt, G, R(G, rc), ss, G.mp, Qdst(G), ss, G.mp, kext(G.m, dt), G.mp, G.mp);
+        gt.alpha = 1.0f;
+        gt.Ct = ws + G.t; gt.ct_ps = ss; gt.ldct = static_cast<int32_t>(G.mp);
+        v.push_back(gt);
+      }
+      if ((st = launch_batch("gram_gemm_full", c, tile, false, EPI_STORE, v)) != MUON_OK) return st;
       // R <- Q T (symmetric: lower tiles, mirrored)
-      GemmArgs gr{};
-      set_sym(gr, G, Qdst, Tt, kext(G.m, dt), G.mp, ss, R[rc ^ 1]);
-      gr.alpha = 1.0f;
-      MUON_LAUNCH("gram_gemm_sym", c.s, launch_ns_gemm(dt, G.tile, true, EPI_STORE, gr, c.s));
+      v.clear();
+      for (const Group* Gp : set) {
+        const Group& G = *Gp;
+        GemmArgs gr{};
+        set_sym(gr, G, Qdst(G), ws + G.t, kext(G.m, dt), G.mp, G.mp * G.mp, R(G, rc ^ 1));
+        gr.alpha = 1.0f;
+        v.push_back(gr);
+      }
+      if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
       rc ^= 1;
     }
   }
   // X = P X0, X0 row-major as the K x N operand, with the apply fused
-  GemmArgs ga = apply_args(c, G);
-  set_full(ga, G, Pb[pc], ss, G.mp, X0, xs, G.np, kext(G.m, dt), G.mp, G.np);
-  ga.alpha = 1.0f;
-  MUON_LAUNCH("gram_gemm_apply", c.s, launch_ns_gemm(dt, G.tile, false, EPI_APPLY, ga, c.s));
-  return MUON_OK;
+  v.clear();
+  for (const Group* Gp : set) {
+    const Group& G = *Gp;
+    GemmArgs ga = apply_args(c, G);
+    set_full(ga, G, Pb(G, pc), G.mp * G.mp, G.mp, ws + G.x[0], G.mp * G.np, G.np, kext(G.m, dt), G.mp, G.np);
+    ga.alpha = 1.0f;
+    v.push_back(ga);
+  }
+  return launch_batch("gram_gemm_apply", c, tile, false, EPI_APPLY, v);
 }
 
 }  // namespace muon
@@ -440,8 +513,8 @@ static int step_impl(float* params, int64_t params_numel, const void* grads, flo
                 launch_finalize_norm(partials + G.partial_first, G.chunks, G.count, h->ns_eps, invn + G.first, s));
   StepCtx c{P, h, ws, momentum, params, update_out, bf16_shadow,
             static_cast<float>(1.0 - static_cast<double>(h->lr) * static_cast<double>(h->weight_decay)), s};
-  for (const Group& G : P->L.groups) {
-    st = (h->ns_method == MUON_NS_STANDARD) ? run_standard(c, G) : run_gram(c, G);
+  for (const GroupSet& set : group_sets(P->L)) {
+    st = (h->ns_method == MUON_NS_STANDARD) ? run_standard(c, set) : run_gram(c, set);
     if (st != MUON_OK) return st;
   }
   return MUON_OK;

@@ -85,13 +85,6 @@ template <> struct TrRead<_Float16> {
   }
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-// contiguous range of logical tiles so that neighbours share its L2.
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-  const int q = n >> 3, r = n & 7, x = b & 7, k = b >> 3;
-  return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
-}
-
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> { using U = u16x8; };
 template <> struct Vec8<_Float16> { using U = u16x8; };
@@ -136,15 +129,18 @@ template <typename T, int TILE> struct Geo {
   using V = typename Mfma<T>::V;
 };
 
-// Logical tile (problem, tile row, tile column) of this workgroup.
+// Logical tile (problem, tile row, tile column) of block b of a launch.
+// Symmetric launches walk the lower triangle column by column (tj = 0: rows
+// 0..T-1, tj = 1: rows 1..T-1, ...). Full launches go column-major within a
+// problem: the workgroups running at one time cover whole tile columns of one
+// problem, and XCD x (workgroups are dealt round-robin over the 8 XCDs) takes
+// tile rows x, x + 8, ... of every column, so each Q strip is fetched from HBM
+// once and shared through the last-level cache.
 template <bool SYM>
-__device__ __forceinline__ void decode_tile(const GemmArgs& a, int& prob, int& ti, int& tj) {
-  if (SYM && a.group_m < 0) {
-    // lower triangle column by column (tj = 0: rows 0..T-1, tj = 1: rows 1..T-1,
-    // ...), no XCD remap
-    const int b = blockIdx.x;
-    prob = b / a.tiles_per_problem;
-    int t = b - prob * a.tiles_per_problem;
+__device__ __forceinline__ void decode_tile(const GemmArgs& a, int b, int& prob, int& ti, int& tj) {
+  prob = b / a.tiles_per_problem;
+  int t = b - prob * a.tiles_per_problem;
+  if constexpr (SYM) {
     const int T = a.tiles_m;
     int c = 0;
     while (t >= T - c) {
@@ -153,39 +149,9 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int& prob, int& t
     }
     tj = c;
     ti = c + t;
-    return;
-  }
-  if (!SYM && a.group_m < 0) {
-    // column-major within a problem, no XCD remap: the workgroups running at
-    // one time cover whole tile columns of one problem; XCD x (workgroups are
-    // dealt round-robin) takes tile rows x, x + 8, ... of every column, so each
-    // Q strip is fetched from HBM once and shared through the last-level cache
-    const int b = blockIdx.x;
-    prob = b / a.tiles_per_problem;
-    const int t = b - prob * a.tiles_per_problem;
+  } else {
     tj = t / a.tiles_m;
     ti = t - tj * a.tiles_m;
-    return;
-  }
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  prob = bid / a.tiles_per_problem;
-  const int t = bid - prob * a.tiles_per_problem;
-  if constexpr (SYM) {
-    ti = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-    while (ti * (ti + 1) / 2 > t) --ti;
-    tj = t - ti * (ti + 1) / 2;
-  } else {
-    // groups of G tile rows, walked column by column, so that the P strips of
-    // a group and each Q strip are read while they are still cached
-    const int G = a.group_m > 0 ? a.group_m : 4;
-    const int per_group = G * a.tiles_n;
-    const int g = t / per_group;
-    const int first = g * G;
-    const int gsz = min(a.tiles_m - first, G);
-    const int w = t - g * per_group;
-    ti = first + w % gsz;
-    tj = w / gsz;
   }
 }
 
@@ -688,13 +654,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   }
 }
 
+// One launch covers up to kBatchGroups shape groups: block b belongs to the last
+// group g with start[g] <= b.
 template <typename T, int TILE, bool SYM, int EPI, bool NN>
-__global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
+__global__ __launch_bounds__(256) void ns_gemm(GemmBatch batch) {
   using Gm = Geo<T, TILE>;
   __shared__ __attribute__((aligned(1024))) char lds0[2 * Gm::OPB];
   __shared__ __attribute__((aligned(1024))) char lds1[2 * Gm::OPB];
+  const int bid = static_cast<int>(blockIdx.x);
+  int g = 0;
+#pragma unroll
+  for (int q = 1; q < kBatchGroups; ++q)
+    if (q < batch.n && bid >= batch.start[q]) g = q;
+  const GemmArgs& a = batch.g[g];
   int prob, ti, tj;
-  decode_tile<SYM>(a, prob, ti, tj);
+  decode_tile<SYM>(a, bid - batch.start[g], prob, ti, tj);
   f32x16 acc[Gm::WB][Gm::WB];
   mainloop<T, TILE, NN>(a, prob, ti, tj, lds0, lds1, acc);
   epilogue<T, TILE, SYM, EPI>(a, prob, ti, tj, lds0, lds1, acc);
@@ -704,33 +678,38 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmArgs a) {
 // launchers
 
 template <typename T, int TILE, bool SYM, int EPI, bool NN>
-static hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
-  if (a.total_tiles <= 0) return hipSuccess;
-  // the main loop runs whole pairs of 128-byte K slices
-  if (a.K <= 0 || a.K % (2 * 128 / static_cast<int>(sizeof(T))) != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ns_gemm<T, TILE, SYM, EPI, NN>), dim3(a.total_tiles), dim3(256), 0, s, a);
+static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
+  if (b.n < 1 || b.n > kBatchGroups) return hipErrorInvalidValue;
+  for (int g = 0; g < b.n; ++g) {
+    const GemmArgs& a = b.g[g];
+    // the main loop runs whole pairs of 128-byte K slices
+    if (a.K <= 0 || a.K % (2 * 128 / static_cast<int>(sizeof(T))) != 0) return hipErrorInvalidValue;
+    if (b.start[g + 1] - b.start[g] != a.total_tiles || a.total_tiles < 0) return hipErrorInvalidValue;
+  }
+  if (b.start[0] != 0 || b.start[b.n] <= 0) return b.start[b.n] == 0 ? hipSuccess : hipErrorInvalidValue;
+  hipLaunchKernelGGL((ns_gemm<T, TILE, SYM, EPI, NN>), dim3(b.start[b.n]), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
 // Symmetric launches take both operands K-contiguous (NT); full launches take the
 // second operand stored K x N (NN).
 template <typename T, int TILE>
-static hipError_t launch_tile(bool sym, int epi, const GemmArgs& a, hipStream_t s) {
-  if (sym) return epi == EPI_STORE ? launch_t<T, TILE, true, EPI_STORE, false>(a, s) : hipErrorInvalidValue;
-  if (epi == EPI_APPLY) return launch_t<T, TILE, false, EPI_APPLY, true>(a, s);
-  return launch_t<T, TILE, false, EPI_STORE, true>(a, s);
+static hipError_t launch_tile(bool sym, int epi, const GemmBatch& b, hipStream_t s) {
+  if (sym) return epi == EPI_STORE ? launch_t<T, TILE, true, EPI_STORE, false>(b, s) : hipErrorInvalidValue;
+  if (epi == EPI_APPLY) return launch_t<T, TILE, false, EPI_APPLY, true>(b, s);
+  return launch_t<T, TILE, false, EPI_STORE, true>(b, s);
 }
 
 template <typename T>
-static hipError_t launch_dtype(int tile, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
-  return tile == 256 ? launch_tile<T, 256>(sym, epi, a, s) : launch_tile<T, 128>(sym, epi, a, s);
+static hipError_t launch_dtype(int tile, bool sym, int epi, const GemmBatch& b, hipStream_t s) {
+  return tile == 256 ? launch_tile<T, 256>(sym, epi, b, s) : launch_tile<T, 128>(sym, epi, b, s);
 }
 
-hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmBatch& b, hipStream_t s) {
   switch (dtype) {
-    case MUON_DTYPE_BF16: return launch_dtype<__bf16>(tile, sym, epi, a, s);
-    case MUON_DTYPE_F16: return launch_dtype<_Float16>(tile, sym, epi, a, s);
-    default: return launch_dtype<float>(tile, sym, epi, a, s);
+    case MUON_DTYPE_BF16: return launch_dtype<__bf16>(tile, sym, epi, b, s);
+    case MUON_DTYPE_F16: return launch_dtype<_Float16>(tile, sym, epi, b, s);
+    default: return launch_dtype<float>(tile, sym, epi, b, s);
   }
 }
 

@@ -20,7 +20,6 @@ struct GemmArgs {
   const void* Q; int64_t q_ps; int32_t ldq;
   int32_t K;
   int32_t tiles_m, tiles_n, tiles_per_problem, total_tiles;
-  int32_t group_m;                               // tile order: > 0 rows per group, 0 = 4, < 0 column-major
   float alpha, beta, gamma;
   const void* D; int64_t d_ps; int32_t ldd;      // optional (beta term)
   void* C; int64_t c_ps; int32_t ldc;            // optional row-major store
@@ -31,7 +30,17 @@ struct GemmArgs {
   float* update_out; unsigned short* shadow;
 };
 
-hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmArgs& a, hipStream_t s);
+// Several shape groups in one launch (same element type, tile and kind):
+// group g owns blocks [start[g], start[g + 1]); start[0] = 0 and
+// start[g + 1] - start[g] = g[g].total_tiles.
+constexpr int kBatchGroups = 4;
+struct GemmBatch {
+  GemmArgs g[kBatchGroups];
+  int32_t start[kBatchGroups + 1];
+  int32_t n;
+};
+
+hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmBatch& b, hipStream_t s);
 
 // M <- mu M + G over every problem of a group (each m n contiguous elements at
 // its src_off), kMomChunk elements per block; partials[b] = sum of squares of the
