@@ -321,12 +321,13 @@ def main() -> int:
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
         dom_flops = sum(2.0 * m * m * n for m, n in probs) * (h.ns_steps - 1) * args.steps
     else:
-        # symmetric launches: R0 = X0 X0^T, five Q = aI + bR + cRR, four R <- Q (R Q)
+        # symmetric launches: R0 = X0 X0^T, five Q = aI + bR + cRR, four T = R Q and
+        # four R <- Q T
         dom_kind = "gram_gemm_sym"
         tile = 256 if probs and probs[0][0] >= 512 else 128
         dom_kernel = f"muon::ns_gemm<{'_Float16' if ns_dtype == 'f16' else 'float'}, {tile}, true, 0, false>"
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
-        dom_flops = sum(2.0 * m * m * n + 18.0 * m ** 3 for m, n in probs) * args.steps
+        dom_flops = sum(2.0 * m * m * n + 26.0 * m ** 3 for m, n in probs) * args.steps
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
     traffic = measured_traffic(dom_kernel, args.workload, args.method)
     mom_launches, mom_ms = kstats.get("momentum_sumsq", (0, 0.0))

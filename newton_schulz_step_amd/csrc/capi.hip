@@ -309,7 +309,9 @@ static int run_standard(const StepCtx& c, const GroupSet& set) {
 // Gram variant (same section): R0 = s X0 X0^T (s an exact power of two keeping
 // R's entries in fp16's normal range; b and c are rescaled to match); per step
 //   Q = a I + (b/s) R + (c/s^2) R R;  P <- Q P (P = Q first);  R <- Q (R Q)
-// (not after the last step); finally X = P X0 with the apply fused.
+// (not after the last step); finally X = P X0 with the apply fused. R, Q and
+// R Q are symmetric and computed as such (lower tiles, mirrored); P is computed
+// in full.
 static int run_gram(const StepCtx& c, const GroupSet& set) {
   const int dt = c.h->ns_dtype;
   const int tile = set.front()->tile;
@@ -366,18 +368,17 @@ static int run_gram(const StepCtx& c, const GroupSet& set) {
       pc ^= 1;
     }
     if (k < S - 1) {
-      // T = R Q, stored as T^T (the second operand of the symmetric launch below)
+      // T = R Q, symmetric (R and Q commute): lower tiles, mirrored; Q is stored
+      // symmetric, so R Q = R Q^T
       v.clear();
       for (const Group* Gp : set) {
         const Group& G = *Gp;
-        const int64_t ss = G.mp * G.mp;
         GemmArgs gt{};
-        set_full(gt, G, R(G, rc), ss, G.mp, Qdst(G), ss, G.mp, kext(G.m, dt), G.mp, G.mp);
+        set_sym(gt, G, R(G, rc), Qdst(G), kext(G.m, dt), G.mp, G.mp * G.mp, ws + G.t);
         gt.alpha = 1.0f;
-        gt.Ct = ws + G.t; gt.ct_ps = ss; gt.ldct = static_cast<int32_t>(G.mp);
         v.push_back(gt);
       }
-      if ((st = launch_batch("gram_gemm_full", c, tile, false, EPI_STORE, v)) != MUON_OK) return st;
+      if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
       // R <- Q T (symmetric: lower tiles, mirrored)
       v.clear();
       for (const Group* Gp : set) {

@@ -5,10 +5,11 @@
 //   NT (symmetric launches): Q is N x K, K contiguous, C = P Q^T
 //     A = X X^T          P = X,  Q = X
 //     A A  (A symmetric) P = A,  Q = A
-//     Gram: R0 = X0 X0^T, Q = a I + b R + c R R, R <- Q T (T stored as T^T)
+//     Gram: R0 = X0 X0^T, Q = a I + b R + c R R, T = R Q, R <- Q T (Q and T
+//     are stored symmetric, so they serve as their own transposes)
 //   NN (full launches): Q is K x N, N contiguous, C = P Q
 //     B X                P = B,  Q = X
-//     Gram: Q P, R Q, P X0
+//     Gram: Q P, P X0
 // The NN operand is staged in LDS as K rows and read with the transposed LDS
 // read of gfx950, so X is stored only once, row-major, and no product needs a
 // transposed copy of its operand.

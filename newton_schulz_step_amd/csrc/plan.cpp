@@ -178,7 +178,7 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
       G.b = off; off = align256(off + sbytes);      // Q
       G.p[0] = off; off = align256(off + sbytes);   // P
       G.p[1] = off; off = align256(off + sbytes);   // next P
-      G.t = off; off = align256(off + sbytes);      // (R Q)^T
+      G.t = off; off = align256(off + sbytes);      // R Q
     }
   }
   L.ws_bytes = std::max<size_t>(off, 256);

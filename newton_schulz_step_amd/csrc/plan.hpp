@@ -32,7 +32,7 @@ struct Group {
   // workspace byte offsets
   size_t x[2] = {0, 0};                  // X, ping-pong (standard); X0 in [0] (gram)
   size_t a = 0, b = 0;                   // standard: A, B; gram: R, Q
-  size_t r2 = 0, p[2] = {0, 0}, t = 0;   // gram: next R, P (ping-pong), (R Q)^T
+  size_t r2 = 0, p[2] = {0, 0}, t = 0;   // gram: next R, P (ping-pong), R Q
 };
 
 struct Layout {

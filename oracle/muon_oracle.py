@@ -44,9 +44,11 @@ those points stays float64. Standard: X0, A, B and X1..X4 are stored; X5 is not.
 Gram: X0, R0, every Q, P and R, and the intermediate R Q are stored; P X0 is not.
 The Gram state may carry an exact power-of-two scale s (R is kept as s X X^T, and
 b, c become b/s, c/s^2); with s = 1 this is the plain recurrence.
-A, B, R and Q are symmetric by definition (A = X X^T and R = X X^T, the article's
-Gram matrix, and B, Q are polynomials in them), so a stored one is a symmetric
-matrix: its lower triangle (row index >= column index) is rounded and mirrored.
+A, B, R, Q and R Q are symmetric by definition (A = X X^T and R = X X^T, the
+article's Gram matrix, B and Q are polynomials in them, and R Q is a product of
+two commuting polynomials in R), so a stored one is a symmetric matrix: its lower
+triangle (row index >= column index) is rounded and mirrored. P is stored as
+computed.
 The exact mode evaluates the products as they are.
 """
 from __future__ import annotations
@@ -126,7 +128,7 @@ def newton_schulz_gram(X0: np.ndarray, steps: int = NS_STEPS,
         Q = sym(a * eye + bs * R + cs * (R @ R))
         P = Q if k == 0 else store(Q @ P)
         if k < steps - 1:
-            RQ = store(R @ Q)
+            RQ = sym(R @ Q)
             R = sym(Q @ RQ)
     return P @ X
 
