@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -34,14 +35,18 @@ struct ProfRec {
 };
 
 static std::mutex g_prof_mu;
-static bool g_prof_active = false;
+static std::atomic<bool> g_prof_active{false};
 static std::vector<ProfRec> g_prof;
 
 template <typename F>
 static hipError_t timed(const char* kind, hipStream_t s, F&& launch) {
-  if (!g_prof_active) return launch();
+  if (!g_prof_active.load(std::memory_order_acquire)) return launch();
   hipEvent_t a = nullptr, b = nullptr;
-  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return hipErrorOutOfMemory;
+  if (hipEventCreate(&a) != hipSuccess) return hipErrorOutOfMemory;
+  if (hipEventCreate(&b) != hipSuccess) {
+    hipEventDestroy(a);
+    return hipErrorOutOfMemory;
+  }
   hipEventRecord(a, s);
   const hipError_t r = launch();
   hipEventRecord(b, s);
@@ -50,22 +55,56 @@ static hipError_t timed(const char* kind, hipStream_t s, F&& launch) {
   return r;
 }
 
+// A set of shape groups that share the tile edge; each NS product is one launch
+// over all of them. Groups are ordered by decreasing n, so the tiles with the
+// longest K (X X^T) are dispatched first and the short ones fill the tail.
+using GroupSet = std::vector<const Group*>;
+
+static std::vector<GroupSet> group_sets(const Layout& L) {
+  std::vector<GroupSet> sets;
+  for (int tile : {256, 128}) {
+    GroupSet all;
+    for (const Group& G : L.groups)
+      if (G.tile == tile) all.push_back(&G);
+    std::stable_sort(all.begin(), all.end(), [](const Group* x, const Group* y) { return x->n > y->n; });
+    for (size_t i = 0; i < all.size(); i += kBatchGroups)
+      sets.emplace_back(all.begin() + i, all.begin() + std::min(all.size(), i + kBatchGroups));
+  }
+  return sets;
+}
+
 // ---------------------------------------------------------------------------
-// plan cache: device copies of the problem and chunk descriptors per table
+// plan cache: the layout and a device copy of the problem descriptors per
+// (device, table, windows, method, dtypes). A plan is shared: a call holds it
+// until its launches are enqueued, so dropping it from the cache (when the
+// cache is full, or on muon_release_plans) never frees one in use. Its device
+// array is freed once no call holds it, after that device has finished every
+// kernel that may read it.
 
 struct Plan {
   Layout L;
+  int device = 0;
   ProblemDesc* d_problems = nullptr;
+  std::vector<GroupSet> sets;   // shape groups launched together
+  Plan() = default;
+  Plan(const Plan&) = delete;
+  Plan& operator=(const Plan&) = delete;
+  ~Plan() {
+    if (!d_problems) return;
+    int cur = 0;
+    const bool restore = hipGetDevice(&cur) == hipSuccess && cur != device;
+    if (restore) hipSetDevice(device);
+    hipDeviceSynchronize();
+    hipFree(d_problems);
+    if (restore) hipSetDevice(cur);
+  }
 };
 
+// The cache is never destroyed: at process exit the HIP runtime may already be
+// gone, so cached plans are left to the process teardown.
 static std::mutex g_plan_mu;
-static std::map<std::string, std::unique_ptr<Plan>> g_plans;
+static auto& g_plans = *new std::map<std::string, std::shared_ptr<Plan>>();
 static constexpr size_t kMaxPlans = 1024;
-
-static void free_plan(Plan& p) {
-  if (p.d_problems) hipFree(p.d_problems);
-  p.d_problems = nullptr;
-}
 
 static std::string plan_key(int device, const muon_matrix_t* t, const muon_window_t* w, int32_t n,
                             const muon_hyper_t* h) {
@@ -77,23 +116,22 @@ static std::string plan_key(int device, const muon_matrix_t* t, const muon_windo
   return k;
 }
 
-static int get_plan(const muon_matrix_t* t, const muon_window_t* w, int32_t n, const muon_hyper_t* h, Plan** out) {
+static int get_plan(const muon_matrix_t* t, const muon_window_t* w, int32_t n, const muon_hyper_t* h,
+                    std::shared_ptr<Plan>& out) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
   const std::string key = plan_key(device, t, w, n, h);
   std::lock_guard<std::mutex> lk(g_plan_mu);
   auto it = g_plans.find(key);
   if (it != g_plans.end()) {
-    *out = it->second.get();
+    out = it->second;
     return MUON_OK;
   }
-  if (g_plans.size() >= kMaxPlans) {
-    hipDeviceSynchronize();
-    for (auto& kv : g_plans) free_plan(*kv.second);
-    g_plans.clear();
-  }
-  std::unique_ptr<Plan> p(new Plan);
+  if (g_plans.size() >= kMaxPlans) g_plans.clear();
+  std::shared_ptr<Plan> p = std::make_shared<Plan>();
+  p->device = device;
   p->L = build_layout(t, n, h, w);
+  p->sets = group_sets(p->L);
   std::vector<ProblemDesc> probs(p->L.problems.size());
   for (size_t i = 0; i < probs.size(); ++i) {
     const HostProblem& hp = p->L.problems[i];
@@ -101,15 +139,13 @@ static int get_plan(const muon_matrix_t* t, const muon_window_t* w, int32_t n, c
   }
   const size_t pb = std::max<size_t>(probs.size(), 1) * sizeof(ProblemDesc);
   if (hipMalloc(&p->d_problems, pb) != hipSuccess) {
-    free_plan(*p);
+    p->d_problems = nullptr;
     return fail(MUON_ERR_HIP, "hipMalloc of the problem descriptors failed");
   }
   if (!probs.empty() &&
-      hipMemcpy(p->d_problems, probs.data(), probs.size() * sizeof(ProblemDesc), hipMemcpyHostToDevice) != hipSuccess) {
-    free_plan(*p);
+      hipMemcpy(p->d_problems, probs.data(), probs.size() * sizeof(ProblemDesc), hipMemcpyHostToDevice) != hipSuccess)
     return fail(MUON_ERR_HIP, "copying the problem descriptors failed");
-  }
-  *out = p.get();
+  out = p;
   g_plans[key] = std::move(p);
   return MUON_OK;
 }
@@ -209,24 +245,6 @@ static void set_full(GemmArgs& g, const Group& G, const void* P, int64_t p_ps, i
   g.tiles_n = static_cast<int32_t>(cols / G.tile);
   g.tiles_per_problem = g.tiles_m * g.tiles_n;
   g.total_tiles = g.tiles_per_problem * G.count;
-}
-
-// A set of shape groups that share the tile edge; each NS product is one launch
-// over all of them. Groups are ordered by decreasing n, so the tiles with the
-// longest K (X X^T) are dispatched first and the short ones fill the tail.
-using GroupSet = std::vector<const Group*>;
-
-static std::vector<GroupSet> group_sets(const Layout& L) {
-  std::vector<GroupSet> sets;
-  for (int tile : {256, 128}) {
-    GroupSet all;
-    for (const Group& G : L.groups)
-      if (G.tile == tile) all.push_back(&G);
-    std::stable_sort(all.begin(), all.end(), [](const Group* x, const Group* y) { return x->n > y->n; });
-    for (size_t i = 0; i < all.size(); i += kBatchGroups)
-      sets.emplace_back(all.begin() + i, all.begin() + std::min(all.size(), i + kBatchGroups));
-  }
-  return sets;
 }
 
 // One launch of `kind` over the per-group arguments `v` (at most kBatchGroups).
@@ -494,9 +512,10 @@ static int step_impl(float* params, int64_t params_numel, const void* grads, flo
   std::string which;
   if (overlapping(spans, which)) return fail(MUON_ERR_OVERLAP, "buffers overlap: " + which);
 
-  Plan* P = nullptr;
-  st = get_plan(table, windows, n_entries, h, &P);
+  std::shared_ptr<Plan> plan;
+  st = get_plan(table, windows, n_entries, h, plan);
   if (st != MUON_OK) return st;
+  const Plan* P = plan.get();
   if (workspace_bytes < P->L.ws_bytes)
     return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(P->L.ws_bytes) + " bytes");
 
@@ -514,7 +533,7 @@ static int step_impl(float* params, int64_t params_numel, const void* grads, flo
                 launch_finalize_norm(partials + G.partial_first, G.chunks, G.count, h->ns_eps, invn + G.first, s));
   StepCtx c{P, h, ws, momentum, params, update_out, bf16_shadow,
             static_cast<float>(1.0 - static_cast<double>(h->lr) * static_cast<double>(h->weight_decay)), s};
-  for (const GroupSet& set : group_sets(P->L)) {
+  for (const GroupSet& set : P->sets) {
     st = (h->ns_method == MUON_NS_STANDARD) ? run_standard(c, set) : run_gram(c, set);
     if (st != MUON_OK) return st;
   }
@@ -652,8 +671,6 @@ double muon_comm_elements(int64_t p_m, int32_t n_ranks, int32_t zero_stage, int3
 int muon_release_plans(void) {
   g_err.clear();
   std::lock_guard<std::mutex> lk(g_plan_mu);
-  if (!g_plans.empty()) hipDeviceSynchronize();
-  for (auto& kv : g_plans) free_plan(*kv.second);
   g_plans.clear();
   return MUON_OK;
 }
@@ -666,14 +683,14 @@ int muon_profile_begin(void) {
     hipEventDestroy(r.b);
   }
   g_prof.clear();
-  g_prof_active = true;
+  g_prof_active.store(true, std::memory_order_release);
   return MUON_OK;
 }
 
 int muon_profile_end(muon_kernel_stat_t* out, int32_t max_kinds, int32_t* n_kinds_out) {
   g_err.clear();
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_active = false;
+  g_prof_active.store(false, std::memory_order_release);
   std::vector<muon_kernel_stat_t> stats;
   int status = MUON_OK;
   for (auto& r : g_prof) {
