@@ -312,14 +312,30 @@ def main() -> int:
     peak = FP32_PEAK_TFLOPS if ns_dtype == "f32" else BF16_PEAK_TFLOPS
 
     # dominant kernel: the standard update GEMM B X (+ a X); algorithmic 2 m^2 n per
-    # problem per launch. Gram: its symmetric GEMM family (nominal FLOPs of the chain).
-    if args.method == "standard":
+    # problem per launch. On 128-row problems in 16-bit the update and the next
+    # X X^T are one pass (ns_update_gram), bound by memory: algorithmic bytes per
+    # problem per launch are X read and X' written (2 m n elements) plus B read and
+    # A' written (2 m^2 elements). Gram: its symmetric GEMM family (nominal FLOPs).
+    bound, unit, roof_peak = "mfma", "TFLOP/s", peak
+    if args.method == "standard" and kstats.get("ns_update_gram", (0, 0.0))[1] > \
+            kstats.get("ns_gemm_update", (0, 0.0))[1]:
+        dom_kind = "ns_update_gram"
+        dt_name = {"bf16": "__bf16", "f16": "_Float16"}[ns_dtype]
+        dom_kernel = f"muon::ns_update_gram<{dt_name}>"
+        launches, dom_ms = kstats[dom_kind]
+        esz = 2
+        dom_work = sum(esz * (2.0 * m * n + 2.0 * m * m) for m, n in probs if m <= 128) * \
+            (h.ns_steps - 1) * args.steps
+        bound, unit, roof_peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = dom_work / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else None
+    elif args.method == "standard":
         dom_kind = "ns_gemm_update"
         tile = 256 if probs and probs[0][0] >= 512 else 128
         dt_name = {"bf16": "__bf16", "f16": "_Float16", "f32": "float"}[ns_dtype]
         dom_kernel = f"muon::ns_gemm<{dt_name}, {tile}, false, 0, true>"
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
         dom_flops = sum(2.0 * m * m * n for m, n in probs) * (h.ns_steps - 1) * args.steps
+        achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
     else:
         # symmetric launches: R0 = X0 X0^T, five Q = aI + bR + cRR, four T = R Q and
         # four R <- Q T
@@ -328,7 +344,7 @@ def main() -> int:
         dom_kernel = f"muon::ns_gemm<{'_Float16' if ns_dtype == 'f16' else 'float'}, {tile}, true, 0, false>"
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
         dom_flops = sum(2.0 * m * m * n + 26.0 * m ** 3 for m, n in probs) * args.steps
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
+        achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
     traffic = measured_traffic(dom_kernel, args.workload, args.method)
     mom_launches, mom_ms = kstats.get("momentum_sumsq", (0, 0.0))
     gbytes = elems * (10 if wl.grad_dtype != "f32" else 12) * args.steps / 1e9
@@ -358,10 +374,10 @@ def main() -> int:
         "ns_tflops": ns_total / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None,
         "ns_frac_of_peak": (ns_total / (ns_ms * 1e-3) / 1e12 / peak) if ns_ms > 0 else None,
         "roofline": {
-            "bound": "mfma", "kernel": dom_kernel, "launches": launches,
+            "bound": bound, "kernel": dom_kernel, "launches": launches,
             "avg_launch_ms": dom_ms / launches if launches else None,
-            "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak if achieved else None,
+            "achieved": achieved, "peak": roof_peak, "unit": unit,
+            "frac": achieved / roof_peak if achieved else None,
             "traffic": traffic,
         },
         "momentum_pass": {

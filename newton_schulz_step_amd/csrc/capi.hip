@@ -44,12 +44,12 @@ static hipError_t timed(const char* kind, hipStream_t s, F&& launch) {
   hipEvent_t a = nullptr, b = nullptr;
   if (hipEventCreate(&a) != hipSuccess) return hipErrorOutOfMemory;
   if (hipEventCreate(&b) != hipSuccess) {
-    hipEventDestroy(a);
+    (void)hipEventDestroy(a);
     return hipErrorOutOfMemory;
   }
-  hipEventRecord(a, s);
+  (void)hipEventRecord(a, s);
   const hipError_t r = launch();
-  hipEventRecord(b, s);
+  (void)hipEventRecord(b, s);
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof.push_back({kind, a, b});
   return r;
@@ -58,14 +58,19 @@ static hipError_t timed(const char* kind, hipStream_t s, F&& launch) {
 // A set of shape groups that share the tile edge; each NS product is one launch
 // over all of them. Groups are ordered by decreasing n, so the tiles with the
 // longest K (X X^T) are dispatched first and the short ones fill the tail.
+// Groups with a single tile row (m <= 128) form sets of their own, which the
+// standard iteration runs with the fused update + Gram kernel.
 using GroupSet = std::vector<const Group*>;
+
+static bool single_row(const Group& G) { return G.mp == G.tile; }
 
 static std::vector<GroupSet> group_sets(const Layout& L) {
   std::vector<GroupSet> sets;
-  for (int tile : {256, 128}) {
+  for (int kind = 0; kind < 3; ++kind) {
+    const int tile = kind == 0 ? 256 : 128;
     GroupSet all;
     for (const Group& G : L.groups)
-      if (G.tile == tile) all.push_back(&G);
+      if (G.tile == tile && (kind == 0 || single_row(G) == (kind == 2))) all.push_back(&G);
     std::stable_sort(all.begin(), all.end(), [](const Group* x, const Group* y) { return x->n > y->n; });
     for (size_t i = 0; i < all.size(); i += kBatchGroups)
       sets.emplace_back(all.begin() + i, all.begin() + std::min(all.size(), i + kBatchGroups));
@@ -93,10 +98,11 @@ struct Plan {
     if (!d_problems) return;
     int cur = 0;
     const bool restore = hipGetDevice(&cur) == hipSuccess && cur != device;
-    if (restore) hipSetDevice(device);
-    hipDeviceSynchronize();
-    hipFree(d_problems);
-    if (restore) hipSetDevice(cur);
+    // nothing useful can be done about a failure while releasing
+    if (restore) (void)hipSetDevice(device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(d_problems);
+    if (restore) (void)hipSetDevice(cur);
   }
 };
 
@@ -247,9 +253,7 @@ static void set_full(GemmArgs& g, const Group& G, const void* P, int64_t p_ps, i
   g.total_tiles = g.tiles_per_problem * G.count;
 }
 
-// One launch of `kind` over the per-group arguments `v` (at most kBatchGroups).
-static int launch_batch(const char* kind, const StepCtx& c, int tile, bool sym, int epi,
-                        const std::vector<GemmArgs>& v) {
+static GemmBatch make_batch(const std::vector<GemmArgs>& v) {
   GemmBatch b{};
   b.n = static_cast<int32_t>(v.size());
   b.start[0] = 0;
@@ -257,6 +261,13 @@ static int launch_batch(const char* kind, const StepCtx& c, int tile, bool sym, 
     b.g[g] = v[g];
     b.start[g + 1] = b.start[g] + v[g].total_tiles;
   }
+  return b;
+}
+
+// One launch of `kind` over the per-group arguments `v` (at most kBatchGroups).
+static int launch_batch(const char* kind, const StepCtx& c, int tile, bool sym, int epi,
+                        const std::vector<GemmArgs>& v) {
+  const GemmBatch b = make_batch(v);
   MUON_LAUNCH(kind, c.s, launch_ns_gemm(c.h->ns_dtype, tile, sym, epi, b, c.s));
   return MUON_OK;
 }
@@ -277,6 +288,8 @@ static int run_prep(const StepCtx& c, const Group& G) {
 static int run_standard(const StepCtx& c, const GroupSet& set) {
   const int dt = c.h->ns_dtype;
   const int tile = set.front()->tile;
+  // single-tile-row groups in 16-bit: X X^T of each new X comes out of the update
+  const bool fused = single_row(*set.front()) && dt != MUON_DTYPE_F32;
   char* ws = c.ws;
   int st;
   for (const Group* G : set)
@@ -310,12 +323,24 @@ static int run_standard(const StepCtx& c, const GroupSet& set) {
       g3.beta = c.h->ns_a;
       g3.D = X[cur]; g3.d_ps = xs; g3.ldd = static_cast<int32_t>(G.np);
       if (!last) { g3.C = X[cur ^ 1]; g3.c_ps = xs; g3.ldc = static_cast<int32_t>(G.np); }
+      if (fused && !last) {
+        // one block per problem; the new X X^T goes to A (already consumed by B)
+        g3.K = static_cast<int32_t>(G.mp);
+        g3.total_tiles = G.count;
+        g3.Ct = A; g3.ct_ps = ss; g3.ldct = static_cast<int32_t>(G.mp);
+      }
       v3.push_back(g3);
     }
-    if ((st = launch_batch("ns_gemm_xxt", c, tile, true, EPI_STORE, v1)) != MUON_OK) return st;
+    if (!fused || k == 0)
+      if ((st = launch_batch("ns_gemm_xxt", c, tile, true, EPI_STORE, v1)) != MUON_OK) return st;
     if ((st = launch_batch("ns_gemm_poly", c, tile, true, EPI_STORE, v2)) != MUON_OK) return st;
     if (!last) {
-      if ((st = launch_batch("ns_gemm_update", c, tile, false, EPI_STORE, v3)) != MUON_OK) return st;
+      if (fused) {
+        const GemmBatch b = make_batch(v3);
+        MUON_LAUNCH("ns_update_gram", c.s, launch_update_gram(dt, b, c.s));
+      } else if ((st = launch_batch("ns_gemm_update", c, tile, false, EPI_STORE, v3)) != MUON_OK) {
+        return st;
+      }
       cur ^= 1;
     } else {
       if ((st = launch_batch("ns_gemm_apply", c, tile, false, EPI_APPLY, v3)) != MUON_OK) return st;
@@ -679,8 +704,8 @@ int muon_profile_begin(void) {
   g_err.clear();
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (auto& r : g_prof) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
   g_prof_active.store(true, std::memory_order_release);
@@ -709,8 +734,8 @@ int muon_profile_end(muon_kernel_stat_t* out, int32_t max_kinds, int32_t* n_kind
     }
     k->launches += 1;
     k->total_ms += ms;
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
   const int32_t n = static_cast<int32_t>(stats.size());

@@ -42,6 +42,15 @@ template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { re
 
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 
+// x as a materialised fp32 value: a conversion that follows rounds this value,
+// instead of being merged with the arithmetic that produced x into a single
+// rounding (which the compiler does for fp16 results in some kernels and not in
+// others). Every kernel that stores an iterate rounds it this way.
+__device__ __forceinline__ float keep_f32(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ unsigned short bf16_bits(float x) {
   __bf16 b = static_cast<__bf16>(x);
   return __builtin_bit_cast(unsigned short, b);

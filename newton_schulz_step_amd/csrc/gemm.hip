@@ -434,6 +434,8 @@ __device__ __forceinline__ void apply8(const GemmArgs& a, int64_t pidx, int64_t 
 }
 
 // Epilogue: v = alpha acc + beta D + gamma I, stored (or applied) as the launch asks.
+// The beta D term is one explicit fused multiply-add, fma(beta, D, alpha acc), so
+// every kernel that forms it rounds it the same way.
 // Per wave and per 32-row block i: the accumulators are staged in LDS; a row pass
 // gives each lane 8 consecutive columns of several rows (row-major store, or the
 // apply of a matrix stored as is), a column pass 8 consecutive rows of one column
@@ -525,7 +527,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       for (int e = 0; e < 4; ++e) { v[e] = a.alpha * s0[e]; v[e + 4] = a.alpha * s1[e]; }
       if (D != nullptr) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += a.beta * dq[t].get(e);
+        for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(a.beta, dq[t].get(e), v[e]);
       }
       if (a.gamma != 0.0f) {
 #pragma unroll
@@ -541,7 +543,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       } else {
         T o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(v[e]);
+        for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(keep_f32(v[e]));
         if (C != nullptr) {
           T* cp = C + static_cast<int64_t>(prob) * a.c_ps + static_cast<int64_t>(gi) * a.ldc + gj;
           if (!diag || gi >= gj + 7) {
@@ -673,6 +675,245 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmBatch batch) {
   f32x16 acc[Gm::WB][Gm::WB];
   mainloop<T, TILE, NN>(a, prob, ti, tj, lds0, lds1, acc);
   epilogue<T, TILE, SYM, EPI>(a, prob, ti, tj, lds0, lds1, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Groups with a single tile row (m <= 128, 16-bit iterates): the update
+// X' = a X + B X and the next Gram matrix A' = X' X'^T in one pass.
+//
+// One workgroup per problem keeps B in LDS and streams X one 128-column tile at a
+// time: each tile is the K x N operand of B X and also the a X term, so X is
+// read once; X' goes out to HBM and, rounded as stored, into LDS, where it is
+// the operand of the tile's contribution to X' X'^T, accumulated in registers
+// over all tiles. Every output element sees the same products in the same k
+// order as the separate update and X X^T launches, so the results are
+// bit-identical to theirs.
+//
+// Arguments: P = B (mp x mp), Q = D = X (mp x np), C = X', Ct = A' (mp x mp,
+// stored symmetric); alpha, beta as in the update; tiles_n = np / 128.
+template <typename T>
+__global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
+  using Gm = Geo<T, 128>;
+  static_assert(sizeof(T) == 2, "16-bit iterates only");
+  constexpr int HALF = Gm::HALF, WB = Gm::WB, SP = Gm::SP;   // 64, 2, 68
+  constexpr int KS = 64;                                      // K elements per slice
+  constexpr int RB = 256;                                     // bytes of one X row of a tile
+  constexpr int SLB = 128 * 128;                              // bytes of one K-contiguous slice plane
+  constexpr int XSB = KS * RB;                                // bytes of one NN slice of an X tile
+  constexpr int STG = 32 * SP * 4;                            // epilogue staging bytes per wave
+  __shared__ __attribute__((aligned(1024))) char Bs[2 * SLB];      // B, K-contiguous, two slices
+  __shared__ __attribute__((aligned(1024))) char Xs[2 * XSB];      // X tile, K x N, two slices
+  __shared__ __attribute__((aligned(1024))) char Ns[2 * SLB];      // X' tile, K-contiguous planes
+  __shared__ __attribute__((aligned(1024))) char St[4 * STG];      // epilogue staging
+
+  const int bid = static_cast<int>(blockIdx.x);
+  int g = 0;
+#pragma unroll
+  for (int q = 1; q < kBatchGroups; ++q)
+    if (q < batch.n && bid >= batch.start[q]) g = q;
+  const GemmArgs& a = batch.g[g];
+  const int prob = bid - batch.start[g];
+  const int NT = a.tiles_n;
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  using V = typename Gm::V;
+
+  // ---- B into LDS (row r = (wave * 4 + it) * 8 + lane / 8, chunk lane % 8 of slice sl)
+  {
+    const char* Bg = static_cast<const char*>(a.P) + static_cast<int64_t>(prob) * a.p_ps * 2;
+    u16x8 rb[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int sl = v >> 2, r = (wave * 4 + (v & 3)) * 8 + (lane >> 3), c = lane & 7;
+      rb[v] = *reinterpret_cast<const u16x8*>(Bg + static_cast<int64_t>(r) * a.ldp * 2 + sl * 128 + c * 16);
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int sl = v >> 2, r = (wave * 4 + (v & 3)) * 8 + (lane >> 3), c = lane & 7;
+      *reinterpret_cast<u16x8*>(Bs + sl * SLB + r * 128 + ((c ^ swz(r)) << 4)) = rb[v];
+    }
+  }
+
+  // ---- X tile loads: thread t covers chunk (it * 256 + t) of slice it / 4, i.e. row
+  // kr = (it % 4) * 16 + t / 16 of that slice, 16-byte chunk t % 16
+  const char* Xg = static_cast<const char*>(a.Q) + static_cast<int64_t>(prob) * a.q_ps * 2;
+  int xofs[8];
+  int64_t xsrc[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int sl = v >> 2, id = (v & 3) * 256 + tid, kr = id >> 4, c = id & 15;
+    xsrc[v] = (static_cast<int64_t>(sl * KS + kr) * a.ldq) * 2 + c * 16;
+    xofs[v] = sl * XSB + kr * RB + (((c >> 1) ^ (kr & 7)) << 5) + ((c & 1) << 4);
+  }
+  auto xload = [&](u16x8 (&r)[8], int jt) {
+    const int64_t col = static_cast<int64_t>(jt) * 128 * 2;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) r[v] = *reinterpret_cast<const u16x8*>(Xg + xsrc[v] + col);
+  };
+  auto xwrite = [&](const u16x8 (&r)[8]) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) *reinterpret_cast<u16x8*>(Xs + xofs[v]) = r[v];
+  };
+
+  // ---- MFMA operand offsets: K-contiguous planes (B, X') and the NN X tile
+  int aoff[WB][4], boff[WB][4], bnn[WB][2];
+#pragma unroll
+  for (int i = 0; i < WB; ++i) {
+    const int ra = wm * HALF + i * 32 + (lane & 31);
+    const int rb = wn * HALF + i * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      aoff[i][ks] = ra * 128 + ((c ^ swz(ra)) << 4);
+      boff[i][ks] = rb * 128 + ((c ^ swz(rb)) << 4);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < WB; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int gq = lane >> 4, sl = lane & 15;
+      const int kr = 8 * (gq >> 1) + 4 * h + (sl >> 2);
+      const int cb = (wn * HALF + j * 32 + 16 * (gq & 1) + 4 * (sl & 3)) * 2;
+      bnn[j][h] = kr * RB + (((cb >> 5) ^ (kr & 7)) << 5) + (cb & 31);
+    }
+
+  f32x16 accA[WB][WB], accC[WB][WB];
+#pragma unroll
+  for (int i = 0; i < WB; ++i)
+#pragma unroll
+    for (int j = 0; j < WB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accA[i][j][r] = 0.0f;
+
+  float* stg = reinterpret_cast<float*>(St + wave * STG);
+  auto srow = [&](int r, int c) { return r * SP + (c ^ (((r >> 3) & 3) << 3)); };
+  T* Cg = static_cast<T*>(a.C) + static_cast<int64_t>(prob) * a.c_ps;
+
+  auto tile = [&](u16x8 (&r)[8], int jt) {
+    xwrite(r);
+    __syncthreads();                       // X tile (and, first time, B) in LDS; last Gram reads done
+    if (jt + 2 < NT) xload(r, jt + 2);
+
+    // X'_tile = B X_tile over K = 128 (two slices, four sub-steps each)
+#pragma unroll
+    for (int i = 0; i < WB; ++i)
+#pragma unroll
+      for (int j = 0; j < WB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) accC[i][j][e] = 0.0f;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        V xa[WB], xb[WB];
+#pragma unroll
+        for (int i = 0; i < WB; ++i) xa[i] = *reinterpret_cast<const V*>(Bs + sl * SLB + aoff[i][ks]);
+#pragma unroll
+        for (int j = 0; j < WB; ++j) {
+          const char* base = Xs + sl * XSB + ks * 16 * RB;
+          const auto lo = TrRead<T>::get(base + bnn[j][0]);
+          const auto hi = TrRead<T>::get(base + bnn[j][1]);
+          xb[j] = __builtin_bit_cast(V, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int i = 0; i < WB; ++i)
+#pragma unroll
+          for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], accC[i][j]);
+      }
+
+    // epilogue: v = alpha acc + beta X (from the tile in LDS), rounded; to HBM and
+    // to the K-contiguous planes of X'
+#pragma unroll
+    for (int i = 0; i < WB; ++i) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < WB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          stg[srow((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), j * 32 + (lane & 31))] = accC[i][j][r];
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int q = lane + 64 * t;
+        const int rr = q >> 3, cc = (q & 7) * 8;
+        const int gi = wm * HALF + i * 32 + rr, gj = wn * HALF + cc;   // row (= k of X), column in tile
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
+        const int ksl = gi >> 6, kr = gi & 63, cb = gj * 2;
+        const u16x8 dq = *reinterpret_cast<const u16x8*>(Xs + ksl * XSB + kr * RB +
+                                                         (((cb >> 5) ^ (kr & 7)) << 5) + (cb & 31));
+        T o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float v = a.alpha * (e < 4 ? s0[e] : s1[e - 4]);
+          v = __builtin_fmaf(a.beta, static_cast<float>(__builtin_bit_cast(T, static_cast<unsigned short>(dq[e]))), v);
+          o[e] = from_f32<T>(keep_f32(v));
+        }
+        st8<T>(Cg + static_cast<int64_t>(gi) * a.ldc + static_cast<int64_t>(jt) * 128 + gj, o);
+        const int pl = gj >> 6, c = (gj & 63) >> 3;
+        u16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = __builtin_bit_cast(unsigned short, o[e]);
+        *reinterpret_cast<u16x8*>(Ns + pl * SLB + gi * 128 + ((c ^ swz(gi)) << 4)) = w;
+      }
+    }
+    __syncthreads();                       // X' planes complete; X tile no longer read
+
+    // A' += X'_tile X'_tile^T over the tile's 128 columns
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        V xa[WB], xb[WB];
+#pragma unroll
+        for (int i = 0; i < WB; ++i) xa[i] = *reinterpret_cast<const V*>(Ns + pl * SLB + aoff[i][ks]);
+#pragma unroll
+        for (int j = 0; j < WB; ++j) xb[j] = *reinterpret_cast<const V*>(Ns + pl * SLB + boff[j][ks]);
+#pragma unroll
+        for (int i = 0; i < WB; ++i)
+#pragma unroll
+          for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], accA[i][j]);
+      }
+  };
+
+  u16x8 r0[8], r1[8];
+  xload(r0, 0);
+  if (NT > 1) xload(r1, 1);
+  for (int jt = 0; jt < NT; jt += 2) {
+    tile(r0, jt);
+    if (jt + 1 < NT) tile(r1, jt + 1);
+  }
+
+  // A' stored symmetric (lower triangle, mirrored), as the X X^T launch stores it
+  GemmArgs s{};
+  s.C = a.Ct; s.c_ps = a.ct_ps; s.ldc = a.ldct;
+  s.Ct = a.Ct; s.ct_ps = a.ct_ps; s.ldct = a.ldct;
+  s.alpha = 1.0f;
+  epilogue<T, 128, true, EPI_STORE>(s, prob, 0, 0, St, St + 2 * STG, accA);
+}
+
+hipError_t launch_update_gram(int dtype, const GemmBatch& b, hipStream_t s) {
+  if (b.n < 1 || b.n > kBatchGroups || b.start[0] != 0) return hipErrorInvalidValue;
+  for (int g = 0; g < b.n; ++g) {
+    const GemmArgs& a = b.g[g];
+    if (a.K != 128 || a.tiles_n < 1 || b.start[g + 1] - b.start[g] != a.total_tiles) return hipErrorInvalidValue;
+  }
+  if (b.start[b.n] <= 0) return hipSuccess;
+  switch (dtype) {
+    case MUON_DTYPE_BF16:
+      hipLaunchKernelGGL(ns_update_gram<__bf16>, dim3(b.start[b.n]), dim3(256), 0, s, b);
+      break;
+    case MUON_DTYPE_F16:
+      hipLaunchKernelGGL(ns_update_gram<_Float16>, dim3(b.start[b.n]), dim3(256), 0, s, b);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -42,6 +42,12 @@ struct GemmBatch {
 
 hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmBatch& b, hipStream_t s);
 
+// Single-tile-row groups (mp = 128, bf16/fp16): X' = alpha B X + beta X and
+// A' = X' X'^T (stored symmetric) in one pass, one block per problem. Per group:
+// P = B, Q = D = X, C = X', Ct = A', K = 128, tiles_n = np / 128,
+// total_tiles = number of problems.
+hipError_t launch_update_gram(int dtype, const GemmBatch& b, hipStream_t s);
+
 // M <- mu M + G over every problem of a group (each m n contiguous elements at
 // its src_off), kMomChunk elements per block; partials[b] = sum of squares of the
 // new M in block b (problem b / chunks, block b % chunks of that problem).
