@@ -282,6 +282,22 @@ static int run_prep(const StepCtx& c, const Group& G) {
   return MUON_OK;
 }
 
+// Single-tile-row group in 16-bit: X0 and R = alpha X0 X0^T in one pass.
+static int run_prep_gram(const StepCtx& c, const Group& G, void* R, float alpha) {
+  PrepGramArgs a{};
+  a.M = c.M;
+  a.probs = c.P->d_problems + G.first;
+  a.inv_norm = reinterpret_cast<const float*>(c.ws + c.P->L.off_invnorm) + G.first;
+  a.X = c.ws + G.x[0];
+  a.R = R;
+  a.m = static_cast<int32_t>(G.m); a.n = static_cast<int32_t>(G.n);
+  a.mp = static_cast<int32_t>(G.mp); a.np = static_cast<int32_t>(G.np);
+  a.n_problems = G.count;
+  a.alpha = alpha;
+  MUON_LAUNCH("prep_gram", c.s, launch_prep_gram(c.h->ns_dtype, a, c.s));
+  return MUON_OK;
+}
+
 // Standard quintic (DeepSpeed-Muon article, section 核心算子): per step
 //   A = X X^T;  B = b A + c A A;  X <- a X + B X,
 // the last step's epilogue applying p <- p * decay - lr * X.
@@ -293,7 +309,7 @@ static int run_standard(const StepCtx& c, const GroupSet& set) {
   char* ws = c.ws;
   int st;
   for (const Group* G : set)
-    if ((st = run_prep(c, *G)) != MUON_OK) return st;
+    if ((st = fused ? run_prep_gram(c, *G, ws + G->a, 1.0f) : run_prep(c, *G)) != MUON_OK) return st;
   int cur = 0;
   for (int k = 0; k < c.h->ns_steps; ++k) {
     const bool last = (k == c.h->ns_steps - 1);
@@ -331,7 +347,7 @@ static int run_standard(const StepCtx& c, const GroupSet& set) {
       }
       v3.push_back(g3);
     }
-    if (!fused || k == 0)
+    if (!fused)
       if ((st = launch_batch("ns_gemm_xxt", c, tile, true, EPI_STORE, v1)) != MUON_OK) return st;
     if ((st = launch_batch("ns_gemm_poly", c, tile, true, EPI_STORE, v2)) != MUON_OK) return st;
     if (!last) {
@@ -361,21 +377,28 @@ static int run_gram(const StepCtx& c, const GroupSet& set) {
   const int S = c.h->ns_steps;
   char* ws = c.ws;
   int st;
-  for (const Group* G : set)
-    if ((st = run_prep(c, *G)) != MUON_OK) return st;
   auto scale = [&](const Group& G) { return (dt == MUON_DTYPE_F16) ? gram_scale(G.m) : 1.0f; };
   auto R = [&](const Group& G, int i) -> void* { return ws + (i == 0 ? G.a : G.r2); };
   auto Pb = [&](const Group& G, int i) -> void* { return ws + G.p[i]; };
+  // single-tile-row groups in 16-bit: X0 and R0 in one pass
+  const bool fused = single_row(*set.front()) && dt != MUON_DTYPE_F32;
 
   std::vector<GemmArgs> v;
-  for (const Group* Gp : set) {
-    const Group& G = *Gp;
-    GemmArgs r0{};
-    set_sym(r0, G, ws + G.x[0], ws + G.x[0], kext(G.n, dt), G.np, G.mp * G.np, R(G, 0));
-    r0.alpha = scale(G);
-    v.push_back(r0);
+  if (fused) {
+    for (const Group* G : set)
+      if ((st = run_prep_gram(c, *G, R(*G, 0), scale(*G))) != MUON_OK) return st;
+  } else {
+    for (const Group* G : set)
+      if ((st = run_prep(c, *G)) != MUON_OK) return st;
+    for (const Group* Gp : set) {
+      const Group& G = *Gp;
+      GemmArgs r0{};
+      set_sym(r0, G, ws + G.x[0], ws + G.x[0], kext(G.n, dt), G.np, G.mp * G.np, R(G, 0));
+      r0.alpha = scale(G);
+      v.push_back(r0);
+    }
+    if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
   }
-  if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
 
   int rc = 0, pc = 0;
   for (int k = 0; k < S; ++k) {

@@ -136,8 +136,8 @@ __device__ __forceinline__ void store16(T* dst, const float (&v)[16]) {
     u16x8 w0, w1;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      w0[e] = __builtin_bit_cast(unsigned short, from_f32<T>(v[e]));
-      w1[e] = __builtin_bit_cast(unsigned short, from_f32<T>(v[e + 8]));
+      w0[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[e])));
+      w1[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[e + 8])));
     }
     u16x8* d = reinterpret_cast<u16x8*>(dst);
     d[0] = w0;

@@ -917,6 +917,167 @@ hipError_t launch_update_gram(int dtype, const GemmBatch& b, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Single-tile-row groups (m <= 128, 16-bit iterates): X0 and its Gram matrix
+// R = alpha X0 X0^T in one pass.
+//
+// One workgroup per problem streams the momentum one 128-column tile of X0 at a
+// time: it forms X0 = round(M * inv_norm) exactly as the X0 kernel does (a matrix
+// stored transposed is turned in LDS), writes it to HBM and into LDS, and adds the
+// tile's contribution to X0 X0^T in registers; the next tile's momentum is loaded
+// while the current one's products run. The products and their k order are those
+// of the symmetric launch, so X0 and R are bit-identical to the separate kernels.
+template <typename T>
+__global__ __launch_bounds__(256) void prep_gram_kernel(PrepGramArgs a) {
+  using Gm = Geo<T, 128>;
+  static_assert(sizeof(T) == 2, "16-bit iterates only");
+  constexpr int WB = Gm::WB, HALF = Gm::HALF, SP = Gm::SP;   // 2, 64, 68
+  constexpr int SLB = 128 * 128;                              // bytes of one K-contiguous plane
+  constexpr int MP = 129;                                     // pitch (floats) of the transpose tile
+  constexpr int STG = 32 * SP * 4;                            // epilogue staging bytes per wave
+  static_assert(4 * STG <= 128 * MP * 4, "epilogue staging fits in the transpose tile");
+  __shared__ __attribute__((aligned(1024))) float Ms[128 * MP];   // transpose tile, then staging
+  __shared__ __attribute__((aligned(1024))) char Ns[2 * SLB];     // X0 tile, K-contiguous planes
+
+  const int p = static_cast<int>(blockIdx.x);
+  const ProblemDesc pd = a.probs[p];
+  const float inv = a.inv_norm[p];
+  const int m = a.m, n = a.n, NT = a.np / 128;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = tid >> 1, hh = tid & 1;   // this thread's row (or stored row) and half of it
+  using V = typename Gm::V;
+
+  // raw momentum of tile jt for this thread: 64 consecutive stored elements
+  auto load = [&](float (&buf)[64], int jt) {
+    int64_t base;
+    bool ok, vec;
+    if (!pd.transposed) {                 // row r, columns jt*128 + hh*64 ..
+      const int k0 = jt * 128 + hh * 64;
+      base = pd.src_off + static_cast<int64_t>(r) * n + k0;
+      ok = r < m;
+      vec = ok && k0 + 64 <= n && (base & 3) == 0;
+#pragma unroll
+      for (int e = 0; e < 64; e += 4) {
+        if (vec) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(a.M + base + e);
+          buf[e] = w[0]; buf[e + 1] = w[1]; buf[e + 2] = w[2]; buf[e + 3] = w[3];
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) buf[e + u] = (ok && k0 + e + u < n) ? a.M[base + e + u] : 0.0f;
+        }
+      }
+    } else {                              // stored row jt*128 + r, elements hh*64 ..
+      const int kk = jt * 128 + r, i0 = hh * 64;
+      base = pd.src_off + static_cast<int64_t>(kk) * m + i0;
+      ok = kk < n;
+      vec = ok && i0 + 64 <= m && (base & 3) == 0;
+#pragma unroll
+      for (int e = 0; e < 64; e += 4) {
+        if (vec) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(a.M + base + e);
+          buf[e] = w[0]; buf[e + 1] = w[1]; buf[e + 2] = w[2]; buf[e + 3] = w[3];
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) buf[e + u] = (ok && i0 + e + u < m) ? a.M[base + e + u] : 0.0f;
+        }
+      }
+    }
+  };
+
+  int aoff[WB][4], boff[WB][4];
+#pragma unroll
+  for (int i = 0; i < WB; ++i) {
+    const int ra = wm * HALF + i * 32 + (lane & 31);
+    const int rb = wn * HALF + i * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      aoff[i][ks] = ra * 128 + ((c ^ swz(ra)) << 4);
+      boff[i][ks] = rb * 128 + ((c ^ swz(rb)) << 4);
+    }
+  }
+  f32x16 acc[WB][WB];
+#pragma unroll
+  for (int i = 0; i < WB; ++i)
+#pragma unroll
+    for (int j = 0; j < WB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  T* Xg = static_cast<T*>(a.X) + static_cast<int64_t>(p) * a.mp * a.np;
+  auto tile = [&](float (&buf)[64], int jt) {
+    // X0 row r, columns hh*64 .. of the tile (through LDS when stored transposed)
+    float v[64];
+    if (pd.transposed) {
+#pragma unroll
+      for (int e = 0; e < 64; ++e) Ms[(hh * 64 + e) * MP + r] = buf[e];
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 64; ++e) v[e] = Ms[r * MP + hh * 64 + e] * inv;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 64; ++e) v[e] = buf[e] * inv;
+    }
+    T* dst = Xg + static_cast<int64_t>(r) * a.np + jt * 128 + hh * 64;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      u16x8 w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[c * 8 + e])));
+      *reinterpret_cast<u16x8*>(dst + c * 8) = w;
+      *reinterpret_cast<u16x8*>(Ns + hh * SLB + r * 128 + ((c ^ swz(r)) << 4)) = w;
+    }
+    __syncthreads();                       // X0 tile complete in LDS; transpose tile read
+    if (jt + 1 < NT) load(buf, jt + 1);
+
+    // R += X0_tile X0_tile^T over the tile's 128 columns
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        V xa[WB], xb[WB];
+#pragma unroll
+        for (int i = 0; i < WB; ++i) xa[i] = *reinterpret_cast<const V*>(Ns + pl * SLB + aoff[i][ks]);
+#pragma unroll
+        for (int j = 0; j < WB; ++j) xb[j] = *reinterpret_cast<const V*>(Ns + pl * SLB + boff[j][ks]);
+#pragma unroll
+        for (int i = 0; i < WB; ++i)
+#pragma unroll
+          for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], acc[i][j]);
+      }
+    __syncthreads();                       // products done before the tile buffers are reused
+  };
+  float buf[64];
+  load(buf, 0);
+  for (int jt = 0; jt < NT; ++jt) tile(buf, jt);
+
+  GemmArgs s{};
+  s.C = a.R; s.c_ps = static_cast<int64_t>(a.mp) * a.mp; s.ldc = a.mp;
+  s.Ct = a.R; s.ct_ps = s.c_ps; s.ldct = a.mp;
+  s.alpha = a.alpha;
+  char* st = reinterpret_cast<char*>(Ms);
+  epilogue<T, 128, true, EPI_STORE>(s, p, 0, 0, st, st + 2 * STG, acc);
+}
+
+hipError_t launch_prep_gram(int dtype, const PrepGramArgs& a, hipStream_t s) {
+  if (a.n_problems <= 0) return hipSuccess;
+  if (a.mp != 128 || a.m < 1 || a.m > 128 || a.np % 128 != 0 || a.n > a.np) return hipErrorInvalidValue;
+  switch (dtype) {
+    case MUON_DTYPE_BF16:
+      hipLaunchKernelGGL(prep_gram_kernel<__bf16>, dim3(a.n_problems), dim3(256), 0, s, a);
+      break;
+    case MUON_DTYPE_F16:
+      hipLaunchKernelGGL(prep_gram_kernel<_Float16>, dim3(a.n_problems), dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 
 template <typename T, int TILE, bool SYM, int EPI, bool NN>

@@ -48,6 +48,18 @@ hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmBatc
 // total_tiles = number of problems.
 hipError_t launch_update_gram(int dtype, const GemmBatch& b, hipStream_t s);
 
+// Single-tile-row groups (mp = 128, bf16/fp16): X0 = round(M * inv_norm) as the
+// X0 kernel writes it, and R = alpha X0 X0^T (stored symmetric) as the symmetric
+// launch computes it, in one pass; one block per problem.
+struct PrepGramArgs {
+  const float* M; const ProblemDesc* probs; const float* inv_norm;
+  void* X;        // n_problems x mp x np
+  void* R;        // n_problems x mp x mp
+  int32_t m, n, mp, np, n_problems;
+  float alpha;
+};
+hipError_t launch_prep_gram(int dtype, const PrepGramArgs& a, hipStream_t s);
+
 // M <- mu M + G over every problem of a group (each m n contiguous elements at
 // its src_off), kMomChunk elements per block; partials[b] = sum of squares of the
 // new M in block b (problem b / chunks, block b % chunks of that problem).
