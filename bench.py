@@ -131,6 +131,27 @@ def summarize_counters(fetch_csv, write_csv, fetch_copy_csv, write_copy_csv, cop
            "hbm_write_bytes_per_launch": write_kib * 1024.0 * w_scale,
            "gemm_sha256_16": gemm_source_hash()}
     rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+
+    # cross-check of the streaming passes: scaled counter bytes over all their
+    # dispatches against the algorithmic bytes of the same dispatches (the run
+    # does 1 warm-up + 2 timed steps of the workload, then the AdamW measurement)
+    import workloads as W
+    wl = W.workload(workload)
+    steps = 3
+    mom_bytes = wl.muon_elements * (10 if wl.grad_dtype != "f32" else 12) * steps
+
+    def total(path, name_part):
+        return sum(float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                   if name_part in r["Kernel_Name"])
+
+    def streaming(name_part, algorithmic):
+        rd = total(fetch_csv, name_part) * 1024.0 * f_scale
+        wr = total(write_csv, name_part) * 1024.0 * w_scale
+        return {"counter_read_bytes": rd, "counter_write_bytes": wr,
+                "algorithmic_bytes": algorithmic,
+                "counter_over_algorithmic": (rd + wr) / algorithmic if algorithmic else None}
+
+    rec["streaming"] = {"momentum_sumsq_kernel": streaming("momentum_sumsq_kernel", mom_bytes)}
     run = f"python3 $REPO/bench.py --workload {workload} --method {method} --steps 2 --warmup 1 --no-cpu-baseline"
     cal = "python3 $REPO/bench.py --copy-calibration"
     rec["commands"] = [
@@ -144,6 +165,25 @@ def summarize_counters(fetch_csv, write_csv, fetch_copy_csv, write_copy_csv, cop
         "<write_copy>/run_counter_collection.csv",
     ]
     return rec
+
+
+def summarize_mfma(csv_path, symbol):
+    """MFMA utilisation of `symbol` from a rocprofv3 run with SQ_VALU_MFMA_BUSY_CYCLES
+    and GRBM_GUI_ACTIVE: MFMA-busy SIMD cycles over the SIMD cycles the kernel was
+    active (GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs)."""
+    import csv
+    busy, gui, n = 0.0, 0.0, 0
+    for r in csv.DictReader(open(csv_path)):
+        if symbol not in r["Kernel_Name"]:
+            continue
+        if r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES":
+            busy += float(r["Counter_Value"])
+            n += 1
+        elif r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            gui += float(r["Counter_Value"])
+    frac = busy / (gui / 8.0 * 1024.0) if gui > 0 else None
+    return {"kernel_symbol": symbol, "dispatches": n, "mfma_busy_cycles": busy,
+            "gui_active_cycles": gui, "mfma_busy_fraction": frac}
 
 
 def cpu_baseline(wl, method, budget_s=25.0):
@@ -251,7 +291,25 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                               "FETCH_COPY_CSV", "WRITE_COPY_CSV"))
+    ap.add_argument("--summarize-mfma", metavar="MFMA_CSV")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0ELb1EEEvNS_9GemmBatchE" if args.method == "standard"
+                  else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0ELb0EEEvNS_9GemmBatchE")
+        rec = summarize_mfma(args.summarize_mfma, symbol)
+        run = (f"python3 $REPO/bench.py --workload {args.workload} --method {args.method} "
+               "--steps 2 --warmup 1 --no-cpu-baseline")
+        rec["commands"] = [
+            "cd /tmp && export TMPDIR=/tmp",
+            f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -d <mfma> -o run --output-format csv -- {run}",
+            f"python3 bench.py --workload {args.workload} --method {args.method} "
+            "--summarize-mfma <mfma>/run_counter_collection.csv",
+        ]
+        path = os.path.join(ROOT, "profiles", f"mfma_ns_gemm_update_{WORKLOAD_SLUG[args.workload]}_{args.method}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
     if args.summarize_counters:
         ns_dtype = "bf16" if args.method == "standard" else "f16"
         symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0ELb1EEEvNS_9GemmBatchE" if ns_dtype == "bf16"
