@@ -170,6 +170,23 @@ def test_batch_invariance_and_determinism(lib, method, ns_dtype):
             assert np.array_equal(x[sl], y[sl])        # alone == in a batch
 
 
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_transposed_neighbour_changes_nothing(lib, method, ns_dtype):
+    # short side <= 128 (one tile row): X0 and its Gram matrix come out of one
+    # pass, which turns a transposed problem in LDS. Adding transposed problems to
+    # the shape groups must not move the other problems' results by a bit.
+    shapes = [(128, 640, 0), (96, 700, 0), (128, 640, 0), (640, 128, 0), (700, 96, 0)]
+    wl = W.custom_workload(shapes, wid=111)
+    params, grads, mom = W.host_inputs(wl)
+    tab = wl.table()
+    h = _hyper(lib, wl, method, ns_dtype)
+    plain = _dev_step(lib, params, grads, mom, tab[:3], h)
+    mixed = _dev_step(lib, params, grads, mom, tab, h)
+    for sl in entry_slices(tab[:3]):
+        for x, y in zip(plain, mixed):
+            assert np.array_equal(x[sl], y[sl])
+
+
 def test_special_cases_bit_exact(lib):
     wl = W.custom_workload([(64, 200, 0), (300, 64, 0)], grad_dtype="bf16", wid=108)
     params, grads, mom = W.host_inputs(wl)
