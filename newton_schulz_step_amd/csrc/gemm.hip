@@ -66,6 +66,14 @@ template <> struct Mfma<float> {
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
+// Pair swizzle of the K x N operand (rows of 32-byte pairs in LDS): pair p of K row
+// kr is stored at pair slot p ^ nn_swz(kr). A 16-bit transposed read takes, per
+// half wave, two adjacent pairs (2q, 2q + 1) from four consecutive K rows; the
+// slots of those rows differ in bits 1-2, so the eight 32-byte reads fall in eight
+// different bank groups. An fp32 read takes four pairs from rows kr and kr + 4,
+// whose slots differ in bit 2. Row writes stay a permutation of each row.
+__device__ __forceinline__ int nn_swz(int kr) { return ((kr & 3) << 1) ^ (kr & 4); }
+
 // Transposed LDS read of 16-bit elements (gfx950 ds_read_b64_tr_b16). In each
 // group of 16 lanes, lane s supplies the address of 4 consecutive elements;
 // lane l of the group receives element l % 4 of the rows addressed by lanes
@@ -208,7 +216,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
   // chunk ^ swz(row) of its 128-byte LDS row.
   // NN Q (stored K x N, N contiguous): the slice is KS rows of TILE columns; load
   // `it` of thread t covers chunk (it * 256 + t) of the row-major slice, stored in
-  // an RB-byte LDS row with its 32-byte pair index XORed with (row & 7).
+  // an RB-byte LDS row with its 32-byte pair index XORed with nn_swz(row).
   const char* Pb = static_cast<const char*>(a.P) +
                    (static_cast<int64_t>(prob) * a.p_ps + static_cast<int64_t>(ti) * TILE * a.ldp) * ESZ;
   const char* Qb = static_cast<const char*>(a.Q) +
@@ -223,7 +231,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
       const int id = it * 256 + static_cast<int>(threadIdx.x);
       const int kr = id / CPRQ, c = id % CPRQ;
       gp[v] = Qb + static_cast<int64_t>(kr) * a.ldq * ESZ + c * 16;
-      wofs[v] = OPB + kr * RB + (((c >> 1) ^ (kr & 7)) << 5) + ((c & 1) << 4);
+      wofs[v] = OPB + kr * RB + (((c >> 1) ^ nn_swz(kr)) << 5) + ((c & 1) << 4);
     } else {
       const int r = (wave * LOADS + it) * 8 + (lane >> 3);
       const int c = lane & 7;
@@ -279,7 +287,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
           col = nb + (lane & 31);
         }
         const int cb = col * ESZ;   // byte column
-        bnn[j][h] = OPB + kr * RB + ((((cb >> 5) ^ (kr & 7))) << 5) + (cb & 31);
+        bnn[j][h] = OPB + kr * RB + ((((cb >> 5) ^ nn_swz(kr))) << 5) + (cb & 31);
       }
     }
   }
@@ -755,7 +763,7 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
   for (int v = 0; v < 8; ++v) {
     const int sl = v >> 2, id = (v & 3) * 256 + tid, kr = id >> 4, c = id & 15;
     xsrc[v] = (static_cast<int64_t>(sl * KS + kr) * a.ldq) * 2 + c * 16;
-    xofs[v] = sl * XSB + kr * RB + (((c >> 1) ^ (kr & 7)) << 5) + ((c & 1) << 4);
+    xofs[v] = sl * XSB + kr * RB + (((c >> 1) ^ nn_swz(kr)) << 5) + ((c & 1) << 4);
   }
   auto xload = [&](u16x8 (&r)[8], int jt) {
     const int64_t col = static_cast<int64_t>(jt) * 128 * 2;
@@ -787,7 +795,7 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
       const int gq = lane >> 4, sl = lane & 15;
       const int kr = 8 * (gq >> 1) + 4 * h + (sl >> 2);
       const int cb = (wn * HALF + j * 32 + 16 * (gq & 1) + 4 * (sl & 3)) * 2;
-      bnn[j][h] = kr * RB + (((cb >> 5) ^ (kr & 7)) << 5) + (cb & 31);
+      bnn[j][h] = kr * RB + (((cb >> 5) ^ nn_swz(kr)) << 5) + (cb & 31);
     }
 
   f32x16 accA[WB][WB], accC[WB][WB];
@@ -854,7 +862,7 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
         const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
         const int ksl = gi >> 6, kr = gi & 63, cb = gj * 2;
         const u16x8 dq = *reinterpret_cast<const u16x8*>(Xs + ksl * XSB + kr * RB +
-                                                         (((cb >> 5) ^ (kr & 7)) << 5) + (cb & 31));
+                                                         (((cb >> 5) ^ nn_swz(kr)) << 5) + (cb & 31));
         T o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
