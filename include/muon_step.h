@@ -83,9 +83,14 @@ enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1, MUON_DTYPE_F16 = 2 };
 enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 };
 
 /* Size limits: min(rows, cols) of a problem <= MUON_MAX_SHORT_SIDE,
- * max(rows, cols) <= MUON_MAX_LONG_SIDE. */
+ * max(rows, cols) <= MUON_MAX_LONG_SIDE; over a whole table, the sum of
+ * rows * cols <= MUON_MAX_TABLE_ELEMENTS (2^36: 275 GB of fp32 parameters
+ * alone, more than one GPU holds) and the problems (whole matrices plus split
+ * blocks) <= MUON_MAX_PROBLEMS. Within them every launch grid of a step fits. */
 #define MUON_MAX_SHORT_SIDE 16384
 #define MUON_MAX_LONG_SIDE (1 << 24)
+#define MUON_MAX_TABLE_ELEMENTS (1LL << 36)
+#define MUON_MAX_PROBLEMS (1 << 24)
 
 /* One Muon-target matrix inside the packed buffers. params, grads, momentum
  * (and update_out / bf16_shadow when given) share one layout: the matrix is

@@ -54,6 +54,7 @@ int validate(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* 
   }
   std::vector<std::pair<int64_t, int64_t>> spans;
   spans.reserve(n_entries);
+  int64_t elements = 0, problems = 0;
   for (int32_t i = 0; i < n_entries; ++i) {
     const muon_matrix_t& e = table[i];
     const std::string at = " (entry " + std::to_string(i) + ")";
@@ -63,7 +64,16 @@ int validate(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* 
     const int64_t pr = e.split_rows > 0 ? e.split_rows : e.rows;
     const int64_t m = std::min(pr, e.cols), n = std::max(pr, e.cols);
     if (m > MUON_MAX_SHORT_SIDE || n > MUON_MAX_LONG_SIDE) { err = "matrix beyond the size limits" + at; return MUON_ERR_BAD_SHAPE; }
+    // running totals, compared without overflow: rows <= (limit - elements) / cols
+    if (e.rows > (MUON_MAX_TABLE_ELEMENTS - elements) / e.cols) {
+      err = "the table holds more than MUON_MAX_TABLE_ELEMENTS elements" + at;
+      return MUON_ERR_BAD_SHAPE;
+    }
+    elements += e.rows * e.cols;
+    problems += e.rows / pr;
+    if (problems > MUON_MAX_PROBLEMS) { err = "the table expands to more than MUON_MAX_PROBLEMS problems" + at; return MUON_ERR_BAD_SHAPE; }
     if (e.offset < 0) { err = "offset < 0" + at; return MUON_ERR_RANGE; }
+    if (e.offset > INT64_MAX - MUON_MAX_TABLE_ELEMENTS) { err = "offset beyond the addressable range" + at; return MUON_ERR_RANGE; }
     if (e.offset % 8 != 0) { err = "offset is not a multiple of 8 elements" + at; return MUON_ERR_ALIGN; }
     spans.emplace_back(e.offset, e.rows * e.cols);
   }

@@ -82,6 +82,19 @@ def test_workspace_size_validation(lib):
     assert "standard" in msg and "gram" in msg
 
 
+def test_table_wide_limits(lib):
+    # MUON_MAX_TABLE_ELEMENTS (2^36) over the whole table, MUON_MAX_PROBLEMS
+    # (2^24) expanded problems, and offsets that cannot overflow offset + size
+    lim = 1 << 36
+    assert _ws([(0, 1 << 12, 1 << 24, 1 << 8)])[0] == nss.OK                 # exactly 2^36
+    assert _ws([(0, 1 << 12, 1 << 24, 1 << 8), (1 << 36, 1, 8, 0)])[0] == nss.ERR_BAD_SHAPE
+    assert _ws([(0, (1 << 40) + 8, 1 << 24, 8)])[0] == nss.ERR_BAD_SHAPE     # product would overflow
+    st, msg = _ws([(0, (1 << 24) + 1, 1, 1)])                                # one problem too many
+    assert st == nss.ERR_BAD_SHAPE and "MUON_MAX_PROBLEMS" in msg
+    assert _ws([((1 << 63) - 8, 1, 8, 0)])[0] == nss.ERR_RANGE
+    assert _ws([(lim, 1, 8, 0)])[0] == nss.OK
+
+
 def test_workspace_grows_with_the_table(lib):
     h = nss.hyper(ns_method="standard", ns_dtype="bf16")
     small = nss.workspace_size([(0, 128, 128, 0)], h)
