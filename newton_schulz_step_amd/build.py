@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -27,15 +28,36 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# per-kernel resource remarks of the device compile, checked below
+REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def _scratch_users(stderr: str):
+    """Kernels whose resource remarks report scratch (private) memory."""
+    users, name = [], None
+    for line in stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            users.append((name, int(m.group(1))))
+    return users
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    hip = src.endswith(".hip")
+    lang = ["-x", "hip"] if hip else []
+    cmd = [HIPCC, *FLAGS, *lang, *(REMARKS if hip else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    # a kernel that spills to scratch runs several times slower: refuse to build it
+    bad = _scratch_users(r.stderr) if hip else []
+    if bad:
+        raise RuntimeError(f"kernels in {src} use scratch memory: " +
+                           ", ".join(f"{k} ({b} bytes/lane)" for k, b in bad))
     return obj
 
 

@@ -187,6 +187,25 @@ def test_transposed_neighbour_changes_nothing(lib, method, ns_dtype):
             assert np.array_equal(x[sl], y[sl])
 
 
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_tile_edge_invariance_with_padding(lib, method, ns_dtype):
+    # 64 blocks of 640 x 640: the batch is large enough for 256-tiles, padded to
+    # 768 (the last tile row half empty); one block alone runs 128-tiles. Same
+    # products in the same k order, so the same bits; and the batch meets the
+    # oracle's gates.
+    k, cnt = 640, 64
+    wl = W.custom_workload([(k * cnt, k, k)], wid=112)
+    _check(lib, wl, method, ns_dtype, faithful=True)
+    params, grads, mom = W.host_inputs(wl)
+    h = _hyper(lib, wl, method, ns_dtype)
+    batch = _dev_step(lib, params, grads, mom, wl.table(), h)
+    for b in (0, cnt - 1):
+        sl = slice(b * k * k, (b + 1) * k * k)
+        alone = _dev_step(lib, params, grads, mom, [(b * k * k, k, k, 0)], h)
+        for x, y in zip(alone, batch):
+            assert np.array_equal(x[sl], y[sl]), b
+
+
 def test_special_cases_bit_exact(lib):
     wl = W.custom_workload([(64, 200, 0), (300, 64, 0)], grad_dtype="bf16", wid=108)
     params, grads, mom = W.host_inputs(wl)
