@@ -218,19 +218,51 @@ def _stream(t, stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _device(*tensors):
+    """The one GPU all given tensors (None skipped) live on. The library builds its
+    per-table plan on the current device, so every call runs under this one."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"tensors passed to libmuonstep must share one GPU, got {sorted(map(str, devs))}")
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError("tensors passed to libmuonstep must be on a GPU")
+    return dev
+
+
 _ws_cache: Dict[Tuple[int, int], object] = {}
+_ws_lock = threading.Lock()
+_WS_CACHE_MAX = 16      # (device, stream) pairs kept; the oldest is dropped first
 
 
-def workspace(nbytes: int, device) -> "torch.Tensor":
-    """A cached device workspace of at least `nbytes` bytes (torch allocation)."""
+def workspace(nbytes: int, device, stream=None) -> "torch.Tensor":
+    """A device workspace of at least `nbytes` bytes, cached per (device, stream).
+
+    Steps enqueued on one stream reuse it in stream order; steps on different
+    streams get different buffers, so they may run concurrently. A torch stream's
+    buffer is allocated on that stream, so when a larger one replaces it the old
+    memory is recycled in that stream's order. With a raw stream handle the
+    caller orders the stream against torch's current stream. At most
+    _WS_CACHE_MAX buffers are kept (a dropped one was allocated on its own
+    stream, so torch reuses its memory in that stream's order)."""
     torch = _torch()
     dev = torch.device(device)
-    key = dev.index if dev.index is not None else torch.cuda.current_device()
-    buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
-        _ws_cache.pop(key, None)
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-        _ws_cache[key] = buf
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    s = stream if stream is not None else torch.cuda.current_stream(idx)
+    key = (idx, s.cuda_stream if hasattr(s, "cuda_stream") else int(s))
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            _ws_cache.pop(key, None)
+            size = max(nbytes, 256)
+            if isinstance(s, torch.cuda.Stream):
+                with torch.cuda.stream(s):
+                    buf = torch.empty(size, dtype=torch.uint8, device=torch.device("cuda", idx))
+            else:
+                buf = torch.empty(size, dtype=torch.uint8, device=torch.device("cuda", idx))
+            _ws_cache[key] = buf
+            while len(_ws_cache) > _WS_CACHE_MAX:
+                _ws_cache.pop(next(iter(_ws_cache)))
     return buf
 
 
@@ -245,18 +277,20 @@ def step(params, grads, momentum, entries, h: MuonHyper, ws=None, update_out=Non
     numel = params.numel()
     if grads.numel() != numel or momentum.numel() != numel:
         raise ValueError("params, grads and momentum must have the same numel")
+    dev = _device(params, grads, momentum, ws, update_out, bf16_shadow)
     arr, n = table(entries)
     need = ctypes.c_size_t(0)
     _check(load().muon_workspace_size(arr, n, ctypes.byref(h), ctypes.byref(need)))
     if ws is None:
-        ws = workspace(need.value, params.device)
+        ws = workspace(need.value, dev, stream)
     if update_out is not None and (update_out.dtype != torch.float32 or update_out.numel() != numel):
         raise ValueError("update_out must be float32 with params' numel")
     if bf16_shadow is not None and (bf16_shadow.element_size() != 2 or bf16_shadow.numel() != numel):
         raise ValueError("bf16_shadow must be a 16-bit tensor with params' numel")
-    _check(load().muon_step(_ptr(params), _ptr(grads), _ptr(momentum), numel, arr, n,
-                            ctypes.byref(h), _ptr(ws), ws.numel() * ws.element_size(),
-                            _ptr(update_out), _ptr(bf16_shadow), _stream(params, stream)))
+    with torch.cuda.device(dev):
+        _check(load().muon_step(_ptr(params), _ptr(grads), _ptr(momentum), numel, arr, n,
+                                ctypes.byref(h), _ptr(ws), ws.numel() * ws.element_size(),
+                                _ptr(update_out), _ptr(bf16_shadow), _stream(params, stream)))
 
 
 def windows(ws: Iterable[Sequence[int]], n: int):
@@ -283,21 +317,23 @@ def step_window(partition, grads, momentum, entries, wins, h: MuonHyper, ws=None
     numel = momentum.numel()
     if grads.numel() != numel:
         raise ValueError("grads and momentum must have the same numel")
+    dev = _device(partition, grads, momentum, ws, update_out, bf16_shadow)
     arr, n = table(entries)
     warr = windows(wins, n)
     need = ctypes.c_size_t(0)
     _check(load().muon_workspace_size(arr, n, ctypes.byref(h), ctypes.byref(need)))
     if ws is None:
-        ws = workspace(need.value, momentum.device)
+        ws = workspace(need.value, dev, stream)
     if update_out is not None and (update_out.dtype != torch.float32 or update_out.numel() != numel):
         raise ValueError("update_out must be float32 with momentum's numel")
     if bf16_shadow is not None and (bf16_shadow.element_size() != 2 or
                                     bf16_shadow.numel() != partition.numel()):
         raise ValueError("bf16_shadow must be a 16-bit tensor with the partition's numel")
-    _check(load().muon_step_window(_ptr(partition), partition.numel(), _ptr(grads), _ptr(momentum),
-                                   numel, arr, warr, n, ctypes.byref(h), _ptr(ws),
-                                   ws.numel() * ws.element_size(), _ptr(update_out),
-                                   _ptr(bf16_shadow), _stream(momentum, stream)))
+    with torch.cuda.device(dev):
+        _check(load().muon_step_window(_ptr(partition), partition.numel(), _ptr(grads), _ptr(momentum),
+                                       numel, arr, warr, n, ctypes.byref(h), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _ptr(update_out),
+                                       _ptr(bf16_shadow), _stream(momentum, stream)))
 
 
 def _method_code(method) -> int:
@@ -362,24 +398,44 @@ def adamw(params, grads, m, v, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-10, weight
     h.lr, h.beta1, h.beta2, h.eps, h.weight_decay = lr, beta1, beta2, eps, weight_decay
     h.step = step
     h.grad_dtype = _dtype_code(grads)
-    _check(load().adamw_step(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), numel, ctypes.byref(h),
-                             _stream(params, stream)))
+    dev = _device(params, grads, m, v)
+    with torch.cuda.device(dev):
+        _check(load().adamw_step(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), numel, ctypes.byref(h),
+                                 _stream(params, stream)))
+
+
+def _copy_args(packed, tensors: Sequence, entries):
+    """Table and pointer array for pack / unpack; each tensor must hold exactly its
+    entry's rows * cols elements of the packed buffer's dtype (the copy is sized
+    from the table and that dtype)."""
+    tensors = list(tensors)
+    arr, n = table(entries)
+    if len(tensors) != n:
+        raise ValueError(f"{len(tensors)} tensors for {n} table entries")
+    for i, t in enumerate(tensors):
+        if t.dtype != packed.dtype or t.numel() != arr[i].rows * arr[i].cols:
+            raise ValueError(f"tensor {i} must be {packed.dtype} with {arr[i].rows * arr[i].cols} elements, "
+                             f"got {t.dtype} with {t.numel()}")
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in tensors])
+    return arr, n, ptrs, _device(packed, *tensors)
 
 
 def pack(packed, tensors: Sequence, entries, stream=None) -> None:
     """Copy each tensor bit for bit into `packed` at its table offset."""
-    arr, n = table(entries)
-    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in tensors])
-    _check(load().muon_pack(_ptr(packed), packed.numel(), ptrs, arr, n, _dtype_code(packed),
-                            _stream(packed, stream)))
+    torch = _torch()
+    arr, n, ptrs, dev = _copy_args(packed, tensors, entries)
+    with torch.cuda.device(dev):
+        _check(load().muon_pack(_ptr(packed), packed.numel(), ptrs, arr, n, _dtype_code(packed),
+                                _stream(packed, stream)))
 
 
 def unpack(tensors: Sequence, packed, entries, stream=None) -> None:
     """Copy each table entry of `packed` bit for bit into its tensor."""
-    arr, n = table(entries)
-    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in tensors])
-    _check(load().muon_unpack(ptrs, _ptr(packed), packed.numel(), arr, n, _dtype_code(packed),
-                              _stream(packed, stream)))
+    torch = _torch()
+    arr, n, ptrs, dev = _copy_args(packed, tensors, entries)
+    with torch.cuda.device(dev):
+        _check(load().muon_unpack(ptrs, _ptr(packed), packed.numel(), arr, n, _dtype_code(packed),
+                                  _stream(packed, stream)))
 
 
 def release_plans() -> None:
