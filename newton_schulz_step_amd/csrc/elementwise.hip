@@ -29,11 +29,13 @@ __global__ __launch_bounds__(kMomThreads) void momentum_sumsq_kernel(float* M, c
   const int64_t c = b - p * chunks;
   const int64_t first = c * kMomChunk;                      // first element of the block within the problem
   const int len = static_cast<int>(min<int64_t>(kMomChunk, per_problem - first));
-  const int64_t start = probs[p].src_off + first;           // a multiple of 8 elements
+  // a multiple of 8 elements, except for split blocks whose size is not
+  // (those take the element path: the vector path needs 16-byte momentum)
+  const int64_t start = probs[p].src_off + first;
   const int tid = threadIdx.x;
   const int e0 = tid * 4;
   float ss = 0.0f;
-  if (e0 + 4 <= len) {
+  if (e0 + 4 <= len && ((start + e0) & 3) == 0) {
     float g[4];
     load_grad4<GDT>(G, start + e0, g);
     f32x4* mp = reinterpret_cast<f32x4*>(M + start + e0);
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(kMomThreads) void momentum_sumsq_kernel(float* M, c
     }
     *mp = m;
   } else {
-    for (int e = e0; e < len; ++e) {
+    for (int e = e0; e < min(e0 + 4, len); ++e) {
       const int64_t i = start + e;
       const float m = mu * M[i] + grad_to_f32<GDT>(G, i);
       M[i] = m;

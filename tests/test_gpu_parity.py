@@ -268,12 +268,14 @@ def test_three_steps_and_resume(lib):
 
 
 def test_unaligned_offsets_multiple_of_8(lib):
+    # entries at offsets that are multiples of 8 but not of 64, and split blocks
+    # of 15 and 14 elements, which start at any element alignment
     for gdt in ("f32", "bf16"):
-        shapes = [(40, 72, 0), (72, 40, 0), (9, 8, 0), (16, 24, 8)]
+        shapes = [(40, 72, 0), (72, 40, 0), (9, 8, 0), (16, 24, 8), (12, 5, 3), (10, 7, 2)]
         offs, cur = [], 8
         for r, c, _ in shapes:
             offs.append(cur)
-            cur += r * c + 8
+            cur = (cur + r * c + 8 + 7) // 8 * 8
         tab = [(o, r, c, s) for o, (r, c, s) in zip(offs, shapes)]
         rng = np.random.default_rng(5)
         n = cur + 8
