@@ -295,6 +295,17 @@ def test_unaligned_offsets_multiple_of_8(lib):
         assert np.array_equal(p[mask], params[mask]) and np.array_equal(m[mask], mom[mask])
 
 
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_misaligned_split_blocks_half_precision(lib, method, ns_dtype):
+    # split blocks of 15, 30 (stored transposed: 10 x 3), 14 and 260 elements
+    # start at every alignment; short sides <= 128 take the one-pass X0 + Gram
+    # kernel, which reads them (and turns the transposed ones) per element when
+    # a vector read would be misaligned
+    wl = W.custom_workload([(12, 5, 3), (20, 3, 10), (10, 7, 2), (6, 130, 2)], grad_dtype="bf16",
+                           wid=113)
+    _check(lib, wl, method, ns_dtype, faithful=True)
+
+
 def test_empty_table_and_small_workspace(lib):
     import torch
     dev = "cuda:0"
