@@ -295,6 +295,38 @@ def test_unaligned_offsets_multiple_of_8(lib):
         assert np.array_equal(p[mask], params[mask]) and np.array_equal(m[mask], mom[mask])
 
 
+@pytest.mark.parametrize("method,ns_dtype,steps,coeffs", [
+    ("standard", "f32", 1, None), ("standard", "f32", 2, (3.0, -3.2, 1.2)), ("gram", "f32", 1, None),
+    ("gram", "f32", 3, (3.0, -3.2, 1.2)), ("standard", "bf16", 1, None), ("standard", "bf16", 7, None),
+    ("gram", "f16", 2, None), ("gram", "f16", 4, (3.0, -3.2, 1.2))])
+def test_step_counts_and_coefficients(lib, method, ns_dtype, steps, coeffs):
+    # the launch sequence special-cases the first and the last iteration (one
+    # step: no update + Gram pass, no R update; P = Q at the first Gram step),
+    # on a 128-row group (one-pass kernels) and a 256-row one. (Gram in fp16 with
+    # these coefficients at 6 steps is not a fair case for the 3e-2 gate: on this
+    # input two storage-faithful evaluations that differ only in float64 vs
+    # float32 arithmetic between the rounding points are already 4.7e-2 apart;
+    # at 4 steps, 2.5e-3.)
+    wl = W.custom_workload([(128, 640, 0), (640, 128, 0), (256, 384, 0)],
+                           grad_dtype="f32" if ns_dtype == "f32" else "bf16", wid=114)
+    params, grads, mom = W.host_inputs(wl)
+    tab = wl.table()
+    kw = dict(ns_steps=steps)
+    if coeffs:
+        kw.update(ns_a=coeffs[0], ns_b=coeffs[1], ns_c=coeffs[2])
+    gpu = run_step(lib, params, grads, mom, tab, _hyper(lib, wl, method, ns_dtype, **kw))
+    g64 = W.grad_as_f64(wl, grads)
+    okw = dict(lr=wl.lr, mu=wl.momentum, weight_decay=wl.weight_decay, method=method, steps=steps)
+    if coeffs:
+        okw["coeffs"] = coeffs
+    ref = oracle.muon_step(params, g64, mom, tab, store_fmt=None if ns_dtype == "f32" else ns_dtype, **okw)
+    gate = FP32_GATE if ns_dtype == "f32" else LP_GATE
+    for i, sl in enumerate(entry_slices(tab)):
+        eo = rel(gpu["update"][sl], ref["update"][sl])
+        print(f"  entry {i}: O {eo:.2e}")
+        assert eo <= gate, (i, eo)
+
+
 @pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
 def test_misaligned_split_blocks_half_precision(lib, method, ns_dtype):
     # split blocks of 15, 30 (stored transposed: 10 x 3), 14 and 260 elements
