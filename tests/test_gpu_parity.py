@@ -114,6 +114,28 @@ def test_half_precision_lowrank(lib, method, ns_dtype):
     _check(lib, wl, method, ns_dtype, faithful=True, subspace=True)
 
 
+def test_fp16_grads(lib):
+    # fp16 gradients (read with their own conversion) through an fp32 iteration,
+    # against the exact oracle, on a 128-tile group, a transposed matrix and a split
+    import torch
+    shapes = [(200, 300, 0), (300, 200, 0), (128, 512, 0), (96, 700, 32)]
+    wl = W.custom_workload(shapes, grad_dtype="f32", wid=115, grad_kind="lowrank")
+    params, g32, mom = W.host_inputs(wl)
+    g16 = g32.astype(np.float16)
+    h = _hyper(lib, wl, "standard", "f32", grad_dtype="f16")
+    p = to_device(params, "cuda:0", torch)
+    g = torch.from_numpy(g16).to("cuda:0")
+    m = to_device(mom, "cuda:0", torch)
+    u = torch.zeros_like(p)
+    lib.step(p, g, m, wl.table(), h, update_out=u)
+    torch.cuda.synchronize()
+    ref = oracle.muon_step(params, g16.astype(np.float64), mom, wl.table(), lr=wl.lr, mu=wl.momentum,
+                           weight_decay=wl.weight_decay, method="standard")
+    for i, sl in enumerate(entry_slices(wl.table())):
+        assert rel(u.cpu().numpy()[sl], ref["update"][sl]) <= FP32_GATE, i
+        assert rel(m.cpu().numpy()[sl], ref["momentum"][sl]) <= MOM_GATE, i
+
+
 def test_fp32_grads_half_iteration(lib):
     wl = W.custom_workload([(192, 320, 0), (320, 192, 0)], grad_dtype="f32", wid=104,
                            grad_kind="lowrank")
@@ -393,17 +415,20 @@ def test_pack_unpack_bit_exact(lib, dtype):
 
 # --------------------------------------------------------------------------- AdamW
 
-@pytest.mark.parametrize("gdt", ["bf16", "f32"])
+@pytest.mark.parametrize("gdt", ["bf16", "f32", "f16"])
 def test_adamw_against_oracle(lib, gdt):
     import torch
     dev = "cuda:0"
     n = 1_000_003                                   # ragged tail (n % 8 != 0)
     p0, gb, m0, v0 = W.adamw_inputs(n, seed=1)
     g32 = W.bf16_bits_to_f32(gb)
-    grads_host = gb if gdt == "bf16" else g32
+    if gdt == "f16":                                # the same values, exactly representable in fp16
+        g32 = g32.astype(np.float16).astype(np.float32)
+        g = torch.from_numpy(g32.astype(np.float16)).to(dev)
+    else:
+        g = to_device(gb if gdt == "bf16" else g32, dev, torch)
     lr, b1, b2, eps, wd = 3e-4, 0.9, 0.95, 1e-8, 0.1
     p, m, v = (torch.from_numpy(a.copy()).to(dev) for a in (p0, m0, v0))
-    g = to_device(grads_host, dev, torch)
     P, M, V = p0.astype(np.float64), m0.astype(np.float64), v0.astype(np.float64)
     for t in (1, 2, 3):
         lib.adamw(p, g, m, v, lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, step=t)
