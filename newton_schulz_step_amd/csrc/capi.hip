@@ -569,7 +569,7 @@ static int step_impl(float* params, int64_t params_numel, const void* grads, flo
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* partials = reinterpret_cast<float*>(ws + P->L.off_partials);
+  double* partials = reinterpret_cast<double*>(ws + P->L.off_partials);
   float* invn = reinterpret_cast<float*>(ws + P->L.off_invnorm);
   const float mu = h->momentum;
   for (const Group& G : P->L.groups)

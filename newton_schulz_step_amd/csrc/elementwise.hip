@@ -19,11 +19,13 @@ namespace muon {
 // One block of kMomThreads threads updates kMomChunk consecutive elements of one
 // problem, four per thread (one 16-byte momentum vector): many small blocks keep
 // the most reads and writes in flight across the HBM channels.
+// The squares are summed in float64: the update does not depend on the scale of
+// M, and the square of an entry above ~1.8e19 overflows float32.
 template <int GDT>
 __global__ __launch_bounds__(kMomThreads) void momentum_sumsq_kernel(float* M, const void* G, const ProblemDesc* probs,
                                                                      int64_t per_problem, int64_t chunks, float mu,
-                                                                     float* partials) {
-  __shared__ float red[kMomThreads / 64];
+                                                                     double* partials) {
+  __shared__ double red[kMomThreads / 64];
   const int64_t b = blockIdx.x;
   const int64_t p = b / chunks;
   const int64_t c = b - p * chunks;
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(kMomThreads) void momentum_sumsq_kernel(float* M, c
   const int64_t start = probs[p].src_off + first;
   const int tid = threadIdx.x;
   const int e0 = tid * 4;
-  float ss = 0.0f;
+  double ss = 0.0;
   if (e0 + 4 <= len && ((start + e0) & 3) == 0) {
     float g[4];
     load_grad4<GDT>(G, start + e0, g);
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(kMomThreads) void momentum_sumsq_kernel(float* M, c
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       m[e] = mu * m[e] + g[e];
-      ss += m[e] * m[e];
+      ss += static_cast<double>(m[e]) * m[e];
     }
     *mp = m;
   } else {
@@ -51,17 +53,17 @@ __global__ __launch_bounds__(kMomThreads) void momentum_sumsq_kernel(float* M, c
       const int64_t i = start + e;
       const float m = mu * M[i] + grad_to_f32<GDT>(G, i);
       M[i] = m;
-      ss += m * m;
+      ss += static_cast<double>(m) * m;
     }
   }
-  ss = wave_sum(ss);
+  ss = wave_sum_d(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
   if (tid == 0) partials[b] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const ProblemDesc* probs, int n_problems,
-                                 int64_t per_problem, int64_t chunks, float mu, float* partials, hipStream_t s) {
+                                 int64_t per_problem, int64_t chunks, float mu, double* partials, hipStream_t s) {
   static_assert(kMomThreads == 256, "the block reduction sums four waves");
   const int64_t blocks = static_cast<int64_t>(n_problems) * chunks;
   if (blocks <= 0) return hipSuccess;
@@ -88,19 +90,19 @@ hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const 
 // One block per problem: thread t sums partials t, t + 256, ... into four
 // float64 accumulators (k mod 4), combined in a fixed order, then waves and the
 // block in a fixed order; the result depends only on the problem's own partials.
-__global__ __launch_bounds__(256) void finalize_norm_kernel(const float* partials, int64_t chunks, float eps,
+__global__ __launch_bounds__(256) void finalize_norm_kernel(const double* partials, int64_t chunks, float eps,
                                                             float* inv_norm) {
   __shared__ double red[4];
   const int p = blockIdx.x;
   const int tid = threadIdx.x;
-  const float* part = partials + static_cast<int64_t>(p) * chunks;
+  const double* part = partials + static_cast<int64_t>(p) * chunks;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   int64_t k = tid;
   for (; k + 3 * 256 < chunks; k += 4 * 256) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += static_cast<double>(part[k + u * 256]);
+    for (int u = 0; u < 4; ++u) acc[u] += part[k + u * 256];
   }
-  for (int u = 0; k < chunks; k += 256, ++u) acc[u] += static_cast<double>(part[k]);
+  for (int u = 0; k < chunks; k += 256, ++u) acc[u] += part[k];
   double s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   s = wave_sum_d(s);
   if ((tid & 63) == 0) red[tid >> 6] = s;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(const float* partial
                                                         static_cast<double>(eps)));
 }
 
-hipError_t launch_finalize_norm(const float* partials, int64_t chunks, int n_problems, float eps, float* inv_norm,
+hipError_t launch_finalize_norm(const double* partials, int64_t chunks, int n_problems, float eps, float* inv_norm,
                                 hipStream_t s) {
   if (n_problems <= 0) return hipSuccess;
   hipLaunchKernelGGL(finalize_norm_kernel, dim3(n_problems), dim3(256), 0, s, partials, chunks, eps, inv_norm);

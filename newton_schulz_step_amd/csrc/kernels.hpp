@@ -62,12 +62,12 @@ hipError_t launch_prep_gram(int dtype, const PrepGramArgs& a, hipStream_t s);
 
 // M <- mu M + G over every problem of a group (each m n contiguous elements at
 // its src_off), kMomChunk elements per block; partials[b] = sum of squares of the
-// new M in block b (problem b / chunks, block b % chunks of that problem).
+// new M in block b (problem b / chunks, block b % chunks of that problem), float64.
 hipError_t launch_momentum_sumsq(int grad_dtype, float* M, const void* G, const ProblemDesc* probs, int n_problems,
-                                 int64_t per_problem, int64_t chunks, float mu, float* partials, hipStream_t s);
+                                 int64_t per_problem, int64_t chunks, float mu, double* partials, hipStream_t s);
 
 // inv_norm[p] = 1 / (sqrt(sum of the `chunks` partials of p) + eps), summed in a fixed order.
-hipError_t launch_finalize_norm(const float* partials, int64_t chunks, int n_problems, float eps, float* inv_norm,
+hipError_t launch_finalize_norm(const double* partials, int64_t chunks, int n_problems, float eps, float* inv_norm,
                                 hipStream_t s);
 
 // X0 (canonical m x n, padded mp x np, row-major) of every problem of a group,

@@ -170,7 +170,7 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
   const size_t esz = static_cast<size_t>(element_size(h->ns_dtype));
   size_t off = 0;
   L.off_partials = off;
-  off = align256(off + L.n_partials * sizeof(float));
+  off = align256(off + L.n_partials * sizeof(double));
   L.off_invnorm = off;
   off = align256(off + L.problems.size() * sizeof(float));
   for (Group& G : L.groups) {

@@ -251,6 +251,24 @@ def test_special_cases_bit_exact(lib):
         assert np.array_equal(p[s], params[s] * decay)
 
 
+@pytest.mark.parametrize("scale", [1e20, 1e35])
+def test_huge_gradients_keep_their_direction(lib, scale):
+    # the update is invariant to the scale of the momentum; squares of entries
+    # above ~1.8e19 overflow float32, so the sums of squares must not be kept in it
+    wl = W.custom_workload([(128, 512, 0), (300, 200, 0)], grad_dtype="f32", ns_dtype="f32", wid=117)
+    params, grads, mom = W.host_inputs(wl)
+    grads = (grads.astype(np.float64) * scale).astype(np.float32)
+    tab = wl.table()
+    h = _hyper(lib, wl, "standard", "f32")
+    _, m, u = _dev_step(lib, params, grads, mom, tab, h)
+    ref = oracle.muon_step(params, grads.astype(np.float64), mom, tab, lr=wl.lr, mu=wl.momentum,
+                           weight_decay=wl.weight_decay, method="standard")
+    for i, sl in enumerate(entry_slices(tab)):
+        assert np.all(np.isfinite(u[sl])), i
+        assert rel(u[sl], ref["update"][sl]) <= FP32_GATE, (i, rel(u[sl], ref["update"][sl]))
+        assert rel(m[sl], ref["momentum"][sl]) <= MOM_GATE, i
+
+
 def test_nan_gradient_propagates_only_to_its_problem(lib):
     wl = W.custom_workload([(128, 256, 0), (128, 256, 0)], grad_dtype="bf16", wid=109)
     params, grads, mom = W.host_inputs(wl)
