@@ -1,0 +1,121 @@
+"""GPU: the library's runtime services, through the C ABI.
+
+- Plan cache: a step after muon_release_plans() rebuilds the table's plan and
+  gives the same bits; many distinct tables each get their own plan.
+- Profiling hooks: between muon_profile_begin() and muon_profile_end() every
+  launch is counted under its kind; the counts are the launch sequence of the
+  method (which bench.py's per-kernel times rely on).
+- Threads: two host threads stepping different tables on their own streams
+  give the same bits as the same steps run one after the other.
+"""
+import threading
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_helpers import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(shapes, wid, grad_dtype="bf16"):
+    wl = W.custom_workload(shapes, grad_dtype=grad_dtype, wid=wid)
+    params, grads, mom = W.host_inputs(wl)
+    return wl, params, grads, mom
+
+
+def _step(nss, wl, params, grads, mom, h, stream=None):
+    import torch
+    p, g, m = (to_device(a.copy(), "cuda:0", torch) for a in (params, grads, mom))
+    nss.step(p, g, m, wl.table(), h, stream=stream)
+    return p, m
+
+
+def _hyper(nss, wl, method="standard", ns_dtype="bf16"):
+    return nss.hyper(ns_method=method, ns_dtype=ns_dtype, grad_dtype=wl.grad_dtype, lr=wl.lr,
+                     momentum=wl.momentum, weight_decay=wl.weight_decay)
+
+
+def test_release_plans_and_many_tables(lib):
+    import torch
+    nss = lib
+    wl, params, grads, mom = _inputs([(256, 384, 0), (384, 256, 0), (128, 640, 0)], wid=130)
+    h = _hyper(nss, wl)
+    p1, m1 = _step(nss, wl, params, grads, mom, h)
+    torch.cuda.synchronize()
+    nss.release_plans()
+    p2, m2 = _step(nss, wl, params, grads, mom, h)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(m1, m2)
+    # 40 distinct tables (different shapes), then the first again
+    for k in range(40):
+        wk, pk, gk, mk = _inputs([(64 + 8 * k, 96, 0), (32, 40 + 8 * k, 0)], wid=131 + k)
+        _step(nss, wk, pk, gk, mk, _hyper(nss, wk))
+    p3, m3 = _step(nss, wl, params, grads, mom, h)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p3) and torch.equal(m1, m3)
+
+
+@pytest.mark.parametrize("method,ns_dtype,shapes,want", [
+    # one 128-tile group (m >= 129): the separate launches
+    ("standard", "bf16", [(256, 384, 0)],
+     {"momentum_sumsq": 1, "finalize_norm": 1, "prep_x0": 1, "ns_gemm_xxt": 5, "ns_gemm_poly": 5,
+      "ns_gemm_update": 4, "ns_gemm_apply": 1}),
+    # one single-row group (m <= 128, 16-bit): X0 + Gram and update + Gram in one pass each
+    ("standard", "bf16", [(128, 640, 0)],
+     {"momentum_sumsq": 1, "finalize_norm": 1, "prep_gram": 1, "ns_gemm_poly": 5,
+      "ns_update_gram": 4, "ns_gemm_apply": 1}),
+    ("gram", "f16", [(256, 384, 0)],
+     {"momentum_sumsq": 1, "finalize_norm": 1, "prep_x0": 1, "gram_gemm_sym": 14, "gram_gemm_full": 4,
+      "gram_gemm_apply": 1}),
+    ("gram", "f16", [(128, 640, 0)],
+     {"momentum_sumsq": 1, "finalize_norm": 1, "prep_gram": 1, "gram_gemm_sym": 13, "gram_gemm_full": 4,
+      "gram_gemm_apply": 1}),
+])
+def test_profile_counts_the_launch_sequence(lib, method, ns_dtype, shapes, want):
+    import torch
+    nss = lib
+    wl, params, grads, mom = _inputs(shapes, wid=175)
+    h = _hyper(nss, wl, method, ns_dtype)
+    _step(nss, wl, params, grads, mom, h)          # plan built outside the profile
+    torch.cuda.synchronize()
+    nss.profile_begin()
+    _step(nss, wl, params, grads, mom, h)
+    got = nss.profile_end()
+    assert {k: v[0] for k, v in got.items()} == want
+    assert all(ms > 0 for _, ms in got.values())
+
+
+def test_two_threads_two_streams(lib):
+    import torch
+    nss = lib
+    cases = [_inputs([(512, 768, 0), (96, 700, 32)], wid=176), _inputs([(384, 1024, 0), (128, 128, 0)], wid=177)]
+    hs = [_hyper(nss, c[0]) for c in cases]
+    want = []
+    for c, h in zip(cases, hs):
+        p, m = _step(nss, *c, h)
+        torch.cuda.synchronize()
+        want.append((p.cpu(), m.cpu()))
+    for _ in range(3):
+        got = [None, None]
+        errors = []
+
+        def run(k):
+            try:
+                s = torch.cuda.Stream()
+                with torch.cuda.stream(s):
+                    p, m = _step(nss, *cases[k], hs[k], stream=s)
+                s.synchronize()
+                got[k] = (p.cpu(), m.cpu())
+            except Exception as e:          # surfaced in the main thread
+                errors.append(e)
+
+        threads = [threading.Thread(target=run, args=(k,)) for k in range(2)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        assert not errors, errors
+        for k in range(2):
+            assert torch.equal(got[k][0], want[k][0]) and torch.equal(got[k][1], want[k][1]), k
