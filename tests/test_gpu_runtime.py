@@ -7,6 +7,9 @@
   method (which bench.py's per-kernel times rely on).
 - Threads: two host threads stepping different tables on their own streams
   give the same bits as the same steps run one after the other.
+- Graphs: after one call with a table a step is kernel launches only; captured
+  into a HIP graph and replayed (with eager work and synchronisation between
+  replays), every replay equals an eager step from the same state.
 """
 import threading
 
@@ -119,3 +122,40 @@ def test_two_threads_two_streams(lib):
         assert not errors, errors
         for k in range(2):
             assert torch.equal(got[k][0], want[k][0]) and torch.equal(got[k][1], want[k][1]), k
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16"), ("standard", "f32")])
+def test_graph_capture_and_replay(lib, method, ns_dtype):
+    # after one call with a table (which builds its plan), a step is kernel
+    # launches only, so it can be captured into a HIP graph; each replay is one
+    # more step and must equal an eager step from the same state
+    import torch
+    nss = lib
+    gdt = "f32" if ns_dtype == "f32" else "bf16"
+    wl, params, grads, mom = _inputs([(256, 384, 0), (128, 640, 0), (300, 140, 0)], wid=178, grad_dtype=gdt)
+    h = nss.hyper(ns_method=method, ns_dtype=ns_dtype, grad_dtype=gdt, lr=wl.lr, momentum=wl.momentum,
+                  weight_decay=wl.weight_decay)
+    tab = wl.table()
+    dev = "cuda:0"
+    p, g, m = (to_device(a.copy(), dev, torch) for a in (params, grads, mom))
+    pe, ge, me = (to_device(a.copy(), dev, torch) for a in (params, grads, mom))
+    ws = torch.empty(nss.workspace_size(tab, h), dtype=torch.uint8, device=dev)
+    ws_e = torch.empty_like(ws)
+    nss.step(p, g, m, tab, h, ws=ws)              # plan built; first step eager on both copies
+    nss.step(pe, ge, me, tab, h, ws=ws_e)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=s):
+        nss.step(p, g, m, tab, h, ws=ws)
+    torch.cuda.synchronize()
+    for r in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        nss.step(pe, ge, me, tab, h, ws=ws_e)     # the same step, eager
+        torch.cuda.synchronize()
+        assert torch.equal(p, pe) and torch.equal(m, me), r
+        # eager work on the graph's own buffers between replays
+        g.mul_(1.0)
+        torch.cuda.synchronize()
