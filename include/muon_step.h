@@ -33,16 +33,21 @@
  *   - Device pointers are HIP device memory (for example torch CUDA tensors);
  *     host pointers are ordinary memory read during the call and not retained.
  *   - `stream` is a hipStream_t passed as void* (NULL: the default stream). All
- *     device work is enqueued on it asynchronously; nothing synchronises the
- *     host. Faults in device work surface at the caller's next synchronisation.
+ *     device work is enqueued on it asynchronously; apart from the first call
+ *     with a new shape table (below), nothing synchronises the host. Faults in
+ *     device work surface at the caller's next synchronisation.
  *   - Return value: MUON_OK or one of the MUON_ERR_* codes below. Every argument
  *     check runs before the first launch, so a call that fails a check leaves
  *     every buffer unchanged. muon_last_error() gives a message for the last
  *     failing call on the calling thread.
  *   - The caller owns all buffers, including the workspace. The library keeps
  *     one small device array of per-problem descriptors (48 bytes per problem)
- *     for each distinct shape table it has seen, created on the first call with
- *     that table and reused after; muon_release_plans() frees them.
+ *     for each distinct shape table it has seen on a device, created on the
+ *     first call with that table (hipMalloc and a synchronous copy, on the
+ *     current device) and reused after; muon_release_plans() frees them.
+ *   - After that first call, a call with the same table enqueues kernel
+ *     launches only (no allocation, copy or memset), so it may be captured
+ *     into a HIP graph; the profiling hooks below must be off while capturing.
  *   - Calls that share a workspace, or that update the same buffers, must be
  *     ordered by the caller (same stream, or events).
  */
