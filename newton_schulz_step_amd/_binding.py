@@ -92,7 +92,14 @@ _lock = threading.Lock()
 
 
 def load() -> ctypes.CDLL:
-    """Load the built library (raises if it has not been built)."""
+    """Load the built library (raises if it has not been built).
+
+    torch is imported first: torch ships its own HIP runtime under the same
+    soname (libamdhip64.so.7) as the system one the library links against, and
+    the first one loaded serves the whole process. Loaded in this order the
+    library shares torch's runtime (and torch's tensors and streams); loaded
+    the other way round, torch ran on the system runtime and the library's
+    first HIP call failed."""
     global _lib
     with _lock:
         if _lib is not None:
@@ -100,6 +107,7 @@ def load() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing; build it with "
                               "`python -m newton_schulz_step_amd.build`")
+        import torch  # noqa: F401  (see above)
         lib = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         pm = ctypes.POINTER(MuonMatrix)
