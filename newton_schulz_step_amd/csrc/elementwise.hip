@@ -125,30 +125,25 @@ hipError_t launch_finalize_norm(const double* partials, int64_t chunks, int n_pr
 // stored orientation (coalesced) and turned in LDS. Padding rows/columns are
 // written as zeros.
 
+// 4 consecutive elements, rounded to T from materialised fp32 values
 template <typename T>
-__device__ __forceinline__ void store16(T* dst, const float (&v)[16]) {
+__device__ __forceinline__ void store4(T* dst, const float (&v)[4]) {
   if constexpr (sizeof(T) == 4) {
-    f32x4* d = reinterpret_cast<f32x4*>(dst);
+    f32x4 w;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = v[q * 4 + e];
-      d[q] = w;
-    }
+    for (int e = 0; e < 4; ++e) w[e] = v[e];
+    *reinterpret_cast<f32x4*>(dst) = w;
   } else {
-    u16x8 w0, w1;
+    u16x4 w;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      w0[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[e])));
-      w1[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[e + 8])));
-    }
-    u16x8* d = reinterpret_cast<u16x8*>(dst);
-    d[0] = w0;
-    d[1] = w1;
+    for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[e])));
+    *reinterpret_cast<u16x4*>(dst) = w;
   }
 }
 
+// Thread t covers columns 4 (t % 16) .. + 3 of tile rows 16 k + t / 16, k = 0..3:
+// consecutive lanes read consecutive 16-byte pieces of a row, so one wave
+// instruction reads four whole 256-byte rows.
 template <typename T>
 __global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const ProblemDesc* probs, const float* inv_norm,
                                                       int m, int n, int mp, int np, T* X) {
@@ -160,55 +155,53 @@ __global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const Prob
   const int i0 = (t / tiles_j) * 64, j0 = (t % tiles_j) * 64;
   const ProblemDesc pd = probs[p];
   const float inv = inv_norm[p];
-  const int r = threadIdx.x >> 2, c16 = (threadIdx.x & 3) * 16;
-  T* dst = X + p * static_cast<int64_t>(mp) * np + static_cast<int64_t>(i0 + r) * np + j0 + c16;
-  float v[16];
+  const int rr = threadIdx.x >> 4, c4 = (threadIdx.x & 15) * 4;
+  T* Xp = X + p * static_cast<int64_t>(mp) * np;
 
   if (!pd.transposed) {
-    // stored m x n: element (i, j) at src + i * n + j; this thread covers row i0 + r
-    const int gi = i0 + r;
-    const int64_t base = pd.src_off + static_cast<int64_t>(gi) * n + j0 + c16;
-    if (gi < m && j0 + c16 + 16 <= n && (base & 3) == 0) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(M + base);
+    // stored m x n: element (i, j) at src + i * n + j
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 w = src[q];
+    for (int k = 0; k < 4; ++k) {
+      const int gi = i0 + 16 * k + rr, gj = j0 + c4;
+      const int64_t base = pd.src_off + static_cast<int64_t>(gi) * n + gj;
+      float v[4];
+      if (gi < m && gj + 4 <= n && (base & 3) == 0) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(M + base);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[q * 4 + e] = w[e] * inv;
+        for (int e = 0; e < 4; ++e) v[e] = w[e] * inv;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (gi < m && gj + e < n) ? M[base + e] * inv : 0.0f;
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int gj = j0 + c16 + e;
-        v[e] = (gi < m && gj < n) ? M[base + e] * inv : 0.0f;
-      }
+      store4<T>(Xp + static_cast<int64_t>(gi) * np + gj, v);
     }
-    store16<T>(dst, v);
     return;
   }
 
-  // stored n x m: element (i, j) at src + j * m + i; this thread reads stored row j0 + r
-  const int gj = j0 + r;
-  const int64_t base = pd.src_off + static_cast<int64_t>(gj) * m + i0 + c16;
-  if (gj < n && i0 + c16 + 16 <= m && (base & 3) == 0) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(M + base);
+  // stored n x m: element (i, j) at src + j * m + i; stored row j0 + 16 k + rr holds
+  // canonical column j, and its columns i0 + c4 .. + 3 canonical rows
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 w = src[q];
+  for (int k = 0; k < 4; ++k) {
+    const int sj = j0 + 16 * k + rr, si = i0 + c4;
+    const int64_t base = pd.src_off + static_cast<int64_t>(sj) * m + si;
+    if (sj < n && si + 4 <= m && (base & 3) == 0) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(M + base);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tile[c16 + q * 4 + e][r] = w[e];
-    }
-  } else {
+      for (int e = 0; e < 4; ++e) tile[c4 + e][16 * k + rr] = w[e];
+    } else {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int gi = i0 + c16 + e;
-      tile[c16 + e][r] = (gj < n && gi < m) ? M[base + e] : 0.0f;
+      for (int e = 0; e < 4; ++e) tile[c4 + e][16 * k + rr] = (sj < n && si + e < m) ? M[base + e] : 0.0f;
     }
   }
   __syncthreads();   // the transposed flag is the same for the whole block
 #pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = tile[r][c16 + e] * inv;
-  store16<T>(dst, v);
+  for (int k = 0; k < 4; ++k) {
+    const int r = 16 * k + rr;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = tile[r][c4 + e] * inv;
+    store4<T>(Xp + static_cast<int64_t>(i0 + r) * np + j0 + c4, v);
+  }
 }
 
 hipError_t launch_prep_x0(int ns_dtype, const float* M, const ProblemDesc* probs, const float* inv_norm,
