@@ -25,6 +25,10 @@ Readings where the pages leave a step open (each also listed in the design notes
   * X0 = Y / (||Y||_F + eps), eps = 1e-7; Y is transposed first when it has more
     rows than columns, and the result is transposed back.
   * Momentum: heavy ball, M <- mu M + G, no Nesterov term, no dampening.
+    Parity unpinned: nothing on the pages tells this form from Nesterov. The
+    function is pinned to the reading by the constant-gradient closed form, and
+    one-step results do not depend on the choice (normalisation cancels M = G's
+    scale).
   * Gram recurrence: R0 = X0 X0^T; per step Q = a I + b R + c R R; P <- Q P
     (P = Q on the first step); R <- Q (R Q) except after the last step; the
     result is P X0. In exact arithmetic this equals the standard iteration,
@@ -86,7 +90,8 @@ def _symmetric(store: Store) -> Store:
 
 
 def momentum_update(M: np.ndarray, G: np.ndarray, mu: float) -> np.ndarray:
-    """[DS] 什么是 Muon 优化器？: momentum is formed from the gradient first."""
+    """[DS] 什么是 Muon 优化器？: momentum is formed from the gradient first.
+    Heavy-ball form (a reading; parity unpinned against the pages)."""
     return mu * M + G
 
 
