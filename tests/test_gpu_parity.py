@@ -482,3 +482,64 @@ def test_adamw_first_step_closed_form(lib):
     assert np.array_equal(out[:17], p0[:17] * decay)            # zero gradient: decay only
     expect = p0.astype(np.float64) * (1 - 3e-5) - 3e-4 * g / (np.abs(g) + 1e-8)
     assert np.max(np.abs(out - expect)) < 4e-7
+
+
+# --------------------------------------------------------------------------- rank one: closed form
+
+# quintic coefficients and step count of the DeepSpeed-Muon article's Newton-Schulz
+# section (the library's defaults)
+_QA, _QB, _QC, _QSTEPS = 3.4445, -4.7750, 2.0315, 5
+
+
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_rank_one_closed_form(lib, method):
+    # G = u v^T with integer vectors (every product exact in fp32, so G is exactly
+    # rank one): X0 has the one singular value s0 = ||G|| / (||G|| + eps), both
+    # iterations map it by the scalar quintic, and O = p^5(s0) u v^T / (|u| |v|).
+    # That closed form owes nothing to the oracle (which meets it to ~1e-12).
+    # - The signal component u^T O v must equal p^5(s0) within the fp32 gate for
+    #   the standard iteration (a wrong coefficient, step count or sign moves it
+    #   far more). The Gram iteration works on R = X X^T, whose null-space noise
+    #   grows by about a^2 per step and reaches the signal at second order: 1e-3.
+    # - The rest of O lies in the null space of G. There the fp32 accumulation
+    #   error of each product (about sqrt(K) 2^-24 relative, K <= 700) is
+    #   amplified by up to p'(0) = a per later step, and three products per step
+    #   each add it: at most about 3 * 1.6e-6 * (1 + a + ... + a^5) ~ 3e-3. (In
+    #   16-bit storage this noise is of order one, so the low-precision iterations
+    #   are gated against the storage-faithful oracle instead.)
+    shapes = [(300, 520), (700, 130), (128, 640), (1, 37), (520, 520)]
+    rng = np.random.default_rng(4242)
+    offs, cur = [], 0
+    for r, c in shapes:
+        offs.append(cur)
+        cur = (cur + r * c + 63) // 64 * 64
+    n = cur
+    grads = np.zeros(n, dtype=np.float32)
+    uv = []
+    for (r, c), o in zip(shapes, offs):
+        u = rng.integers(-64, 65, r).astype(np.float64)
+        v = rng.integers(-64, 65, c).astype(np.float64)
+        u[0], v[0] = 64.0, 64.0                          # never all zero
+        G = np.outer(u, v)
+        assert np.array_equal(G.astype(np.float32).astype(np.float64), G)
+        grads[o:o + r * c] = G.astype(np.float32).ravel()
+        uv.append((u / np.linalg.norm(u), v / np.linalg.norm(v), np.linalg.norm(G)))
+    params = rng.standard_normal(n).astype(np.float32)
+    mom = np.zeros(n, dtype=np.float32)
+    tab = [(o, r, c, 0) for o, (r, c) in zip(offs, shapes)]
+    print(f"[case] rank one {method} f32: {tab}", flush=True)
+    h = lib.hyper(ns_method=method, ns_dtype="f32", grad_dtype="f32", lr=0.02, momentum=0.95,
+                  weight_decay=0.1)
+    gpu = run_step(lib, params, grads, mom, tab, h)
+    bad = []
+    for (o, (r, c)), (u, v, gn) in zip(zip(offs, shapes), uv):
+        s = gn / (gn + 1e-7)
+        for _ in range(_QSTEPS):
+            s = _QA * s + _QB * s ** 3 + _QC * s ** 5
+        O = gpu["update"][o:o + r * c].astype(np.float64).reshape(r, c)
+        sig = float(u @ O @ v)
+        err = rel(O.ravel(), (s * np.outer(u, v)).ravel())
+        print(f"  {r}x{c}: p^5(s0) {s:.6f} u^T O v {sig:.6f} whole-update err {err:.2e}")
+        if abs(sig - s) > (FP32_GATE if method == "standard" else 1e-3) * s or err > 3e-3:
+            bad.append((r, c, sig, s, err))
+    assert not bad, bad
