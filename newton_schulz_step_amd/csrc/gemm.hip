@@ -829,7 +829,7 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
   auto tile = [&](u16x8 (&r)[8], int jt) {
     xwrite(r);
     __syncthreads();                       // X tile (and, first time, B) in LDS; last Gram reads done
-    if (jt + 2 < NT) xload(r, jt + 2);
+    if (jt + 3 < NT) xload(r, jt + 3);     // three tiles in flight (two: 0.5% slower steps)
 
     // X'_tile = B X_tile over K = 128 (two slices, four sub-steps each)
 #pragma unroll
@@ -913,12 +913,14 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
       }
   };
 
-  u16x8 r0[8], r1[8];
+  u16x8 r0[8], r1[8], r2[8];
   xload(r0, 0);
   if (NT > 1) xload(r1, 1);
-  for (int jt = 0; jt < NT; jt += 2) {
+  if (NT > 2) xload(r2, 2);
+  for (int jt = 0; jt < NT; jt += 3) {
     tile(r0, jt);
     if (jt + 1 < NT) tile(r1, jt + 1);
+    if (jt + 2 < NT) tile(r2, jt + 2);
   }
 
   // A' stored symmetric (lower triangle, mirrored), as the X X^T launch stores it
