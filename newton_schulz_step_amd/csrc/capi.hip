@@ -122,8 +122,16 @@ static std::string plan_key(int device, const muon_matrix_t* t, const muon_windo
   return k;
 }
 
+// The workspace size is checked here, on a cached plan or right after the host
+// layout of a new one, so a call with too small a workspace allocates and copies
+// nothing.
+static int workspace_fits(const Plan& p, size_t have) {
+  if (have >= p.L.ws_bytes) return MUON_OK;
+  return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(p.L.ws_bytes) + " bytes");
+}
+
 static int get_plan(const muon_matrix_t* t, const muon_window_t* w, int32_t n, const muon_hyper_t* h,
-                    std::shared_ptr<Plan>& out) {
+                    size_t workspace_bytes, std::shared_ptr<Plan>& out) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
   const std::string key = plan_key(device, t, w, n, h);
@@ -131,12 +139,14 @@ static int get_plan(const muon_matrix_t* t, const muon_window_t* w, int32_t n, c
   auto it = g_plans.find(key);
   if (it != g_plans.end()) {
     out = it->second;
-    return MUON_OK;
+    return workspace_fits(*out, workspace_bytes);
   }
-  if (g_plans.size() >= kMaxPlans) g_plans.clear();
   std::shared_ptr<Plan> p = std::make_shared<Plan>();
   p->device = device;
   p->L = build_layout(t, n, h, w);
+  const int st = workspace_fits(*p, workspace_bytes);
+  if (st != MUON_OK) return st;
+  if (g_plans.size() >= kMaxPlans) g_plans.clear();
   p->sets = group_sets(p->L);
   std::vector<ProblemDesc> probs(p->L.problems.size());
   for (size_t i = 0; i < probs.size(); ++i) {
@@ -150,7 +160,7 @@ static int get_plan(const muon_matrix_t* t, const muon_window_t* w, int32_t n, c
   }
   if (!probs.empty() &&
       hipMemcpy(p->d_problems, probs.data(), probs.size() * sizeof(ProblemDesc), hipMemcpyHostToDevice) != hipSuccess)
-    return fail(MUON_ERR_HIP, "copying the problem descriptors failed");
+    return fail(MUON_ERR_HIP, "copying the problem descriptors failed");   // p's destructor frees them
   out = p;
   g_plans[key] = std::move(p);
   return MUON_OK;
@@ -561,11 +571,9 @@ static int step_impl(float* params, int64_t params_numel, const void* grads, flo
   if (overlapping(spans, which)) return fail(MUON_ERR_OVERLAP, "buffers overlap: " + which);
 
   std::shared_ptr<Plan> plan;
-  st = get_plan(table, windows, n_entries, h, plan);
+  st = get_plan(table, windows, n_entries, h, workspace_bytes, plan);
   if (st != MUON_OK) return st;
   const Plan* P = plan.get();
-  if (workspace_bytes < P->L.ws_bytes)
-    return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(P->L.ws_bytes) + " bytes");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);

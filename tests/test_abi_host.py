@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import newton_schulz_step_amd as nss
@@ -201,3 +202,49 @@ def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _binding.load()
+
+
+def test_random_tables_get_the_status_of_their_one_violation(lib):
+    # Seeded random tables: 1-6 entries of random shapes (some split into row
+    # blocks), at 8-aligned offsets with gaps of at least 8 elements. Each table
+    # gets at most one violation, and the returned status must be exactly that
+    # violation's code; an untouched table must pass. Only rejected tables reach
+    # muon_step (with fake pointers: every check runs before the first device
+    # call); valid ones go through the host-only muon_workspace_size.
+    rng = np.random.default_rng(77)
+    h = nss.hyper(ns_method="standard", ns_dtype="bf16")
+    kinds = ["none", "zero_rows", "bad_split", "misaligned", "duplicate", "short", "negative"]
+    want = {"none": nss.OK, "zero_rows": nss.ERR_BAD_SHAPE, "bad_split": nss.ERR_BAD_SHAPE,
+            "misaligned": nss.ERR_ALIGN, "duplicate": nss.ERR_OVERLAP, "short": nss.ERR_RANGE,
+            "negative": nss.ERR_RANGE}
+    for case in range(600):
+        ents, cur = [], 0
+        for _ in range(int(rng.integers(1, 7))):
+            r, c = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+            divs = [d for d in range(1, r + 1) if r % d == 0]
+            split = int(rng.choice(divs)) if rng.random() < 0.3 else 0
+            cur += 8 * int(rng.integers(1, 4))
+            ents.append([cur, r, c, split])
+            cur = (cur + r * c + 7) // 8 * 8
+        numel = cur + 8 * int(rng.integers(1, 4))
+        kind = kinds[case % len(kinds)]
+        k = int(rng.integers(len(ents)))
+        if kind == "zero_rows":
+            ents[k][1], ents[k][3] = 0, 0
+        elif kind == "bad_split":
+            ents[k][3] = ents[k][1] + 1
+        elif kind == "misaligned":
+            ents[k][0] += 4
+        elif kind == "duplicate":
+            ents.append(list(ents[k]))
+        elif kind == "short":
+            numel = ents[-1][0] + ents[-1][1] * ents[-1][2] - 1
+        elif kind == "negative":
+            ents[0][0] = -8
+        table = [tuple(e) for e in ents]
+        if kind != "short":          # the table alone decides
+            st, msg = _status(lambda: nss.workspace_size(table, h))
+            assert st == want[kind], (case, kind, ents, st, msg)
+        if kind != "none":           # never a valid table with fake pointers
+            st, msg = _raw_step(lib, table, numel, h)
+            assert st == want[kind], (case, kind, ents, numel, st, msg)

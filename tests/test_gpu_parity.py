@@ -393,8 +393,18 @@ def test_empty_table_and_small_workspace(lib):
     with pytest.raises(lib.MuonError) as ei:
         lib.step(p, g, m, tab, h, ws=ws)
     assert ei.value.status == lib.ERR_WORKSPACE
+    # a table no earlier call has used: the size is checked on its fresh host
+    # layout, before its plan is uploaded; a later call with room then runs
+    tab2 = [(0, 40, 88, 0), (3584, 8, 8, 0)]
+    need2 = lib.workspace_size(tab2, h)
+    with pytest.raises(lib.MuonError) as ei:
+        lib.step(p, g, m, tab2, h, ws=torch.empty(need2 - 256, dtype=torch.uint8, device=dev))
+    assert ei.value.status == lib.ERR_WORKSPACE
     torch.cuda.synchronize()
     assert torch.equal(p, p0) and not torch.any(m)
+    lib.step(p, g, m, tab2, h, ws=torch.empty(need2, dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+    assert not torch.equal(p[:3520], p0[:3520]) and torch.equal(p[3520:3584], p0[3520:3584])
 
 
 # --------------------------------------------------------------------------- pack / unpack
