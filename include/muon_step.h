@@ -44,7 +44,9 @@
  *     one small device array of per-problem descriptors (48 bytes per problem)
  *     for each distinct shape table it has seen on a device, created on the
  *     first call with that table (hipMalloc and a synchronous copy, on the
- *     current device) and reused after; muon_release_plans() frees them.
+ *     current device) and reused after; muon_release_plans() frees them. The
+ *     cache holds up to 1024 tables: the first call with one more clears it,
+ *     which synchronises the device.
  *   - After that first call, a call with the same table enqueues kernel
  *     launches only (no allocation, copy or memset), so it may be captured
  *     into a HIP graph; the profiling hooks below must be off while capturing.
