@@ -81,8 +81,15 @@ def device_inputs(wl, dev, seed=0):
 
 
 def gemm_source_hash() -> str:
+    """SHA-256 prefix of what decides the GEMM kernels' code: gemm.hip and the
+    flags it is compiled with (include paths, which differ between machines,
+    left out)."""
+    from newton_schulz_step_amd import build as B
     src = os.path.join(ROOT, "newton_schulz_step_amd", "csrc", "gemm.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256(open(src, "rb").read())
+    flags = [f for f in B.FLAGS + B.EXTRA.get("gemm.hip", []) if not f.startswith("-I")]
+    h.update(" ".join(flags).encode())
+    return h.hexdigest()[:16]
 
 
 WORKLOAD_SLUG = {1: "tiny_fp32", 2: "one_layer", 3: "owner_share_7b", 4: "moe_experts",

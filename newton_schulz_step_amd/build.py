@@ -30,6 +30,9 @@ FLAGS = [
 ]
 # per-kernel resource remarks of the device compile, checked below
 REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+# per-source extras: the GEMMs' instruction scheduler maximises ILP (whole steps
+# 0.8-1.4% faster than the default strategy, bit-identical)
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _scratch_users(stderr: str):
@@ -49,7 +52,8 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     hip = src.endswith(".hip")
     lang = ["-x", "hip"] if hip else []
-    cmd = [HIPCC, *FLAGS, *lang, *(REMARKS if hip else []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, *(REMARKS if hip else []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
