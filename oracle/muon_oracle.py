@@ -45,14 +45,16 @@ Storage-faithful mode: the article runs the standard iteration in bf16 and the
 Gram iteration in fp16. `store` rounds (once, to nearest even, from float64) at
 each point where such an implementation stores a matrix; the arithmetic between
 those points stays float64. Standard: X0, A, B and X1..X4 are stored; X5 is not.
-Gram: X0, R0, every Q, P and R, and the intermediate R Q are stored; P X0 is not.
-The Gram state may carry an exact power-of-two scale s (R is kept as s X X^T, and
-b, c become b/s, c/s^2); with s = 1 this is the plain recurrence.
-A, B, R, Q and R Q are symmetric by definition (A = X X^T and R = X X^T, the
-article's Gram matrix, B and Q are polynomials in them, and R Q is a product of
-two commuting polynomials in R), so a stored one is a symmetric matrix: its lower
-triangle (row index >= column index) is rounded and mirrored. P is stored as
-computed.
+Gram: X0, R0, every Q, P and R, and the intermediate T = R Q are stored; P X0 is
+not. The Gram state may carry an exact power-of-two scale s (R is kept as
+s X X^T, and b, c become b/s, c/s^2); with s = 1 this is the plain recurrence.
+A product is stored as a symmetric matrix (its lower triangle, row index >=
+column index, rounded and mirrored) only where its stored operands make it
+exactly symmetric under any fixed-order evaluation: A = X X^T and R0 = X0 X0^T
+(entry (i, j) and (j, i) add the same products in the same order), and B and
+the first Q, polynomials in such a matrix. Everything else is stored as
+computed: T = R Q and R <- Q T (after rounding, Q no longer commutes with R, so
+neither product is symmetric), every later Q (a polynomial in such an R), and P.
 The exact mode evaluates the products as they are.
 """
 from __future__ import annotations
@@ -82,8 +84,9 @@ def _ident(z):
 
 
 def _symmetric(store: Store) -> Store:
-    """Store a matrix that is symmetric by definition: lower triangle, mirrored
-    (storage-faithful mode only; the exact mode keeps the product as computed)."""
+    """Store a product that any fixed-order evaluation leaves exactly symmetric:
+    lower triangle, mirrored (storage-faithful mode only; the exact mode keeps
+    the product as computed)."""
     if store is _ident:
         return store
     return lambda z: store(np.tril(z) + np.tril(z, -1).T)
@@ -130,11 +133,12 @@ def newton_schulz_gram(X0: np.ndarray, steps: int = NS_STEPS,
     bs, cs = b / scale, c / (scale * scale)
     P = None
     for k in range(steps):
-        Q = sym(a * eye + bs * R + cs * (R @ R))
+        # symmetric only while R is: R0, stored symmetric; later R as computed
+        Q = (sym if k == 0 else store)(a * eye + bs * R + cs * (R @ R))
         P = Q if k == 0 else store(Q @ P)
         if k < steps - 1:
-            RQ = sym(R @ Q)
-            R = sym(Q @ RQ)
+            T = store(R @ Q)
+            R = store(Q @ T)
     return P @ X
 
 

@@ -290,26 +290,87 @@ def test_faithful_row_scaled_hadamard_is_per_row_scalars(fmt):
     assert np.array_equal(O, (p * x0)[:, None] * H)
 
 
-def test_faithful_symmetric_iterates_are_stored_symmetric():
-    """A, B (standard) and R, Q, R Q (gram) are symmetric by definition; the
-    faithful mode stores them as symmetric matrices (lower triangle mirrored),
-    and P as computed. Checked through a storer that records what it is given."""
-    rng = np.random.default_rng(21)
-    X0 = rng.standard_normal((6, 10)) / 8
-    seen = []
+def _fixed_order_matmul(A, B):
+    """A B with every entry summed over k = 0, 1, ... in that order (one rounding
+    per product and per addition). Entry (i, j) of X X^T and entry (j, i) then add
+    the same products in the same order, so the result is exactly symmetric."""
+    C = np.zeros((A.shape[0], B.shape[1]))
+    for k in range(A.shape[1]):
+        C = C + np.outer(A[:, k], B[k, :])
+    return C
+
+
+def _recording_storer(fmt, seen):
     def rec(z):
-        z = rounding.round_to(z, "f16")
+        z = rounding.round_to(z, fmt)
         seen.append(z)
         return z
-    oracle.newton_schulz_gram(X0, 5, store=rec)
+    return rec
+
+
+def test_faithful_symmetric_storage_is_a_fixed_order_evaluation():
+    """The faithful mode stores A, B (standard) and R0 and the first Q (gram) as
+    mirrored lower triangles. That is no approximation: a fixed-order evaluation
+    of each, from the stored operands, gives the same bits (and is symmetric)."""
+    rng = np.random.default_rng(21)
+    X0 = rng.standard_normal((6, 10)) / 8
+    a, b, c = 3.4445, -4.7750, 2.0315
+    rnd = lambda z: rounding.round_to(z, "f16")
+    # standard: X0, then A, B, X1, A, B, ...
+    seen = []
+    oracle.newton_schulz_standard(X0, 5, store=_recording_storer("f16", seen))
+    X = seen[0]
+    for k in range(5):
+        A, B = seen[1 + 3 * k], seen[2 + 3 * k]
+        A_fo = _fixed_order_matmul(X, X.T)
+        assert np.array_equal(A_fo, A_fo.T)
+        assert np.array_equal(A, rnd(A_fo)), k
+        B_fo = b * A + c * _fixed_order_matmul(A, A)
+        assert np.array_equal(B_fo, B_fo.T)
+        assert np.array_equal(B, rnd(B_fo)), k
+        if k < 4:
+            X = seen[3 + 3 * k]
+    # gram: X0, R0, Q0, then T0, R1, Q1, P1, ...
+    seen = []
+    s = 8.0
+    oracle.newton_schulz_gram(X0, 5, store=_recording_storer("f16", seen), scale=s)
+    X, R0, Q0 = seen[0], seen[1], seen[2]
+    R0_fo = s * _fixed_order_matmul(X, X.T)
+    assert np.array_equal(R0, rnd(R0_fo)) and np.array_equal(R0_fo, R0_fo.T)
+    Q0_fo = a * np.eye(6) + (b / s) * R0 + (c / s ** 2) * _fixed_order_matmul(R0, R0)
+    assert np.array_equal(Q0, rnd(Q0_fo)) and np.array_equal(Q0_fo, Q0_fo.T)
+
+
+def test_faithful_gram_stores_later_iterates_as_computed():
+    """Once Q is rounded it no longer commutes with R, so T = R Q and R <- Q T are
+    not symmetric; the faithful mode stores them (and every later Q, a
+    polynomial in such an R) as computed, like P."""
+    rng = np.random.default_rng(22)
+    X0 = rng.standard_normal((6, 10)) / 8
+    seen = []
+    oracle.newton_schulz_gram(X0, 5, store=_recording_storer("f16", seen), scale=8.0)
     sq = [z for z in seen if z.shape == (6, 6)]
-    # R0; step 0 stores Q, R Q, R; steps 1-3 store Q, P, R Q, R; step 4 stores Q, P
-    assert len(sq) == 1 + 3 + 3 * 4 + 2
-    p_idx = [5, 9, 13, 17]
-    for i in range(len(sq)):
-        if i not in p_idx:
-            assert np.array_equal(sq[i], sq[i].T), i
-    assert not np.array_equal(sq[5], sq[5].T)          # P as computed is not exactly symmetric
+    # R0, Q0; step 0: T, R; steps 1-3: Q, P, T, R; step 4: Q, P
+    assert len(sq) == 2 + 2 + 3 * 4 + 2
+    R0, Q0, T0, R1, Q1, P1 = sq[:6]
+    assert np.array_equal(R0, R0.T) and np.array_equal(Q0, Q0.T)
+    for z in (T0, R1, Q1, P1):
+        assert not np.array_equal(z, z.T)
+    rnd = lambda z: rounding.round_to(z, "f16")
+    assert np.array_equal(T0, rnd(R0 @ Q0))
+    assert np.array_equal(R1, rnd(Q0 @ T0))
+    assert np.array_equal(P1, rnd(Q1 @ Q0))            # P starts as Q0
+
+
+def test_gram_scale_at_the_workload_shapes():
+    """2^ceil(log2 m), capped at 2^15: values worked out by hand for the short
+    sides of the workloads (head blocks 128, experts 1408, layers 2048 / 4096,
+    the long MLP side 5632 and 11008), the size limit and beyond the cap."""
+    table = {1: 1, 2: 2, 3: 4, 5: 8, 100: 128, 128: 128, 129: 256, 1000: 1024, 1408: 2048,
+             2047: 2048, 2048: 2048, 2049: 4096, 4096: 4096, 5632: 8192, 11008: 16384,
+             16384: 16384, 16385: 32768, 32768: 32768, 40000: 32768, 1 << 20: 32768}
+    for m, s in table.items():
+        assert oracle.gram_scale(m) == float(s), m
 
 
 def test_faithful_first_storage_point_is_x0():
