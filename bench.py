@@ -193,6 +193,17 @@ def summarize_mfma(csv_path, symbol):
             "gui_active_cycles": gui, "mfma_busy_fraction": frac}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, method, budget_s=25.0):
     """The float64 oracle (as it stands) on one matrix per shape group, in table
     order, while the budget lasts; the untimed groups and the other matrices of
@@ -200,11 +211,17 @@ def cpu_baseline(wl, method, budget_s=25.0):
     import numpy as np
     import oracle
     import workloads as W
+    cores, blas = os.cpu_count(), "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 0) for d in threadpool_info()] or [os.cpu_count()])
+        pools = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if pools:
+            cores = max(d.get("num_threads", 0) for d in pools)
+            blas = "; ".join(f"{d.get('internal_api')} {d.get('version')} "
+                             f"({d.get('threading_layer', '?')} threads, {d.get('architecture', '?')})"
+                             for d in pools)
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        pass
     groups = {}
     for i, e in enumerate(wl.entries):
         pr = e.split_rows or e.rows
@@ -229,7 +246,7 @@ def cpu_baseline(wl, method, budget_s=25.0):
     total_flops = sum(ns_flops(m, n, method) for m, n in problems(wl))
     est_step_s = timed_s * total_flops / timed_flops
     return {"value": wl.muon_elements / est_step_s, "unit": "elements/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "blas": blas,
             "sample": (f"float64 exact-mode oracle, {method} NS, one matrix per shape group "
                        f"({', '.join(names)}) timed {timed_s:.1f} s; whole step extrapolated "
                        f"by nominal NS FLOPs to {est_step_s:.1f} s")}

@@ -5,10 +5,15 @@ entries that the CPU oracle computes one by one.
 The sampled entries get their seeded host values; every other entry is filled
 on the device with Gaussian values of the same scale (problems are independent,
 so this does not change what the sampled ones must produce). Gates as in
-test_gpu_parity: bf16 / fp16 iterations within 3e-2 of the storage-faithful
-oracle, and within 3e-2 of the exact oracle on the top-16 signal subspace;
-momentum within 1e-6; untouched sampled neighbours' bytes are not checked here
-(test_gpu_parity covers them).
+test_gpu_parity:
+  - standard bf16: within 3e-2 of the storage-faithful oracle;
+  - gram fp16 (low-rank inputs): no further from the exact update than
+    max(1.25 x the storage-faithful evaluation's own distance, 3e-2); its
+    distance from the storage-faithful oracle is printed, not gated;
+  - both: the top-16 signal subspace within 3e-2 of the exact oracle, the
+    weight change within 1e-4 of p (1 - lr wd) - lr O recomputed from the GPU's
+    own O, momentum within 1e-6.
+Untouched neighbours' bytes are not checked here (test_gpu_parity covers them).
 """
 import time
 
@@ -81,17 +86,26 @@ def _run(nss, wid, method, ns_dtype, sample):
         Oe = exact["update"].reshape(e.rows, e.cols)
         Me = exact["momentum"].reshape(e.rows, e.cols)
         eo = rel(O, Of)
+        ex_o = rel(O, Oe)
+        own = rel(Of, Oe)
         em = rel(M, Me)
         dp = rel(P - p0, ref["params"].reshape(e.rows, e.cols) - p0)
+        decay = np.float64(np.float32(1.0 - np.float64(np.float32(wl.lr)) * np.float64(np.float32(wl.weight_decay))))
+        p0d = p0.astype(np.float64)
+        ea = rel(P - p0d, p0d * decay - np.float64(np.float32(wl.lr)) * O - p0d)
         worst_sub = 0.0
         for r0, nr in _blocks(e):
             Mb, Ob, Oeb = Me[r0:r0 + nr], O[r0:r0 + nr], Oe[r0:r0 + nr]
             if nr > e.cols:
                 Mb, Ob, Oeb = Mb.T, Ob.T, Oeb.T
             worst_sub = max(worst_sub, top_subspace_err(Ob, Oeb, Mb))
-        print(f"  entry {i}: O vs faithful {eo:.2e}, O vs exact {rel(O, Oe):.2e}, "
-              f"top-16 {worst_sub:.2e}, M {em:.2e}, dp {dp:.2e}", flush=True)
-        assert eo <= LP_GATE and dp <= LP_GATE and em <= MOM_GATE
+        print(f"  entry {i}: O vs faithful {eo:.2e}, O vs exact {ex_o:.2e} (faithful vs exact "
+              f"{own:.2e}), top-16 {worst_sub:.2e}, M {em:.2e}, dp {dp:.2e}, apply {ea:.2e}", flush=True)
+        assert em <= MOM_GATE and ea <= 1e-4
+        if method == "gram":
+            assert ex_o <= max(1.25 * own, LP_GATE)
+        else:
+            assert eo <= LP_GATE and dp <= LP_GATE
         assert worst_sub <= LP_GATE
     del params, grads, mom, upd
     torch.cuda.empty_cache()
@@ -104,7 +118,9 @@ def test_one_layer(lib, method, ns_dtype):
 
 @pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
 def test_owner_share_7b(lib, method, ns_dtype):
-    _run(lib, 3, method, ns_dtype, sample=[5])
+    # one 4096 x 4096 matrix and both rectangular shapes: 11008 x 4096 (stored
+    # transposed) and 4096 x 11008, the group with most of the step's work
+    _run(lib, 3, method, ns_dtype, sample=[5, 16, 24])
 
 
 @pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
