@@ -27,29 +27,30 @@
  *                 X <- a X + B X; gram: R = X0 X0^T, Q = a I + b R + c R R,
  *                 P <- Q P, R <- Q R Q, X = P X0)
  *   O  = X, transposed back
- *   p <- p * (1 - lr * weight_decay) - lr * O      (fp32 params, in place)
+ *   p <- p * (1 - lr * weight_decay) - lr * O      (params, in place)
  *
  * Conventions for every entry point:
  *   - Device pointers are HIP device memory (for example torch CUDA tensors);
  *     host pointers are ordinary memory read during the call and not retained.
  *   - `stream` is a hipStream_t passed as void* (NULL: the default stream). All
- *     device work is enqueued on it asynchronously; apart from the first call
- *     with a new shape table (below), nothing synchronises the host. Faults in
- *     device work surface at the caller's next synchronisation.
+ *     device work is enqueued on it asynchronously. No call allocates device
+ *     memory, copies between host and device, or synchronises the host or the
+ *     device (the profiling hooks below aside): a step's per-problem
+ *     descriptors are written into the caller's workspace by a kernel on the
+ *     stream, from the table passed as kernel arguments. Faults in device work
+ *     surface at the caller's next synchronisation.
  *   - Return value: MUON_OK or one of the MUON_ERR_* codes below. Every argument
  *     check runs before the first launch, so a call that fails a check leaves
  *     every buffer unchanged. muon_last_error() gives a message for the last
  *     failing call on the calling thread.
- *   - The caller owns all buffers, including the workspace. The library keeps
- *     one small device array of per-problem descriptors (48 bytes per problem)
- *     for each distinct shape table it has seen on a device, created on the
- *     first call with that table (hipMalloc and a synchronous copy, on the
- *     current device) and reused after; muon_release_plans() frees them. The
- *     cache holds up to 1024 tables: the first call with one more clears it,
- *     which synchronises the device.
- *   - After that first call, a call with the same table enqueues kernel
- *     launches only (no allocation, copy or memset), so it may be captured
- *     into a HIP graph; the profiling hooks below must be off while capturing.
+ *   - The caller owns all device memory, including the workspace. The library
+ *     keeps only host memory: the layout it derives from each distinct table
+ *     (up to 1024 of them; the first call with one more drops them all,
+ *     muon_release_plans() drops them on request).
+ *   - Every call enqueues kernel launches only, so any call may be captured
+ *     into a HIP graph (the profiling hooks below must be off while
+ *     capturing). A replay reads the workspace given at capture time, which
+ *     must then stay allocated and unused by other work.
  *   - Calls that share a workspace, or that update the same buffers, must be
  *     ordered by the caller (same stream, or events).
  */
@@ -76,7 +77,8 @@ enum {
   MUON_ERR_ALIGN = 6,       /* an offset not a multiple of 8 elements, or a buffer
                                pointer not 16-byte aligned */
   MUON_ERR_UNSUPPORTED = 7, /* a dtype combination that is not implemented (gram
-                               with bf16 storage, params other than fp32, ...) */
+                               with bf16 storage, bf16 params with a bf16 shadow or
+                               in a partition holder's step, ...) */
   MUON_ERR_WORKSPACE = 8,   /* workspace smaller than muon_workspace_size() */
   MUON_ERR_HIP = 9,         /* a HIP runtime call or kernel launch failed */
   MUON_ERR_BAD_HYPER = 10   /* a non-finite hyperparameter, ns_steps outside
@@ -125,7 +127,9 @@ typedef struct {
   int32_t ns_steps;    /* default 5 */
   float ns_eps;        /* default 1e-7: X0 = Y / (||Y||_F + ns_eps) */
   int32_t ns_method;   /* MUON_NS_STANDARD | MUON_NS_GRAM; default GRAM */
-  int32_t param_dtype; /* MUON_DTYPE_F32 (the only one implemented) */
+  int32_t param_dtype; /* MUON_DTYPE_F32 (default: fp32 master weights) | BF16 (bf16
+                          weights updated in place: p <- RNE_bf16(p * (1 - lr * wd)
+                          - lr * O), computed in fp32) */
   int32_t grad_dtype;  /* MUON_DTYPE_BF16 (default) | F32 | F16 */
   int32_t ns_dtype;    /* storage/operand type of the iteration: standard F32 | BF16 |
                           F16; gram F32 | F16. Default F16 (the default method is
@@ -150,12 +154,15 @@ void muon_default_adamw_hyper(muon_adamw_hyper_t* h);
 
 /* Bytes of device workspace that muon_step needs for this table and these
  * hyperparameters (validates the table like muon_step, without the buffer and
- * range checks). Host-only; no device work. */
+ * range checks). Host-only; no device work. The workspace holds the
+ * per-problem descriptors (48 bytes per problem), the per-problem norms and
+ * the tile-padded iterates of every shape group. */
 int muon_workspace_size(const muon_matrix_t* table, int32_t n_entries,
                         const muon_hyper_t* h, size_t* bytes_out);
 
 /* One Muon step over the packed buffers.
- *   params      device, float32[numel], updated in place (entries only).
+ *   params      device, param_dtype[numel] (float32, or bf16 as raw 16-bit
+ *               words), updated in place (entries only).
  *   grads       device, grad_dtype[numel], read only.
  *   momentum    device, float32[numel], updated in place (entries only).
  *   numel       element count of each packed buffer.
@@ -167,7 +174,8 @@ int muon_workspace_size(const muon_matrix_t* table, int32_t n_entries,
  *   update_out  optional device float32[numel]: receives O (entries only).
  *   bf16_shadow optional device bf16[numel] (raw 16-bit words): receives the
  *               round-to-nearest-even bf16 copy of the new params (entries only),
- *               the form an owner broadcasts.
+ *               the form an owner broadcasts. fp32 params only (bf16 params are
+ *               that copy themselves: MUON_ERR_UNSUPPORTED).
  * Elements outside the entries are never written in any output. */
 int muon_step(void* params, const void* grads, float* momentum, int64_t numel,
               const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h,
@@ -195,7 +203,8 @@ typedef struct {
  * the holders' windows together equal a muon_step of the whole matrix, bit
  * for bit.
  *   partition       device float32[partition_numel], updated in place
- *                   (window elements only).
+ *                   (window elements only); h->param_dtype must be F32
+ *                   (MUON_ERR_UNSUPPORTED otherwise).
  *   grads, momentum, numel, table, h, workspace: as in muon_step (the table
  *                   describes the full-matrix layout of grads and momentum;
  *                   momentum is updated for every listed matrix in full).
@@ -318,7 +327,8 @@ double muon_comm_elements(int64_t p_m, int32_t n_ranks, int32_t zero_stage, int3
  * next call on this thread. */
 const char* muon_last_error(void);
 
-/* Free the cached per-table descriptor arrays (synchronises the device first). */
+/* Drop the cached per-table host layouts (host memory only; no device work, no
+ * synchronisation). Later calls rebuild them on demand. */
 int muon_release_plans(void);
 
 /* Kernel timing for measurement. Between muon_profile_begin() and

@@ -156,7 +156,7 @@ def hyper(**kw) -> MuonHyper:
 
     Accepts lr / muon_lr (muon_lr wins, as in the DeepSpeed config), momentum,
     weight_decay, ns_method ("standard" | "gram"), ns_steps, ns_eps, ns_a/b/c,
-    grad_dtype and ns_dtype ("f32" | "bf16" | "f16")."""
+    grad_dtype and ns_dtype ("f32" | "bf16" | "f16"), param_dtype ("f32" | "bf16")."""
     h = MuonHyper()
     load().muon_default_hyper(ctypes.byref(h))
     kw = dict(kw)
@@ -227,8 +227,8 @@ def _stream(t, stream) -> Optional[int]:
 
 
 def _device(*tensors):
-    """The one GPU all given tensors (None skipped) live on. The library builds its
-    per-table plan on the current device, so every call runs under this one."""
+    """The one GPU all given tensors (None skipped) live on; every call runs with
+    it as the current device."""
     devs = {t.device for t in tensors if t is not None}
     if len(devs) != 1:
         raise ValueError(f"tensors passed to libmuonstep must share one GPU, got {sorted(map(str, devs))}")
@@ -278,8 +278,10 @@ def step(params, grads, momentum, entries, h: MuonHyper, ws=None, update_out=Non
          bf16_shadow=None, stream=None) -> None:
     """One Muon step (muon_step) on packed torch tensors; updates params and momentum."""
     torch = _torch()
-    if params.dtype != torch.float32 or momentum.dtype != torch.float32:
-        raise TypeError("params and momentum must be float32")
+    if momentum.dtype != torch.float32:
+        raise TypeError("momentum must be float32")
+    if params.dtype not in (torch.float32, torch.bfloat16) or _dtype_code(params) != h.param_dtype:
+        raise TypeError("params must be float32 or bfloat16, matching hyper.param_dtype")
     if _dtype_code(grads) != h.grad_dtype:
         raise TypeError("grads dtype does not match hyper.grad_dtype")
     numel = params.numel()

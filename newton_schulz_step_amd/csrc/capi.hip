@@ -79,90 +79,50 @@ static std::vector<GroupSet> group_sets(const Layout& L) {
 }
 
 // ---------------------------------------------------------------------------
-// plan cache: the layout and a device copy of the problem descriptors per
-// (device, table, windows, method, dtypes). A plan is shared: a call holds it
-// until its launches are enqueued, so dropping it from the cache (when the
-// cache is full, or on muon_release_plans) never frees one in use. Its device
-// array is freed once no call holds it, after that device has finished every
-// kernel that may read it.
+// plan cache: the host layout of a step per (table, windows, method, dtypes).
+// It is host memory only: a step writes its per-problem descriptors into the
+// caller's workspace on the stream, so no device memory is owned here and
+// dropping a plan (cache full, or muon_release_plans) never touches the device.
+// A plan is shared: a call holds it while it enqueues its launches.
 
 struct Plan {
   Layout L;
-  int device = 0;
-  ProblemDesc* d_problems = nullptr;
   std::vector<GroupSet> sets;   // shape groups launched together
-  Plan() = default;
-  Plan(const Plan&) = delete;
-  Plan& operator=(const Plan&) = delete;
-  ~Plan() {
-    if (!d_problems) return;
-    int cur = 0;
-    const bool restore = hipGetDevice(&cur) == hipSuccess && cur != device;
-    // nothing useful can be done about a failure while releasing
-    if (restore) (void)hipSetDevice(device);
-    (void)hipDeviceSynchronize();
-    (void)hipFree(d_problems);
-    if (restore) (void)hipSetDevice(cur);
-  }
 };
 
-// The cache is never destroyed: at process exit the HIP runtime may already be
-// gone, so cached plans are left to the process teardown.
+// The cache is never destroyed (calls may still run during process teardown).
 static std::mutex g_plan_mu;
-static auto& g_plans = *new std::map<std::string, std::shared_ptr<Plan>>();
+static auto& g_plans = *new std::map<std::string, std::shared_ptr<const Plan>>();
 static constexpr size_t kMaxPlans = 1024;
 
-static std::string plan_key(int device, const muon_matrix_t* t, const muon_window_t* w, int32_t n,
-                            const muon_hyper_t* h) {
+static std::string plan_key(const muon_matrix_t* t, const muon_window_t* w, int32_t n, const muon_hyper_t* h) {
   std::string k;
-  const int32_t hdr[6] = {device, n, h->ns_method, h->ns_dtype, h->grad_dtype, w != nullptr};
+  const int32_t hdr[5] = {n, h->ns_method, h->ns_dtype, h->grad_dtype, w != nullptr};
   k.append(reinterpret_cast<const char*>(hdr), sizeof(hdr));
   if (n > 0) k.append(reinterpret_cast<const char*>(t), sizeof(muon_matrix_t) * static_cast<size_t>(n));
   if (n > 0 && w) k.append(reinterpret_cast<const char*>(w), sizeof(muon_window_t) * static_cast<size_t>(n));
   return k;
 }
 
-// The workspace size is checked here, on a cached plan or right after the host
-// layout of a new one, so a call with too small a workspace allocates and copies
-// nothing.
-static int workspace_fits(const Plan& p, size_t have) {
-  if (have >= p.L.ws_bytes) return MUON_OK;
-  return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(p.L.ws_bytes) + " bytes");
-}
-
 static int get_plan(const muon_matrix_t* t, const muon_window_t* w, int32_t n, const muon_hyper_t* h,
-                    size_t workspace_bytes, std::shared_ptr<Plan>& out) {
-  int device = 0;
-  if (hipGetDevice(&device) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
-  const std::string key = plan_key(device, t, w, n, h);
-  std::lock_guard<std::mutex> lk(g_plan_mu);
-  auto it = g_plans.find(key);
-  if (it != g_plans.end()) {
-    out = it->second;
-    return workspace_fits(*out, workspace_bytes);
+                    size_t workspace_bytes, std::shared_ptr<const Plan>& out) {
+  const std::string key = plan_key(t, w, n, h);
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    auto it = g_plans.find(key);
+    if (it != g_plans.end()) out = it->second;
   }
-  std::shared_ptr<Plan> p = std::make_shared<Plan>();
-  p->device = device;
-  p->L = build_layout(t, n, h, w);
-  const int st = workspace_fits(*p, workspace_bytes);
-  if (st != MUON_OK) return st;
-  if (g_plans.size() >= kMaxPlans) g_plans.clear();
-  p->sets = group_sets(p->L);
-  std::vector<ProblemDesc> probs(p->L.problems.size());
-  for (size_t i = 0; i < probs.size(); ++i) {
-    const HostProblem& hp = p->L.problems[i];
-    probs[i] = ProblemDesc{hp.src_off, hp.p_base, hp.lo, hp.hi, hp.transposed, {0, 0, 0}};
+  if (!out) {
+    auto p = std::make_shared<Plan>();
+    p->L = build_layout(t, n, h, w);
+    p->sets = group_sets(p->L);
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    if (g_plans.size() >= kMaxPlans) g_plans.clear();
+    auto ins = g_plans.emplace(key, std::move(p));   // another thread may have built it first
+    out = ins.first->second;
   }
-  const size_t pb = std::max<size_t>(probs.size(), 1) * sizeof(ProblemDesc);
-  if (hipMalloc(&p->d_problems, pb) != hipSuccess) {
-    p->d_problems = nullptr;
-    return fail(MUON_ERR_HIP, "hipMalloc of the problem descriptors failed");
-  }
-  if (!probs.empty() &&
-      hipMemcpy(p->d_problems, probs.data(), probs.size() * sizeof(ProblemDesc), hipMemcpyHostToDevice) != hipSuccess)
-    return fail(MUON_ERR_HIP, "copying the problem descriptors failed");   // p's destructor frees them
-  out = p;
-  g_plans[key] = std::move(p);
+  if (workspace_bytes < out->L.ws_bytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(out->L.ws_bytes) + " bytes");
   return MUON_OK;
 }
 
@@ -212,20 +172,23 @@ static int64_t kext(int64_t len, int dtype) {
 
 struct StepCtx {
   const Plan* P;
+  const ProblemDesc* probs;   // the step's descriptors, in the workspace
   const muon_hyper_t* h;
   char* ws;
   const float* M;
-  float* params;
+  void* params;               // fp32 or bf16 (h->param_dtype)
   float* update_out;
   uint16_t* shadow;
   float decay;
   hipStream_t s;
 };
 
+static int apply_epi(const StepCtx& c) { return c.h->param_dtype == MUON_DTYPE_BF16 ? EPI_APPLY_BF16 : EPI_APPLY; }
+
 static GemmArgs apply_args(const StepCtx& c, const Group& G) {
   GemmArgs g{};
   g.params = c.params;
-  g.probs = c.P->d_problems + G.first;
+  g.probs = c.probs + G.first;
   g.m_valid = static_cast<int32_t>(G.m);
   g.n_valid = static_cast<int32_t>(G.n);
   g.decay = c.decay;
@@ -286,7 +249,7 @@ static int launch_batch(const char* kind, const StepCtx& c, int tile, bool sym, 
 static int run_prep(const StepCtx& c, const Group& G) {
   const float* invn = reinterpret_cast<const float*>(c.ws + c.P->L.off_invnorm) + G.first;
   MUON_LAUNCH("prep_x0", c.s,
-              launch_prep_x0(c.h->ns_dtype, c.M, c.P->d_problems + G.first, invn, G.count, static_cast<int>(G.m),
+              launch_prep_x0(c.h->ns_dtype, c.M, c.probs + G.first, invn, G.count, static_cast<int>(G.m),
                              static_cast<int>(G.n), static_cast<int>(G.mp), static_cast<int>(G.np), c.ws + G.x[0],
                              c.s));
   return MUON_OK;
@@ -296,7 +259,7 @@ static int run_prep(const StepCtx& c, const Group& G) {
 static int run_prep_gram(const StepCtx& c, const Group& G, void* R, float alpha) {
   PrepGramArgs a{};
   a.M = c.M;
-  a.probs = c.P->d_problems + G.first;
+  a.probs = c.probs + G.first;
   a.inv_norm = reinterpret_cast<const float*>(c.ws + c.P->L.off_invnorm) + G.first;
   a.X = c.ws + G.x[0];
   a.R = R;
@@ -369,7 +332,7 @@ static int run_standard(const StepCtx& c, const GroupSet& set) {
       }
       cur ^= 1;
     } else {
-      if ((st = launch_batch("ns_gemm_apply", c, tile, false, EPI_APPLY, v3)) != MUON_OK) return st;
+      if ((st = launch_batch("ns_gemm_apply", c, tile, false, apply_epi(c), v3)) != MUON_OK) return st;
     }
   }
   return MUON_OK;
@@ -477,7 +440,7 @@ static int run_gram(const StepCtx& c, const GroupSet& set) {
     ga.alpha = 1.0f;
     v.push_back(ga);
   }
-  return launch_batch("gram_gemm_apply", c, tile, false, EPI_APPLY, v);
+  return launch_batch("gram_gemm_apply", c, tile, false, apply_epi(c), v);
 }
 
 }  // namespace muon
@@ -529,7 +492,7 @@ int muon_workspace_size(const muon_matrix_t* table, int32_t n_entries, const muo
 
 // The shared body of muon_step and muon_step_window. `windows` NULL: params and
 // the shadow share the table's layout (params_numel == numel).
-static int step_impl(float* params, int64_t params_numel, const void* grads, float* momentum, int64_t numel,
+static int step_impl(void* params, int64_t params_numel, const void* grads, float* momentum, int64_t numel,
                      const muon_matrix_t* table, const muon_window_t* windows, int32_t n_entries,
                      const muon_hyper_t* h, void* workspace, size_t workspace_bytes, float* update_out,
                      uint16_t* bf16_shadow, void* stream) {
@@ -544,9 +507,13 @@ static int step_impl(float* params, int64_t params_numel, const void* grads, flo
     if (table[i].offset + table[i].rows * table[i].cols > numel)
       return fail(MUON_ERR_RANGE, "entry " + std::to_string(i) + " ends beyond numel");
   if (windows) {
+    if (h->param_dtype != MUON_DTYPE_F32)
+      return fail(MUON_ERR_UNSUPPORTED, "a partition holder's step takes float32 params only");
     st = validate_windows(table, windows, n_entries, params_numel, err);
     if (st != MUON_OK) return fail(st, err);
   }
+  if (bf16_shadow && h->param_dtype == MUON_DTYPE_BF16)
+    return fail(MUON_ERR_UNSUPPORTED, "bf16 params are their own bf16 copy: pass no bf16_shadow");
   if (n_entries == 0 || numel == 0) return MUON_OK;
   if (workspace == nullptr) return fail(MUON_ERR_NULL, "workspace is NULL");
   if (misaligned(params, 16) || misaligned(grads, 16) || misaligned(momentum, 16) ||
@@ -554,10 +521,11 @@ static int step_impl(float* params, int64_t params_numel, const void* grads, flo
     return fail(MUON_ERR_ALIGN, "a buffer pointer is not 16-byte aligned");
   if (misaligned(workspace, 256)) return fail(MUON_ERR_ALIGN, "workspace is not 256-byte aligned");
   const size_t gsz = static_cast<size_t>(element_size(h->grad_dtype));
+  const size_t psz = static_cast<size_t>(element_size(h->param_dtype));
   const size_t ne = static_cast<size_t>(numel), pe = static_cast<size_t>(params_numel);
   const char* pname = windows ? "partition" : "params";
   std::vector<Span> spans = {
-      {reinterpret_cast<const char*>(params), reinterpret_cast<const char*>(params) + pe * 4, pname},
+      {static_cast<const char*>(params), static_cast<const char*>(params) + pe * psz, pname},
       {static_cast<const char*>(grads), static_cast<const char*>(grads) + ne * gsz, "grads"},
       {reinterpret_cast<const char*>(momentum), reinterpret_cast<const char*>(momentum) + ne * 4, "momentum"},
       {static_cast<const char*>(workspace), static_cast<const char*>(workspace) + workspace_bytes, "workspace"}};
@@ -570,24 +538,27 @@ static int step_impl(float* params, int64_t params_numel, const void* grads, flo
   std::string which;
   if (overlapping(spans, which)) return fail(MUON_ERR_OVERLAP, "buffers overlap: " + which);
 
-  std::shared_ptr<Plan> plan;
+  std::shared_ptr<const Plan> plan;
   st = get_plan(table, windows, n_entries, h, workspace_bytes, plan);
   if (st != MUON_OK) return st;
   const Plan* P = plan.get();
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  ProblemDesc* probs = reinterpret_cast<ProblemDesc*>(ws + P->L.off_desc);
   double* partials = reinterpret_cast<double*>(ws + P->L.off_partials);
   float* invn = reinterpret_cast<float*>(ws + P->L.off_invnorm);
   const float mu = h->momentum;
+  MUON_LAUNCH("expand_desc", s,
+              launch_expand_desc(P->L.entries.data(), static_cast<int>(P->L.entries.size()), probs, s));
   for (const Group& G : P->L.groups)
     MUON_LAUNCH("momentum_sumsq", s,
-                launch_momentum_sumsq(h->grad_dtype, momentum, grads, P->d_problems + G.first, G.count, G.m * G.n,
+                launch_momentum_sumsq(h->grad_dtype, momentum, grads, probs + G.first, G.count, G.m * G.n,
                                       G.chunks, mu, partials + G.partial_first, s));
   for (const Group& G : P->L.groups)
     MUON_LAUNCH("finalize_norm", s,
                 launch_finalize_norm(partials + G.partial_first, G.chunks, G.count, h->ns_eps, invn + G.first, s));
-  StepCtx c{P, h, ws, momentum, params, update_out, bf16_shadow,
+  StepCtx c{P, probs, h, ws, momentum, params, update_out, bf16_shadow,
             static_cast<float>(1.0 - static_cast<double>(h->lr) * static_cast<double>(h->weight_decay)), s};
   for (const GroupSet& set : P->sets) {
     st = (h->ns_method == MUON_NS_STANDARD) ? run_standard(c, set) : run_gram(c, set);
@@ -599,7 +570,7 @@ static int step_impl(float* params, int64_t params_numel, const void* grads, flo
 int muon_step(void* params, const void* grads, float* momentum, int64_t numel, const muon_matrix_t* table,
               int32_t n_entries, const muon_hyper_t* h, void* workspace, size_t workspace_bytes, float* update_out,
               uint16_t* bf16_shadow, void* stream) {
-  return step_impl(static_cast<float*>(params), numel, grads, momentum, numel, table, nullptr, n_entries, h,
+  return step_impl(params, numel, grads, momentum, numel, table, nullptr, n_entries, h,
                    workspace, workspace_bytes, update_out, bf16_shadow, stream);
 }
 

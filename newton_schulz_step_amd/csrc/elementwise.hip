@@ -13,6 +13,47 @@
 namespace muon {
 
 // ---------------------------------------------------------------------------
+// per-problem descriptors: block y of a launch writes the problems of entry y of
+// its chunk (split blocks of a matrix are consecutive problems of one group)
+
+struct DescChunk {
+  EntryRec e[kDescChunk];
+};
+
+__global__ __launch_bounds__(256) void expand_desc_kernel(DescChunk c, ProblemDesc* out) {
+  const EntryRec r = c.e[blockIdx.y];
+  const int64_t nblk = r.nblk_t >> 1;
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; b < nblk;
+       b += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t first = b * r.size;
+    ProblemDesc d;
+    d.src_off = r.offset + first;
+    d.p_base = r.p0 + first;
+    d.lo = min(max(r.lo - first, int64_t(0)), r.size);
+    d.hi = min(max(r.hi - first, int64_t(0)), r.size);
+    d.transposed = r.nblk_t & 1;
+    d.pad[0] = d.pad[1] = d.pad[2] = 0;
+    out[r.first + b] = d;
+  }
+}
+
+hipError_t launch_expand_desc(const EntryRec* entries, int n, ProblemDesc* out, hipStream_t s) {
+  static_assert(sizeof(ProblemDesc) == kProblemDescBytes, "descriptor size used by the workspace layout");
+  for (int i = 0; i < n; i += kDescChunk) {
+    const int cnt = n - i < kDescChunk ? n - i : kDescChunk;
+    DescChunk c;
+    int64_t most = 1;
+    for (int k = 0; k < kDescChunk; ++k) c.e[k] = k < cnt ? entries[i + k] : EntryRec{};
+    for (int k = 0; k < cnt; ++k) most = max(most, static_cast<int64_t>(entries[i + k].nblk_t >> 1));
+    const int64_t gx = min((most + 255) / 256, int64_t(256));
+    hipLaunchKernelGGL(expand_desc_kernel, dim3(static_cast<unsigned>(gx), cnt), dim3(256), 0, s, c, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
 // momentum (DeepSpeed-Muon article, "什么是 Muon 优化器？": momentum first) and the
 // sum of squares that the Frobenius normalisation needs
 

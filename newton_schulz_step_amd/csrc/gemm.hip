@@ -31,8 +31,9 @@
 // to Ct; a symmetric launch computes only tiles with ti >= tj and mirrors them
 // (on diagonal tiles each element is written exactly once, so the stored matrix
 // is exactly symmetric). The apply epilogue instead finishes the Muon step,
-// p <- p * decay - lr * v, at the matrix's stored (possibly transposed) position,
-// for the elements of the problem's window (the whole problem in an ordinary step).
+// p <- p * decay - lr * v (fp32 or bf16 params), at the matrix's stored (possibly
+// transposed) position, for the elements of the problem's window (the whole
+// problem in an ordinary step).
 // Global loads of the epilogue (D, params) are issued in batches ahead of use.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -421,12 +422,54 @@ template <> struct Pack8<float> {
   __device__ __forceinline__ float get(int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
 };
 
+// Parameter access of the apply epilogues: fp32 (EPI_APPLY) or bf16 words
+// (EPI_APPLY_BF16), as floats. The 8-element forms need pidx a multiple of 8.
+template <int EPI>
+__device__ __forceinline__ void load_p8(const void* params, int64_t pidx, f32x4& p0, f32x4& p1) {
+  if constexpr (EPI == EPI_APPLY_BF16) {
+    const u16x8 w = *reinterpret_cast<const u16x8*>(static_cast<const unsigned short*>(params) + pidx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { p0[e] = bf16_bits_to_f32(w[e]); p1[e] = bf16_bits_to_f32(w[e + 4]); }
+  } else {
+    const f32x4* pp = reinterpret_cast<const f32x4*>(static_cast<const float*>(params) + pidx);
+    p0 = pp[0];
+    p1 = pp[1];
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void store_p8(void* params, int64_t pidx, const f32x4& o0, const f32x4& o1) {
+  if constexpr (EPI == EPI_APPLY_BF16) {
+    u16x8 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { w[e] = bf16_bits(keep_f32(o0[e])); w[e + 4] = bf16_bits(keep_f32(o1[e])); }
+    *reinterpret_cast<u16x8*>(static_cast<unsigned short*>(params) + pidx) = w;
+  } else {
+    f32x4* pp = reinterpret_cast<f32x4*>(static_cast<float*>(params) + pidx);
+    pp[0] = o0;
+    pp[1] = o1;
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ float load_p1(const void* params, int64_t i) {
+  if constexpr (EPI == EPI_APPLY_BF16) return bf16_bits_to_f32(static_cast<const unsigned short*>(params)[i]);
+  else return static_cast<const float*>(params)[i];
+}
+
+template <int EPI>
+__device__ __forceinline__ void store_p1(void* params, int64_t i, float v) {
+  if constexpr (EPI == EPI_APPLY_BF16) static_cast<unsigned short*>(params)[i] = bf16_bits(keep_f32(v));
+  else static_cast<float*>(params)[i] = v;
+}
+
 // One run of up to 8 consecutive stored elements e0 .. e0 + cnt - 1 of a problem:
 // v goes to update_out at uidx (every element), and p <- p * decay - lr * v, with
-// the optional bf16 copy of the new p (shadow), to the params at pidx for the
-// elements inside the problem's window [lo, hi). `vec`: a whole run inside the
-// window with pidx a multiple of 8 and uidx of 4, whose params the caller has
-// loaded into p0, p1; anything else takes the scalar path.
+// the optional bf16 copy of the new p (shadow, fp32 params only), to the params
+// at pidx for the elements inside the problem's window [lo, hi). `vec`: a whole
+// run inside the window with pidx a multiple of 8 and uidx of 4, whose params
+// the caller has loaded into p0, p1; anything else takes the scalar path.
+template <int EPI>
 __device__ __forceinline__ void apply8(const GemmArgs& a, int64_t pidx, int64_t uidx, int64_t e0, int cnt,
                                        int64_t lo, int64_t hi, const float (&v)[8], const f32x4& p0,
                                        const f32x4& p1, bool vec) {
@@ -437,9 +480,7 @@ __device__ __forceinline__ void apply8(const GemmArgs& a, int64_t pidx, int64_t 
       o0[e] = p0[e] * a.decay - a.lr * v[e];
       o1[e] = p1[e] * a.decay - a.lr * v[e + 4];
     }
-    f32x4* pp = reinterpret_cast<f32x4*>(a.params + pidx);
-    pp[0] = o0;
-    pp[1] = o1;
+    store_p8<EPI>(a.params, pidx, o0, o1);
     if (a.update_out) {
       f32x4 u0, u1;
 #pragma unroll
@@ -448,19 +489,23 @@ __device__ __forceinline__ void apply8(const GemmArgs& a, int64_t pidx, int64_t 
       up[0] = u0;
       up[1] = u1;
     }
-    if (a.shadow) {
-      u16x8 sh;
+    if constexpr (EPI == EPI_APPLY) {
+      if (a.shadow) {
+        u16x8 sh;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { sh[e] = bf16_bits(o0[e]); sh[e + 4] = bf16_bits(o1[e]); }
-      *reinterpret_cast<u16x8*>(a.shadow + pidx) = sh;
+        for (int e = 0; e < 4; ++e) { sh[e] = bf16_bits(o0[e]); sh[e + 4] = bf16_bits(o1[e]); }
+        *reinterpret_cast<u16x8*>(a.shadow + pidx) = sh;
+      }
     }
   } else {
     for (int e = 0; e < cnt; ++e) {
       if (a.update_out) a.update_out[uidx + e] = v[e];
       if (e0 + e >= lo && e0 + e < hi) {
-        const float pn = a.params[pidx + e] * a.decay - a.lr * v[e];
-        a.params[pidx + e] = pn;
-        if (a.shadow) a.shadow[pidx + e] = bf16_bits(pn);
+        const float pn = load_p1<EPI>(a.params, pidx + e) * a.decay - a.lr * v[e];
+        store_p1<EPI>(a.params, pidx + e, pn);
+        if constexpr (EPI == EPI_APPLY) {
+          if (a.shadow) a.shadow[pidx + e] = bf16_bits(pn);
+        }
       }
     }
   }
@@ -501,7 +546,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
 
   int transposed = 0;
   int64_t src = 0, pb = 0, wlo = 0, whi = 0;
-  if constexpr (EPI == EPI_APPLY) {
+  constexpr bool APPLY = (EPI == EPI_APPLY || EPI == EPI_APPLY_BF16);
+  if constexpr (APPLY) {
     const ProblemDesc pd = a.probs[prob];
     transposed = pd.transposed;
     src = pd.src_off;
@@ -514,7 +560,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   T* C = static_cast<T*>(a.C);
   T* Ct = static_cast<T*>(a.Ct);
   const T* D = static_cast<const T*>(a.D);
-  const bool need_col = (EPI == EPI_APPLY) ? (transposed != 0) : (Ct != nullptr);
+  const bool need_col = APPLY ? (transposed != 0) : (Ct != nullptr);
 
   Pack8<T> dq[NR];
   auto load_d = [&](int i) {
@@ -544,8 +590,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       for (int r = 0; r < 16; ++r)
         stg[srow((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), j * 32 + (lane & 31))] = acc[i][j][r];
     lds_order();
-
-    constexpr bool APPLY = (EPI == EPI_APPLY);
 
     // ---- row pass: each lane finishes one 8-column chunk at a time
 #pragma unroll
@@ -608,11 +652,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
           const int gi = gi_w + i * 32 + q / CPR, gj = gj_w + (q % CPR) * 8;
           const int64_t e = static_cast<int64_t>(gi) * n + gj;
           pvec[u] = gi < m && gj + 8 <= n && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
-          if (pvec[u]) {
-            const f32x4* pp = reinterpret_cast<const f32x4*>(a.params + pb + e);
-            p0[u] = pp[0];
-            p1[u] = pp[1];
-          }
+          if (pvec[u]) load_p8<EPI>(a.params, pb + e, p0[u], p1[u]);
         }
 #pragma unroll
         for (int u = 0; u < PB; ++u) {
@@ -626,7 +666,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
 #pragma unroll
             for (int e = 0; e < 4; ++e) { v[e] = s0[e]; v[e + 4] = s1[e]; }
             const int64_t e = static_cast<int64_t>(gi) * n + gj;
-            apply8(a, pb + e, src + e, e, min(8, n - gj), wlo, whi, v, p0[u], p1[u], pvec[u]);
+            apply8<EPI>(a, pb + e, src + e, e, min(8, n - gj), wlo, whi, v, p0[u], p1[u], pvec[u]);
           }
         }
       }
@@ -648,11 +688,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
             const int gi = gi_w + i * 32 + (q & 3) * 8, gj = gj_w + (q >> 2);
             const int64_t e = static_cast<int64_t>(gj) * m + gi;
             cvec[u] = gj < n && gi + 8 <= m && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
-            if (cvec[u]) {
-              const f32x4* pp = reinterpret_cast<const f32x4*>(a.params + pb + e);
-              c0[u] = pp[0];
-              c1[u] = pp[1];
-            }
+            if (cvec[u]) load_p8<EPI>(a.params, pb + e, c0[u], c1[u]);
           }
 #pragma unroll
           for (int u = 0; u < PB; ++u) {
@@ -664,7 +700,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
 #pragma unroll
               for (int e = 0; e < 8; ++e) w[e] = stg[srow(r8 + e, cc)];
               const int64_t e = static_cast<int64_t>(gj) * m + gi;
-              apply8(a, pb + e, src + e, e, min(8, m - gi), wlo, whi, w, c0[u], c1[u], cvec[u]);
+              apply8<EPI>(a, pb + e, src + e, e, min(8, m - gi), wlo, whi, w, c0[u], c1[u], cvec[u]);
             }
           }
         }
@@ -1135,6 +1171,7 @@ template <typename T, int TILE>
 static hipError_t launch_tile(bool sym, int epi, const GemmBatch& b, hipStream_t s) {
   if (sym) return epi == EPI_STORE ? launch_t<T, TILE, true, EPI_STORE, false>(b, s) : hipErrorInvalidValue;
   if (epi == EPI_APPLY) return launch_t<T, TILE, false, EPI_APPLY, true>(b, s);
+  if (epi == EPI_APPLY_BF16) return launch_t<T, TILE, false, EPI_APPLY_BF16, true>(b, s);
   return launch_t<T, TILE, false, EPI_STORE, true>(b, s);
 }
 

@@ -2,10 +2,18 @@
 #pragma once
 
 #include "common.hpp"
+#include "plan.hpp"
 
 namespace muon {
 
-enum { EPI_STORE = 0, EPI_APPLY = 1 };
+// Per-problem descriptors of a step, written into the caller's workspace on the
+// stream from the table's entry records, passed by value kDescChunk at a time.
+constexpr int kDescChunk = 32;
+hipError_t launch_expand_desc(const EntryRec* entries, int n, ProblemDesc* out, hipStream_t s);
+
+// EPI_APPLY: fp32 params; EPI_APPLY_BF16: bf16 params (raw 16-bit words), the
+// new value rounded to nearest even
+enum { EPI_STORE = 0, EPI_APPLY = 1, EPI_APPLY_BF16 = 2 };
 
 // One batched GEMM launch: for every problem p of a shape group,
 //   C_p = epilogue(alpha * P_p op(Q_p) + beta * D_p + gamma * I),
@@ -24,8 +32,8 @@ struct GemmArgs {
   const void* D; int64_t d_ps; int32_t ldd;      // optional (beta term)
   void* C; int64_t c_ps; int32_t ldc;            // optional row-major store
   void* Ct; int64_t ct_ps; int32_t ldct;         // optional transposed store (SYM: mirror, = C)
-  // EPI_APPLY: p <- p * decay - lr * v at the problem's stored position
-  float* params; const ProblemDesc* probs; int32_t m_valid, n_valid;
+  // EPI_APPLY(_BF16): p <- p * decay - lr * v at the problem's stored position
+  void* params; const ProblemDesc* probs; int32_t m_valid, n_valid;
   float decay, lr;
   float* update_out; unsigned short* shadow;
 };

@@ -45,7 +45,10 @@ int validate(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* 
     if (!std::isfinite(f)) { err = "a hyperparameter is not finite"; return MUON_ERR_BAD_HYPER; }
   if (h->ns_eps < 0.0f) { err = "ns_eps < 0"; return MUON_ERR_BAD_HYPER; }
   if (h->ns_steps < 1 || h->ns_steps > 64) { err = "ns_steps outside [1, 64]"; return MUON_ERR_BAD_HYPER; }
-  if (h->param_dtype != MUON_DTYPE_F32) { err = "only float32 params are implemented"; return MUON_ERR_UNSUPPORTED; }
+  if (h->param_dtype != MUON_DTYPE_F32 && h->param_dtype != MUON_DTYPE_BF16) {
+    err = "param_dtype must be F32 or BF16";
+    return MUON_ERR_UNSUPPORTED;
+  }
   if (element_size(h->grad_dtype) == 0) { err = "grad_dtype must be F32, BF16 or F16"; return MUON_ERR_UNSUPPORTED; }
   if (element_size(h->ns_dtype) == 0) { err = "ns_dtype must be F32, BF16 or F16"; return MUON_ERR_UNSUPPORTED; }
   if (h->ns_method == MUON_NS_GRAM && h->ns_dtype == MUON_DTYPE_BF16) {
@@ -111,6 +114,7 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
   // canonical shape -> group, in order of first appearance
   std::map<std::pair<int64_t, int64_t>, int> gid;
   std::vector<std::vector<HostProblem>> per_group;
+  std::vector<std::pair<int, size_t>> entry_pos;   // (group, index of its first problem in the group)
   for (int32_t i = 0; i < n_entries; ++i) {
     const muon_matrix_t& e = table[i];
     const int64_t pr = e.split_rows > 0 ? e.split_rows : e.rows;
@@ -129,6 +133,7 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
     } else {
       g = it->second;
     }
+    entry_pos.emplace_back(g, per_group[g].size());
     for (int64_t b = 0; b < nblk; ++b) {
       HostProblem p;
       const int64_t first = b * pr * e.cols;       // entry flat index of the block's element 0
@@ -158,6 +163,25 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
     L.groups[g].count = static_cast<int>(per_group[g].size());
     L.problems.insert(L.problems.end(), per_group[g].begin(), per_group[g].end());
   }
+  for (int32_t i = 0; i < n_entries; ++i) {
+    const muon_matrix_t& e = table[i];
+    const int64_t pr = e.split_rows > 0 ? e.split_rows : e.rows;
+    EntryRec r{};
+    r.offset = e.offset;
+    r.size = pr * e.cols;
+    if (windows == nullptr) {
+      r.lo = 0;
+      r.hi = e.rows * e.cols;
+      r.p0 = e.offset;
+    } else {
+      r.lo = windows[i].lo;
+      r.hi = windows[i].hi;
+      r.p0 = windows[i].param_offset - windows[i].lo;
+    }
+    r.first = L.groups[entry_pos[i].first].first + static_cast<int32_t>(entry_pos[i].second);
+    r.nblk_t = static_cast<int32_t>(((e.rows / pr) << 1) | (pr > e.cols ? 1 : 0));
+    L.entries.push_back(r);
+  }
   // momentum blocks: each problem is cut into blocks of kMomChunk elements; the
   // per-block partial sums of squares are laid out group by group, problem by problem
   for (Group& G : L.groups) {
@@ -169,6 +193,8 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
   // workspace
   const size_t esz = static_cast<size_t>(element_size(h->ns_dtype));
   size_t off = 0;
+  L.off_desc = off;
+  off = align256(off + std::max<size_t>(L.problems.size(), 1) * kProblemDescBytes);
   L.off_partials = off;
   off = align256(off + L.n_partials * sizeof(double));
   L.off_invnorm = off;

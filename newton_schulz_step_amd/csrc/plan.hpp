@@ -35,13 +35,31 @@ struct Group {
   size_t r2 = 0, p[2] = {0, 0}, t = 0;   // gram: next R, P (ping-pong), R Q
 };
 
+// What the descriptor kernel needs to write the problems of one table entry:
+// problem b (b < nblk) of the entry is problem first + b of the layout, with
+// src_off = offset + b * size, p_base = p0 + b * size, and the part of [lo, hi)
+// (flat in the matrix) that falls in [b * size, (b + 1) * size), shifted to the
+// block.
+struct EntryRec {
+  int64_t offset;   // element offset of the matrix in grads / momentum
+  int64_t size;     // elements of one problem (block rows x cols)
+  int64_t lo, hi;   // elements of the flattened matrix whose update is applied
+  int64_t p0;       // params index of flat element 0 of the matrix
+  int32_t first;    // layout index of the entry's first problem
+  int32_t nblk_t;   // problems of the entry << 1 | transposed
+};
+
 struct Layout {
   std::vector<HostProblem> problems;   // ordered by group
   std::vector<Group> groups;
+  std::vector<EntryRec> entries;       // one per table entry, for the descriptor kernel
   size_t n_partials = 0;               // per-block partial sums of squares, all groups
+  size_t off_desc = 0;                 // per-problem descriptors (ProblemDesc, 48 bytes each)
   size_t off_partials = 0, off_invnorm = 0;
   size_t ws_bytes = 0;
 };
+
+constexpr size_t kProblemDescBytes = 48;
 
 int element_size(int dtype);
 

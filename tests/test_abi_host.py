@@ -76,7 +76,8 @@ def test_workspace_size_validation(lib):
     assert _ws([(4, 4, 4, 0)])[0] == nss.ERR_ALIGN
     assert _ws([(0, 4, 4, 0), (8, 4, 4, 0)])[0] == nss.ERR_OVERLAP
     assert _ws([(0, 4, 4, 0)], ns_method="gram", ns_dtype="bf16")[0] == nss.ERR_UNSUPPORTED
-    assert _ws([(0, 4, 4, 0)], param_dtype=1)[0] == nss.ERR_UNSUPPORTED
+    assert _ws([(0, 4, 4, 0)], param_dtype=1)[0] == nss.OK            # bf16 params
+    assert _ws([(0, 4, 4, 0)], param_dtype=2)[0] == nss.ERR_UNSUPPORTED
     assert _ws([(0, 4, 4, 0)], ns_steps=0)[0] == nss.ERR_BAD_HYPER
     assert _ws([(0, 4, 4, 0)], lr=float("nan"))[0] == nss.ERR_BAD_HYPER
     st, msg = _ws([(0, 4, 4, 0)], ns_method=7)
@@ -128,6 +129,21 @@ def test_step_rejects_before_any_device_work(lib):
     assert _raw_step(lib, [], 4096, h)[0] == nss.OK
     st, msg = _raw_step(lib, [(0, 64, 64, 0), (64 * 64, 8, 8, 0)], 4096, h)
     assert st == nss.ERR_RANGE and "entry 1" in msg
+
+
+def test_bf16_params_checks(lib):
+    # bf16 params take 2 bytes per element; they are their own bf16 copy, so a
+    # shadow is refused, and partition holders take float32 partitions only
+    h = nss.hyper(ns_method="standard", ns_dtype="bf16", param_dtype="bf16")
+    ent = [(0, 64, 64, 0)]
+    assert _raw_step(lib, ent, 4096, h, shadow=FAKE + (5 << 36))[0] == nss.ERR_UNSUPPORTED
+    assert _raw_step(lib, ent, 4096, h, mom=FAKE + 4096 * 2 - 16)[0] == nss.ERR_OVERLAP
+    assert _raw_step(lib, ent, 4096, h, mom=FAKE + 4096 * 2, ws=None)[0] == nss.ERR_NULL
+    arr, n = nss.table(ent)
+    warr = nss.windows([(0, 16, 0)], n)
+    st = lib.muon_step_window(FAKE, 16, FAKE + (1 << 36), FAKE + (2 << 36), 4096, arr, warr, n,
+                              ctypes.byref(h), FAKE + (3 << 36), 1 << 40, None, None, None)
+    assert st == nss.ERR_UNSUPPORTED
 
 
 def _raw_window(lib, entries, wins, numel, pnumel, h, part=FAKE + (4 << 36), grads=FAKE + (1 << 36),

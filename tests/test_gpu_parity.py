@@ -186,6 +186,58 @@ def test_bf16_shadow_is_rne_of_new_params(lib):
     assert not np.any(gpu["shadow"][outside_mask(wl.table(), wl.numel)])
 
 
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16"), ("standard", "f32")])
+def test_bf16_params(lib, method, ns_dtype):
+    # bf16 weights updated in place (the bf16 model weights of the ZeRO page's
+    # parameter breakdown, the bf16 packed buffer of the DMuon page). Below bf16
+    # resolution the weight change is mostly rounding, so parity rests on
+    # update_out; the new weights must be the RNE bf16 rounding of what the fp32
+    # path computes from the same (bf16-representable) weights: bit for bit equal
+    # to that path's bf16 shadow, and within one bf16 ulp of the float64 value.
+    import torch
+    shapes = [(300, 200, 0), (130, 700, 0), (64, 2000, 0), (3, 1, 0), (256, 96, 64), (9, 13, 0)]
+    wl = W.custom_workload(shapes, grad_dtype="bf16", wid=118, grad_kind="gaussian")
+    params, grads, mom = W.host_inputs(wl)
+    tab = wl.table()
+    pbits = W.f32_to_bf16_bits(params)
+    p32 = W.bf16_bits_to_f32(pbits)                        # the same weights, exactly
+    dev = "cuda:0"
+    print(f"[case] bf16 params {method} {ns_dtype}: {tab}", flush=True)
+    g = to_device(grads, dev, torch)
+    pb = to_device(pbits, dev, torch)
+    mb = to_device(mom, dev, torch)
+    ub = torch.zeros(len(params), device=dev)
+    lib.step(pb, g, mb, tab, _hyper(lib, wl, method, ns_dtype, param_dtype="bf16"), update_out=ub)
+    pf = to_device(p32, dev, torch)
+    mf = to_device(mom, dev, torch)
+    uf = torch.zeros(len(params), device=dev)
+    sh = torch.zeros(len(params), dtype=torch.int16, device=dev)
+    lib.step(pf, g, mf, tab, _hyper(lib, wl, method, ns_dtype), update_out=uf, bf16_shadow=sh)
+    torch.cuda.synchronize()
+    new_bits = pb.cpu().view(torch.int16).numpy().view(np.uint16)
+    U = ub.cpu().numpy()
+    assert np.array_equal(U, uf.cpu().numpy())             # the iteration does not see the weights
+    assert np.array_equal(mb.cpu().numpy(), mf.cpu().numpy())
+    assert np.array_equal(new_bits, sh.cpu().numpy().view(np.uint16))
+    g64 = W.grad_as_f64(wl, grads)
+    kw = dict(lr=wl.lr, mu=wl.momentum, weight_decay=wl.weight_decay, method=method)
+    ref = oracle.muon_step(p32, g64, mom, tab, store_fmt=None if ns_dtype == "f32" else ns_dtype, **kw)
+    exact = oracle.muon_step(p32, g64, mom, tab, **kw)
+    gate = FP32_GATE if ns_dtype == "f32" else LP_GATE
+    want = p32.astype(np.float64) * _decay32(wl.lr, wl.weight_decay) - np.float64(np.float32(wl.lr)) * U
+    new = W.bf16_bits_to_f32(new_bits).astype(np.float64)
+    ulp = np.abs(W.bf16_bits_to_f32(W.f32_to_bf16_bits(want.astype(np.float32)) + 1).astype(np.float64) -
+                 W.bf16_bits_to_f32(W.f32_to_bf16_bits(want.astype(np.float32))).astype(np.float64))
+    for i, sl in enumerate(entry_slices(tab)):
+        eo = rel(U[sl], ref["update"][sl])
+        print(f"  entry {i}: O {eo:.2e}")
+        assert eo <= gate, (i, eo)
+        assert rel(mb.cpu().numpy()[sl], exact["momentum"][sl]) <= MOM_GATE
+        assert np.all(np.abs(new[sl] - want[sl]) <= ulp[sl]), i
+    mask = outside_mask(tab, len(params))
+    assert np.array_equal(new_bits[mask], pbits[mask]) and not np.any(U[mask])
+
+
 # --------------------------------------------------------------------------- exact properties
 
 def _dev_step(nss, params, grads, mom, tab, h, dev="cuda:0"):

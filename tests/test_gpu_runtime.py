@@ -1,15 +1,19 @@
 """GPU: the library's runtime services, through the C ABI.
 
-- Plan cache: a step after muon_release_plans() rebuilds the table's plan and
-  gives the same bits; many distinct tables each get their own plan.
+- Plan cache (host layouts): a step after muon_release_plans() rebuilds the
+  table's layout and gives the same bits; many distinct tables each get their
+  own.
 - Profiling hooks: between muon_profile_begin() and muon_profile_end() every
   launch is counted under its kind; the counts are the launch sequence of the
   method (which bench.py's per-kernel times rely on).
 - Threads: two host threads stepping different tables on their own streams
   give the same bits as the same steps run one after the other.
-- Graphs: after one call with a table a step is kernel launches only; captured
-  into a HIP graph and replayed (with eager work and synchronisation between
-  replays), every replay equals an eager step from the same state.
+- No synchronisation: the first call ever made with a table returns while a
+  long step queued earlier on another stream is still running.
+- Graphs: every call is kernel launches only, so even the first call with a
+  table can be captured into a HIP graph; every replay (with eager work and
+  synchronisation between replays, and after the host cache has been
+  overflowed and dropped) equals an eager step from the same state.
 """
 import threading
 
@@ -63,17 +67,17 @@ def test_release_plans_and_many_tables(lib):
 @pytest.mark.parametrize("method,ns_dtype,shapes,want", [
     # one 128-tile group (m >= 129): the separate launches
     ("standard", "bf16", [(256, 384, 0)],
-     {"momentum_sumsq": 1, "finalize_norm": 1, "prep_x0": 1, "ns_gemm_xxt": 5, "ns_gemm_poly": 5,
+     {"expand_desc": 1, "momentum_sumsq": 1, "finalize_norm": 1, "prep_x0": 1, "ns_gemm_xxt": 5, "ns_gemm_poly": 5,
       "ns_gemm_update": 4, "ns_gemm_apply": 1}),
     # one single-row group (m <= 128, 16-bit): X0 + Gram and update + Gram in one pass each
     ("standard", "bf16", [(128, 640, 0)],
-     {"momentum_sumsq": 1, "finalize_norm": 1, "prep_gram": 1, "ns_gemm_poly": 5,
+     {"expand_desc": 1, "momentum_sumsq": 1, "finalize_norm": 1, "prep_gram": 1, "ns_gemm_poly": 5,
       "ns_update_gram": 4, "ns_gemm_apply": 1}),
     ("gram", "f16", [(256, 384, 0)],
-     {"momentum_sumsq": 1, "finalize_norm": 1, "prep_x0": 1, "gram_gemm_sym": 14, "gram_gemm_full": 4,
+     {"expand_desc": 1, "momentum_sumsq": 1, "finalize_norm": 1, "prep_x0": 1, "gram_gemm_sym": 14, "gram_gemm_full": 4,
       "gram_gemm_apply": 1}),
     ("gram", "f16", [(128, 640, 0)],
-     {"momentum_sumsq": 1, "finalize_norm": 1, "prep_gram": 1, "gram_gemm_sym": 13, "gram_gemm_full": 4,
+     {"expand_desc": 1, "momentum_sumsq": 1, "finalize_norm": 1, "prep_gram": 1, "gram_gemm_sym": 13, "gram_gemm_full": 4,
       "gram_gemm_apply": 1}),
 ])
 def test_profile_counts_the_launch_sequence(lib, method, ns_dtype, shapes, want):
@@ -124,33 +128,51 @@ def test_two_threads_two_streams(lib):
             assert torch.equal(got[k][0], want[k][0]) and torch.equal(got[k][1], want[k][1]), k
 
 
+def _overflow_plan_cache(nss, n=1030):
+    """More distinct tables than the host cache holds (1024), each stepped once on
+    a tiny buffer; then the cache is dropped."""
+    import torch
+    dev = "cuda:0"
+    p = torch.zeros(4096, device=dev)
+    g = torch.zeros(4096, dtype=torch.bfloat16, device=dev)
+    m = torch.zeros(4096, device=dev)
+    h = nss.hyper(ns_method="standard", ns_dtype="bf16", grad_dtype="bf16")
+    tables = [[(8 * (k % 64), 1 + k // 64, 8 + 8 * (k % 7), 0)] for k in range(n)]
+    assert len({tuple(t[0]) for t in tables}) == n and all(o + r * c <= 4096 for (o, r, c, _), in tables)
+    ws = torch.empty(max(nss.workspace_size(t, h) for t in tables), dtype=torch.uint8, device=dev)
+    for t in tables:
+        nss.step(p, g, m, t, h, ws=ws)
+    nss.release_plans()
+
+
 @pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16"), ("standard", "f32")])
 def test_graph_capture_and_replay(lib, method, ns_dtype):
-    # after one call with a table (which builds its plan), a step is kernel
-    # launches only, so it can be captured into a HIP graph; each replay is one
-    # more step and must equal an eager step from the same state
+    # every call is kernel launches only (the descriptors are written into the
+    # workspace on the stream), so the first call ever made with a table can be
+    # captured into a HIP graph; each replay is one more step and must equal an
+    # eager step from the same state, also after the host cache was overflowed
     import torch
     nss = lib
     gdt = "f32" if ns_dtype == "f32" else "bf16"
-    wl, params, grads, mom = _inputs([(256, 384, 0), (128, 640, 0), (300, 140, 0)], wid=178, grad_dtype=gdt)
+    # a shape set no other test uses, so the captured call is this table's first
+    wl, params, grads, mom = _inputs([(264, 392, 0), (128, 648, 0), (304, 136, 0)], wid=178, grad_dtype=gdt)
     h = nss.hyper(ns_method=method, ns_dtype=ns_dtype, grad_dtype=gdt, lr=wl.lr, momentum=wl.momentum,
                   weight_decay=wl.weight_decay)
     tab = wl.table()
     dev = "cuda:0"
+    nss.release_plans()
     p, g, m = (to_device(a.copy(), dev, torch) for a in (params, grads, mom))
     pe, ge, me = (to_device(a.copy(), dev, torch) for a in (params, grads, mom))
     ws = torch.empty(nss.workspace_size(tab, h), dtype=torch.uint8, device=dev)
     ws_e = torch.empty_like(ws)
-    nss.step(p, g, m, tab, h, ws=ws)              # plan built; first step eager on both copies
-    nss.step(pe, ge, me, tab, h, ws=ws_e)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.graph(graph, stream=s):
-        nss.step(p, g, m, tab, h, ws=ws)
+        nss.step(p, g, m, tab, h, ws=ws, stream=s)
     torch.cuda.synchronize()
-    for r in range(4):
+    for r in range(5):
         graph.replay()
         torch.cuda.synchronize()
         nss.step(pe, ge, me, tab, h, ws=ws_e)     # the same step, eager
@@ -159,3 +181,42 @@ def test_graph_capture_and_replay(lib, method, ns_dtype):
         # eager work on the graph's own buffers between replays
         g.mul_(1.0)
         torch.cuda.synchronize()
+        if r == 2:
+            _overflow_plan_cache(nss)
+            torch.cuda.synchronize()
+
+
+def test_first_call_does_not_synchronise(lib):
+    # a long step queued on stream A; then the first call ever with a new table,
+    # on stream B, must return while A's work is still running (no device or
+    # host synchronisation inside the call), and its result must be right
+    import torch
+    nss = lib
+    dev = "cuda:0"
+    n_long = 8 * 4096 * 4096
+    long_tab = [(k * 4096 * 4096, 4096, 4096, 0) for k in range(8)]
+    hl = nss.hyper(ns_method="standard", ns_dtype="bf16", grad_dtype="bf16")
+    pl = torch.randn(n_long, device=dev)
+    gl = (torch.randn(n_long, device=dev) * 1e-3).to(torch.bfloat16)
+    ml = torch.zeros(n_long, device=dev)
+    wsl = torch.empty(nss.workspace_size(long_tab, hl), dtype=torch.uint8, device=dev)
+    wl, params, grads, mom = _inputs([(200, 328, 0), (96, 520, 24)], wid=179)
+    h = _hyper(nss, wl)
+    tab = wl.table()
+    p, g, m = (to_device(a.copy(), dev, torch) for a in (params, grads, mom))
+    ws = torch.empty(nss.workspace_size(tab, h), dtype=torch.uint8, device=dev)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    done = torch.cuda.Event()
+    torch.cuda.synchronize()
+    nss.release_plans()
+    for _ in range(4):                               # about 50 ms of work on A
+        nss.step(pl, gl, ml, long_tab, hl, ws=wsl, stream=sa)
+    done.record(sa)
+    nss.step(p, g, m, tab, h, ws=ws, stream=sb)      # first call with this table
+    still_running = not done.query()
+    torch.cuda.synchronize()
+    assert still_running, "the call waited for work queued on another stream"
+    pr, gr, mr = (to_device(a.copy(), dev, torch) for a in (params, grads, mom))
+    nss.step(pr, gr, mr, tab, h, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(p, pr) and torch.equal(m, mr)
