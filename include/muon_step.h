@@ -182,6 +182,21 @@ int muon_step(void* params, const void* grads, float* momentum, int64_t numel,
               void* workspace, size_t workspace_bytes,
               float* update_out, uint16_t* bf16_shadow, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): muon_step with its
+ * workspace taken from a device array inside the library, of
+ * MUON_NOALLOC_WORKSPACE_BYTES bytes, one per GPU the library runs on, held
+ * until the process ends. Arguments as in muon_step, without the workspace.
+ * It calls no allocating routine. A table whose muon_workspace_size() exceeds
+ * the array is refused with MUON_ERR_WORKSPACE before any device work. Every
+ * call on one GPU uses that GPU's one array, whose contents do not matter on
+ * entry: calls that may overlap on one GPU (other streams, other threads)
+ * race on it, so the caller must order them (one stream, or events). */
+#define MUON_NOALLOC_WORKSPACE_BYTES (64ull << 20)
+int muon_step_noalloc(void* params, const void* grads, float* momentum, int64_t numel,
+                      const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* h,
+                      float* update_out, uint16_t* bf16_shadow, void* stream);
+
 /* The part of one table entry that a parameter partition holds: elements
  * [lo, hi) of the matrix flattened in stored row-major order, found in the
  * partition from index param_offset on (element e at param_offset + e - lo).

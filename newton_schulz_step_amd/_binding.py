@@ -30,8 +30,9 @@ EXPORTED = (
     "muon_default_hyper", "muon_default_adamw_hyper", "muon_workspace_size", "muon_step",
     "muon_step_window", "adamw_step", "muon_pack", "muon_unpack", "muon_last_error", "muon_release_plans",
     "muon_profile_begin", "muon_profile_end", "muon_version", "muon_ns_flops",
-    "muon_plan_owners", "muon_comm_elements",
+    "muon_plan_owners", "muon_comm_elements", "muon_step_noalloc",
 )
+NOALLOC_WORKSPACE_BYTES = 64 << 20     # MUON_NOALLOC_WORKSPACE_BYTES
 
 
 class MuonError(RuntimeError):
@@ -118,6 +119,7 @@ def load() -> ctypes.CDLL:
         lib.muon_workspace_size.argtypes = [pm, i32, ctypes.POINTER(MuonHyper), ctypes.POINTER(sz)]
         lib.muon_step.argtypes = [vp, vp, vp, i64, pm, i32, ctypes.POINTER(MuonHyper), vp, sz,
                                   vp, vp, vp]
+        lib.muon_step_noalloc.argtypes = [vp, vp, vp, i64, pm, i32, ctypes.POINTER(MuonHyper), vp, vp, vp]
         lib.muon_step_window.argtypes = [vp, i64, vp, vp, i64, pm, ctypes.POINTER(MuonWindow), i32,
                                          ctypes.POINTER(MuonHyper), vp, sz, vp, vp, vp]
         lib.adamw_step.argtypes = [vp, vp, vp, vp, i64, ctypes.POINTER(AdamWHyper), vp]
@@ -132,7 +134,7 @@ def load() -> ctypes.CDLL:
         lib.muon_last_error.restype = ctypes.c_char_p
         lib.muon_version.restype = ctypes.c_char_p
         lib.muon_profile_end.argtypes = [ctypes.POINTER(KernelStat), i32, ctypes.POINTER(i32)]
-        for name in ("muon_workspace_size", "muon_step", "muon_step_window", "muon_plan_owners",
+        for name in ("muon_workspace_size", "muon_step", "muon_step_noalloc", "muon_step_window", "muon_plan_owners",
                      "adamw_step", "muon_pack", "muon_unpack",
                      "muon_release_plans", "muon_profile_begin", "muon_profile_end"):
             getattr(lib, name).restype = ctypes.c_int
@@ -301,6 +303,32 @@ def step(params, grads, momentum, entries, h: MuonHyper, ws=None, update_out=Non
         _check(load().muon_step(_ptr(params), _ptr(grads), _ptr(momentum), numel, arr, n,
                                 ctypes.byref(h), _ptr(ws), ws.numel() * ws.element_size(),
                                 _ptr(update_out), _ptr(bf16_shadow), _stream(params, stream)))
+
+
+def step_noalloc(params, grads, momentum, entries, h: MuonHyper, update_out=None,
+                 bf16_shadow=None, stream=None) -> None:
+    """One Muon step through muon_step_noalloc: no workspace argument, nothing
+    allocated (the library's per-GPU device array serves as the workspace)."""
+    torch = _torch()
+    if momentum.dtype != torch.float32:
+        raise TypeError("momentum must be float32")
+    if params.dtype not in (torch.float32, torch.bfloat16) or _dtype_code(params) != h.param_dtype:
+        raise TypeError("params must be float32 or bfloat16, matching hyper.param_dtype")
+    if _dtype_code(grads) != h.grad_dtype:
+        raise TypeError("grads dtype does not match hyper.grad_dtype")
+    numel = params.numel()
+    if grads.numel() != numel or momentum.numel() != numel:
+        raise ValueError("params, grads and momentum must have the same numel")
+    if update_out is not None and (update_out.dtype != torch.float32 or update_out.numel() != numel):
+        raise ValueError("update_out must be float32 with params' numel")
+    if bf16_shadow is not None and (bf16_shadow.element_size() != 2 or bf16_shadow.numel() != numel):
+        raise ValueError("bf16_shadow must be a 16-bit tensor with params' numel")
+    dev = _device(params, grads, momentum, update_out, bf16_shadow)
+    arr, n = table(entries)
+    with torch.cuda.device(dev):
+        _check(load().muon_step_noalloc(_ptr(params), _ptr(grads), _ptr(momentum), numel, arr, n,
+                                        ctypes.byref(h), _ptr(update_out), _ptr(bf16_shadow),
+                                        _stream(params, stream)))
 
 
 def windows(ws: Iterable[Sequence[int]], n: int):

@@ -490,12 +490,50 @@ int muon_workspace_size(const muon_matrix_t* table, int32_t n_entries, const muo
   return MUON_OK;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// muon_step_noalloc's workspace: a file-scope device array, one copy per GPU
+// (held until the process ends). Host code never uses the array's name as an
+// address: each device's copy is found once with hipGetSymbolAddress, with that
+// device current, and that pointer is what the kernels receive.
+
+namespace muon {
+
+static __device__ __align__(256) char scratch[MUON_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on it).
+static int scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MUON_ERR_HIP, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MUON_ERR_HIP, std::string("hipGetSymbolAddress of the step scratch failed: ") +
+                                    hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MUON_OK;
+}
+
+}  // namespace muon
+
+extern "C" {
+
 // The shared body of muon_step and muon_step_window. `windows` NULL: params and
 // the shadow share the table's layout (params_numel == numel).
 static int step_impl(void* params, int64_t params_numel, const void* grads, float* momentum, int64_t numel,
                      const muon_matrix_t* table, const muon_window_t* windows, int32_t n_entries,
                      const muon_hyper_t* h, void* workspace, size_t workspace_bytes, float* update_out,
-                     uint16_t* bf16_shadow, void* stream) {
+                     uint16_t* bf16_shadow, void* stream, bool use_scratch = false) {
   g_err.clear();
   std::string err;
   int st = validate(table, n_entries, h, err);
@@ -515,6 +553,16 @@ static int step_impl(void* params, int64_t params_numel, const void* grads, floa
   if (bf16_shadow && h->param_dtype == MUON_DTYPE_BF16)
     return fail(MUON_ERR_UNSUPPORTED, "bf16 params are their own bf16 copy: pass no bf16_shadow");
   if (n_entries == 0 || numel == 0) return MUON_OK;
+  if (use_scratch) {
+    // muon_step_noalloc: the library's device array, once the table is known to fit
+    const size_t need = build_layout(table, n_entries, h, windows).ws_bytes;
+    if (need > MUON_NOALLOC_WORKSPACE_BYTES)
+      return fail(MUON_ERR_WORKSPACE, "the table needs " + std::to_string(need) +
+                                          " bytes of workspace; muon_step_noalloc has " +
+                                          std::to_string(static_cast<size_t>(MUON_NOALLOC_WORKSPACE_BYTES)));
+    if ((st = scratch_for_current_device(&workspace)) != MUON_OK) return st;
+    workspace_bytes = MUON_NOALLOC_WORKSPACE_BYTES;
+  }
   if (workspace == nullptr) return fail(MUON_ERR_NULL, "workspace is NULL");
   if (misaligned(params, 16) || misaligned(grads, 16) || misaligned(momentum, 16) ||
       (update_out && misaligned(update_out, 16)) || (bf16_shadow && misaligned(bf16_shadow, 16)))
@@ -572,6 +620,13 @@ int muon_step(void* params, const void* grads, float* momentum, int64_t numel, c
               uint16_t* bf16_shadow, void* stream) {
   return step_impl(params, numel, grads, momentum, numel, table, nullptr, n_entries, h,
                    workspace, workspace_bytes, update_out, bf16_shadow, stream);
+}
+
+int muon_step_noalloc(void* params, const void* grads, float* momentum, int64_t numel, const muon_matrix_t* table,
+                      int32_t n_entries, const muon_hyper_t* h, float* update_out, uint16_t* bf16_shadow,
+                      void* stream) {
+  return step_impl(params, numel, grads, momentum, numel, table, nullptr, n_entries, h, nullptr, 0, update_out,
+                   bf16_shadow, stream, /*use_scratch=*/true);
 }
 
 int muon_step_window(float* partition, int64_t partition_numel, const void* grads, float* momentum, int64_t numel,

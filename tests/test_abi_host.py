@@ -146,6 +146,21 @@ def test_bf16_params_checks(lib):
     assert st == nss.ERR_UNSUPPORTED
 
 
+def test_noalloc_refuses_before_any_device_work(lib):
+    # a table whose workspace exceeds the library's array is refused on the host
+    h = nss.hyper(ns_method="standard", ns_dtype="bf16")
+    ent = [(0, 4096, 4096, 0)]
+    assert nss.workspace_size(ent, h) > nss.NOALLOC_WORKSPACE_BYTES
+    arr, n = nss.table(ent)
+    st = lib.muon_step_noalloc(FAKE, FAKE + (1 << 36), FAKE + (2 << 36), 4096 * 4096, arr, n,
+                               ctypes.byref(h), None, None, None)
+    assert st == nss.ERR_WORKSPACE and "muon_step_noalloc" in lib.muon_last_error().decode()
+    arr, n = nss.table([(0, 64, 64, 0)])
+    st = lib.muon_step_noalloc(FAKE, FAKE + (1 << 36), FAKE + (2 << 36), 4095, arr, n,
+                               ctypes.byref(h), None, None, None)
+    assert st == nss.ERR_RANGE
+
+
 def _raw_window(lib, entries, wins, numel, pnumel, h, part=FAKE + (4 << 36), grads=FAKE + (1 << 36),
                 mom=FAKE + (2 << 36), ws=FAKE + (3 << 36), upd=None, shadow=None, null_windows=False):
     arr, n = nss.table(entries)
