@@ -4,18 +4,20 @@
 A step is one muon_step call over a whole packed buffer of Muon-target
 matrices: momentum, Frobenius normalisation, five Newton-Schulz iterations per
 matrix, weight decay and the lr-scaled update, all in libmuonstep's kernels.
-The default workload is an owner's packed buffer at 1/8 share of a 7B-class
+The headline workload is an owner's packed buffer at 1/8 share of a 7B-class
 model (16 x 4096x4096, 8 x 11008x4096, 4 x 4096x11008; bf16 gradients, fp32
 params and momentum) with the standard quintic in bf16.
 
-Prints one JSON line: Muon-target elements per second (whole job), the
-per-step time, the roofline of the dominant kernel (the Newton-Schulz update
-GEMM, timed per launch with HIP events on its stream over the timed region),
-NS TFLOP/s against the bf16 dense MFMA peak, and the CPU oracle timed on a
-bounded sample of the same workload.
+Prints one JSON line: Muon-target elements per second (whole job) of the
+headline workload, the per-step time, the roofline of the dominant kernel (the
+Newton-Schulz update GEMM, timed per launch with HIP events on its stream over
+the timed region), NS TFLOP/s against the bf16 dense MFMA peak, the CPU oracle
+timed on a bounded sample of the same workload, and under "configs" every
+workload (tiny fp32, one layer, owner share, MoE experts, per-head split) with
+both methods, plus Gram-vs-standard step times per shape group.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload 3]
-                    [--method standard|gram] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--no-cpu-baseline]
+    python bench.py --workload 3 --method standard|gram [...]   # one workload only
     python bench.py --copy-calibration   # plain copy of known size (counter scale)
 """
 from __future__ import annotations
@@ -44,6 +46,16 @@ def ns_flops(m: int, n: int, method: str) -> float:
     if method == "standard":
         return 20.0 * m * m * n + 10.0 * m ** 3
     return 4.0 * m * m * n + 34.0 * m ** 3
+
+
+def ns_flops_min(m: int, n: int, method: str) -> float:
+    """Newton-Schulz FLOPs of one problem with every symmetric product counted once
+    per lower-triangle entry (the least MFMA work the method needs): standard
+    5 x (m^2 n + m^3 + 2 m^2 n); gram m^2 n (R0) + 5 x m^3 (Q) + 4 x 2 m^3 (P)
+    + 4 x (m^3 + m^3) (T = R Q and R <- Q T) + 2 m^2 n (P X0)."""
+    if method == "standard":
+        return 15.0 * m * m * n + 5.0 * m ** 3
+    return 3.0 * m * m * n + 21.0 * m ** 3
 
 
 def problems(wl):
@@ -304,32 +316,189 @@ def adamw_pass(wl, steps: int = 10) -> dict:
             "frac_of_hbm": gbs / HBM_PEAK_GBS}
 
 
+def workload_hyper(nss, wl, method):
+    ns_dtype = "f32" if wl.ns_dtype == "f32" else ("bf16" if method == "standard" else "f16")
+    h = nss.hyper(ns_method=method, ns_dtype=ns_dtype, grad_dtype=wl.grad_dtype, lr=wl.lr,
+                  momentum=wl.momentum, weight_decay=wl.weight_decay)
+    return h, ns_dtype
+
+
+def timed_steps(nss, bufs, tab, h, ws, steps, warmup):
+    """`warmup` untimed steps, then `steps` timed ones between device
+    synchronisations, with the library's per-launch events on. Returns (elapsed
+    seconds, {kernel kind: (launches, summed ms)})."""
+    import torch
+    params, grads, mom = bufs
+    for _ in range(warmup):
+        nss.step(params, grads, mom, tab, h, ws=ws)
+    torch.cuda.synchronize()
+    nss.profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        nss.step(params, grads, mom, tab, h, ws=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return elapsed, nss.profile_end()
+
+
+def dominant_roofline(wl, method, ns_dtype, h, kstats, steps):
+    """Roofline of the step's dominant kernel, from its summed launch time.
+
+    Standard: the update GEMM B X (+ a X), algorithmic 2 m^2 n per problem per
+    launch; on 128-row problems in 16-bit the update and the next X X^T are one
+    pass (ns_update_gram), bound by memory: algorithmic bytes per problem per
+    launch are X read and X' written (2 m n elements) plus B read and A' written
+    (2 m^2 elements). Gram: its symmetric GEMM family (R0, five Q, four T = R Q,
+    four R <- Q T), counting the lower tiles these launches compute: m^2 n + 13 m^3
+    per problem."""
+    probs = problems(wl)
+    peak = FP32_PEAK_TFLOPS if ns_dtype == "f32" else BF16_PEAK_TFLOPS
+    bound, unit, roof_peak = "mfma", "TFLOP/s", peak
+    if method == "standard" and kstats.get("ns_update_gram", (0, 0.0))[1] > \
+            kstats.get("ns_gemm_update", (0, 0.0))[1]:
+        dom_kind = "ns_update_gram"
+        dt_name = {"bf16": "__bf16", "f16": "_Float16"}[ns_dtype]
+        dom_kernel = f"muon::ns_update_gram<{dt_name}>"
+        launches, dom_ms = kstats[dom_kind]
+        dom_work = sum(2 * (2.0 * m * n + 2.0 * m * m) for m, n in probs if m <= 128) * \
+            (h.ns_steps - 1) * steps
+        bound, unit, roof_peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = dom_work / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else None
+    elif method == "standard":
+        dom_kind = "ns_gemm_update"
+        tile = 256 if probs and probs[0][0] >= 512 else 128
+        dt_name = {"bf16": "__bf16", "f16": "_Float16", "f32": "float"}[ns_dtype]
+        dom_kernel = f"muon::ns_gemm<{dt_name}, {tile}, false, 0, true>"
+        launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
+        dom_flops = sum(2.0 * m * m * n for m, n in probs) * (h.ns_steps - 1) * steps
+        achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
+    else:
+        dom_kind = "gram_gemm_sym"
+        tile = 256 if probs and probs[0][0] >= 512 else 128
+        dom_kernel = f"muon::ns_gemm<{'_Float16' if ns_dtype == 'f16' else 'float'}, {tile}, true, 0, false>"
+        launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
+        dom_flops = sum(1.0 * m * m * n + 13.0 * m ** 3 for m, n in probs) * steps
+        achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
+    return {"bound": bound, "kernel": dom_kernel, "kind": dom_kind, "launches": launches,
+            "avg_launch_ms": dom_ms / launches if launches else None,
+            "achieved": achieved, "peak": roof_peak, "unit": unit,
+            "frac": achieved / roof_peak if achieved else None}
+
+
+def step_summary(wl, method, ns_dtype, elapsed, kstats, steps):
+    """Per-step figures of one timed run over a whole workload (or a sub-table):
+    Muon elements/s; NS TFLOP/s over the summed NS kernel time, both with the
+    nominal FLOPs and with symmetric products counted once; the step's
+    algorithmic bandwidth (18 B per element for 16-bit gradients, 20 B for fp32:
+    gradient read, momentum and params read and written); and the step's
+    fraction of its roofline: the larger of the ideal MFMA time (least FLOPs at
+    the dense peak) and the ideal HBM time (algorithmic bytes at 8 TB/s), over
+    the measured step time."""
+    probs = problems(wl)
+    elems = sum(m * n for m, n in probs)
+    step_s = elapsed / steps
+    ns_kinds = [k for k in kstats if k.startswith(("ns_gemm", "gram_gemm", "ns_update_gram"))]
+    ns_ms = sum(kstats[k][1] for k in ns_kinds) / steps
+    nominal = sum(ns_flops(m, n, method) for m, n in probs)
+    least = sum(ns_flops_min(m, n, method) for m, n in probs)
+    peak = FP32_PEAK_TFLOPS if ns_dtype == "f32" else BF16_PEAK_TFLOPS
+    bpe = 20.0 if wl.grad_dtype == "f32" else 18.0
+    t_mfma = least / (peak * 1e12)
+    t_hbm = elems * bpe / (HBM_PEAK_GBS * 1e9)
+    return {
+        "ms_per_step": step_s * 1e3, "elements_per_s": elems / step_s, "muon_elements": elems,
+        "ns_ms_per_step": ns_ms,
+        "ns_tflops_nominal": nominal / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None,
+        "ns_tflops_least": least / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None,
+        "ns_least_frac_of_peak": least / (ns_ms * 1e-3) / 1e12 / peak if ns_ms > 0 else None,
+        "step_algorithmic_gbs": elems * bpe / step_s / 1e9,
+        "step_bound": "mfma" if t_mfma >= t_hbm else "hbm",
+        "step_roofline_frac": max(t_mfma, t_hbm) / step_s,
+        "kernels_ms_per_step": {k: round(v[1] / steps, 4) for k, v in kstats.items()},
+    }
+
+
+def group_key(e):
+    pr = e.split_rows or e.rows
+    return (min(pr, e.cols), max(pr, e.cols))
+
+
+def measure_workload(nss, wid, steps, warmup, groups=True):
+    """Both methods over the whole workload, then each shape group alone with both
+    methods (the pages say Gram NS is about twice as fast on rectangular
+    matrices). Inputs are drawn on the device once and shared by all runs (the
+    cost does not depend on the values)."""
+    import torch
+    import workloads as W
+    dev = torch.device("cuda:0")
+    wl = W.workload(wid)
+    bufs = device_inputs(wl, dev)
+    tab = wl.table()
+    hs = {m: workload_hyper(nss, wl, m) for m in ("standard", "gram")}
+    ws = nss.workspace(max(nss.workspace_size(tab, h) for h, _ in hs.values()), dev)
+    out = {"workload": wl.title, "muon_elements": wl.muon_elements}
+    for method, (h, ns_dtype) in hs.items():
+        elapsed, kstats = timed_steps(nss, bufs, tab, h, ws, steps, warmup)
+        row = step_summary(wl, method, ns_dtype, elapsed, kstats, steps)
+        row["ns_dtype"] = ns_dtype
+        row["dominant_kernel"] = dominant_roofline(wl, method, ns_dtype, h, kstats, steps)
+        out[method] = row
+    if groups:
+        keys = []
+        for e in wl.entries:
+            if group_key(e) not in keys:
+                keys.append(group_key(e))
+        rows = []
+        for key in keys:
+            idx = [i for i, e in enumerate(wl.entries) if group_key(e) == key]
+            sub = [tab[i] for i in idx]
+            sub_wl = W.Workload(wl.wid, wl.title, tuple(wl.entries[i] for i in idx), wl.grad_dtype,
+                                wl.ns_dtype, wl.lr, wl.momentum, wl.weight_decay)
+            r = {"m": key[0], "n": key[1], "problems": len(problems(sub_wl))}
+            for method, (h, ns_dtype) in hs.items():
+                elapsed, kstats = timed_steps(nss, bufs, sub, h, ws, steps, 1)
+                r[method + "_ms"] = elapsed * 1e3 / steps
+                r[method + "_ns_ms"] = step_summary(sub_wl, method, ns_dtype, elapsed, kstats,
+                                                    steps)["ns_ms_per_step"]
+            r["standard_over_gram"] = r["standard_ms"] / r["gram_ms"]
+            r["flops_standard_over_gram"] = ns_flops(key[0], key[1], "standard") / ns_flops(key[0], key[1], "gram")
+            rows.append(r)
+        out["shape_groups"] = rows
+    del bufs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=None,
+                    help="time this workload only (default: the owner share, then every workload)")
     ap.add_argument("--method", default="standard", choices=["standard", "gram"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                               "FETCH_COPY_CSV", "WRITE_COPY_CSV"))
     ap.add_argument("--summarize-mfma", metavar="MFMA_CSV")
     args = ap.parse_args()
+    workload = args.workload if args.workload is not None else 3
     if args.summarize_mfma:
         symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0ELb1EEEvNS_9GemmBatchE" if args.method == "standard"
                   else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0ELb0EEEvNS_9GemmBatchE")
         rec = summarize_mfma(args.summarize_mfma, symbol)
-        run = (f"python3 $REPO/bench.py --workload {args.workload} --method {args.method} "
+        run = (f"python3 $REPO/bench.py --workload {workload} --method {args.method} "
                "--steps 2 --warmup 1 --no-cpu-baseline")
         rec["commands"] = [
             "cd /tmp && export TMPDIR=/tmp",
             f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -d <mfma> -o run --output-format csv -- {run}",
-            f"python3 bench.py --workload {args.workload} --method {args.method} "
+            f"python3 bench.py --workload {workload} --method {args.method} "
             "--summarize-mfma <mfma>/run_counter_collection.csv",
         ]
-        path = os.path.join(ROOT, "profiles", f"mfma_ns_gemm_update_{WORKLOAD_SLUG[args.workload]}_{args.method}.json")
+        path = os.path.join(ROOT, "profiles", f"mfma_ns_gemm_update_{WORKLOAD_SLUG[workload]}_{args.method}.json")
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
@@ -339,8 +508,8 @@ def main() -> int:
         symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0ELb1EEEvNS_9GemmBatchE" if ns_dtype == "bf16"
                   else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0ELb0EEEvNS_9GemmBatchE")
         rec = summarize_counters(*args.summarize_counters, copy_bytes=1 << 32, symbol=symbol,
-                                 workload=args.workload, method=args.method)
-        with open(traffic_path(args.workload, args.method), "w") as f:
+                                 workload=workload, method=args.method)
+        with open(traffic_path(workload, args.method), "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
         return 0
@@ -361,29 +530,13 @@ def main() -> int:
         print(json.dumps(copy_calibration()), flush=True)
         return 0
     dev = torch.device("cuda:0")
-    wl = W.workload(args.workload)
-    ns_dtype = "bf16" if args.method == "standard" else "f16"
-    if wl.ns_dtype == "f32":
-        ns_dtype = "f32"
-    h = nss.hyper(ns_method=args.method, ns_dtype=ns_dtype, grad_dtype=wl.grad_dtype, lr=wl.lr,
-                  momentum=wl.momentum, weight_decay=wl.weight_decay)
+    wl = W.workload(workload)
+    h, ns_dtype = workload_hyper(nss, wl, args.method)
     tab = wl.table()
-    params, grads, mom = device_inputs(wl, dev)
+    bufs = device_inputs(wl, dev)
     ws = nss.workspace(nss.workspace_size(tab, h), dev)
     torch.cuda.synchronize()
-
-    for _ in range(args.warmup):
-        nss.step(params, grads, mom, tab, h, ws=ws)
-    torch.cuda.synchronize()
-
-    nss.profile_begin()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        nss.step(params, grads, mom, tab, h, ws=ws)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kstats = nss.profile_end()
+    elapsed, kstats = timed_steps(nss, bufs, tab, h, ws, args.steps, args.warmup)
 
     probs = problems(wl)
     elems = wl.muon_elements
@@ -392,44 +545,11 @@ def main() -> int:
     ns_kinds = [k for k in kstats if k.startswith(("ns_gemm", "gram_gemm"))]
     ns_ms = sum(kstats[k][1] for k in ns_kinds)
     peak = FP32_PEAK_TFLOPS if ns_dtype == "f32" else BF16_PEAK_TFLOPS
-
-    # dominant kernel: the standard update GEMM B X (+ a X); algorithmic 2 m^2 n per
-    # problem per launch. On 128-row problems in 16-bit the update and the next
-    # X X^T are one pass (ns_update_gram), bound by memory: algorithmic bytes per
-    # problem per launch are X read and X' written (2 m n elements) plus B read and
-    # A' written (2 m^2 elements). Gram: its symmetric GEMM family (nominal FLOPs).
-    bound, unit, roof_peak = "mfma", "TFLOP/s", peak
-    if args.method == "standard" and kstats.get("ns_update_gram", (0, 0.0))[1] > \
-            kstats.get("ns_gemm_update", (0, 0.0))[1]:
-        dom_kind = "ns_update_gram"
-        dt_name = {"bf16": "__bf16", "f16": "_Float16"}[ns_dtype]
-        dom_kernel = f"muon::ns_update_gram<{dt_name}>"
-        launches, dom_ms = kstats[dom_kind]
-        esz = 2
-        dom_work = sum(esz * (2.0 * m * n + 2.0 * m * m) for m, n in probs if m <= 128) * \
-            (h.ns_steps - 1) * args.steps
-        bound, unit, roof_peak = "hbm", "GB/s", HBM_PEAK_GBS
-        achieved = dom_work / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else None
-    elif args.method == "standard":
-        dom_kind = "ns_gemm_update"
-        tile = 256 if probs and probs[0][0] >= 512 else 128
-        dt_name = {"bf16": "__bf16", "f16": "_Float16", "f32": "float"}[ns_dtype]
-        dom_kernel = f"muon::ns_gemm<{dt_name}, {tile}, false, 0, true>"
-        launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
-        dom_flops = sum(2.0 * m * m * n for m, n in probs) * (h.ns_steps - 1) * args.steps
-        achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
-    else:
-        # symmetric launches: R0 = X0 X0^T, five Q = aI + bR + cRR, four T = R Q and
-        # four R <- Q T
-        dom_kind = "gram_gemm_sym"
-        tile = 256 if probs and probs[0][0] >= 512 else 128
-        dom_kernel = f"muon::ns_gemm<{'_Float16' if ns_dtype == 'f16' else 'float'}, {tile}, true, 0, false>"
-        launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
-        dom_flops = sum(2.0 * m * m * n + 26.0 * m ** 3 for m, n in probs) * args.steps
-        achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
-    traffic = measured_traffic(dom_kernel, args.workload, args.method)
+    roof = dominant_roofline(wl, args.method, ns_dtype, h, kstats, args.steps)
+    roof["traffic"] = measured_traffic(roof["kernel"], workload, args.method)
     mom_launches, mom_ms = kstats.get("momentum_sumsq", (0, 0.0))
     gbytes = elems * (10 if wl.grad_dtype != "f32" else 12) * args.steps / 1e9
+    summary = step_summary(wl, args.method, ns_dtype, elapsed, kstats, args.steps)
 
     out = {
         "metric": METRIC,
@@ -455,24 +575,30 @@ def main() -> int:
         },
         "ns_tflops": ns_total / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None,
         "ns_frac_of_peak": (ns_total / (ns_ms * 1e-3) / 1e12 / peak) if ns_ms > 0 else None,
-        "roofline": {
-            "bound": bound, "kernel": dom_kernel, "launches": launches,
-            "avg_launch_ms": dom_ms / launches if launches else None,
-            "achieved": achieved, "peak": roof_peak, "unit": unit,
-            "frac": achieved / roof_peak if achieved else None,
-            "traffic": traffic,
-        },
+        "ns_tflops_least": summary["ns_tflops_least"],
+        "ns_least_frac_of_peak": summary["ns_least_frac_of_peak"],
+        "step_roofline_frac": summary["step_roofline_frac"],
+        "roofline": {k: roof[k] for k in ("bound", "kernel", "launches", "avg_launch_ms", "achieved",
+                                           "peak", "unit", "frac", "traffic")},
         "momentum_pass": {
             "launches": mom_launches,
             "gbs": gbytes / (mom_ms * 1e-3) if mom_ms > 0 else None,
             "frac_of_hbm": gbytes / (mom_ms * 1e-3) / HBM_PEAK_GBS if mom_ms > 0 else None,
         },
-        "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kstats.items()},
+        "kernels_ms_per_step": summary["kernels_ms_per_step"],
     }
-    del params, grads, mom, ws
+    del bufs, ws
     torch.cuda.empty_cache()
     out["adamw_pass"] = adamw_pass(W.workload(5))
     out["adamw_pass"]["workload"] = "32000x4096 embedding + 65 vectors of 4096 (per-head workload's AdamW part)"
+    if args.workload is None and not args.no_configs:
+        csteps = max(3, min(args.steps, 10))
+        out["configs"] = {}
+        for wid in (1, 2, 3, 4, 5):
+            t0 = time.perf_counter()
+            out["configs"][WORKLOAD_SLUG[wid]] = measure_workload(nss, wid, csteps, 1)
+            print(f"[bench] workload {wid} measured in {time.perf_counter() - t0:.1f} s",
+                  file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.method)
     print(json.dumps(out), flush=True)
