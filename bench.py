@@ -351,7 +351,9 @@ def dominant_roofline(wl, method, ns_dtype, h, kstats, steps):
     launch are X read and X' written (2 m n elements) plus B read and A' written
     (2 m^2 elements). Gram: its symmetric GEMM family (R0, five Q, four T = R Q,
     four R <- Q T), counting the lower tiles these launches compute: m^2 n + 13 m^3
-    per problem."""
+    per problem; on 128-row problems in fp16, where the chain runs in LDS, the
+    apply X = P X0, bound by memory: X0 read (2 m n bytes), params read and
+    written (8 m n)."""
     probs = problems(wl)
     peak = FP32_PEAK_TFLOPS if ns_dtype == "f32" else BF16_PEAK_TFLOPS
     bound, unit, roof_peak = "mfma", "TFLOP/s", peak
@@ -373,6 +375,15 @@ def dominant_roofline(wl, method, ns_dtype, h, kstats, steps):
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
         dom_flops = sum(2.0 * m * m * n for m, n in probs) * (h.ns_steps - 1) * steps
         achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
+    elif kstats.get("gram_gemm_apply", (0, 0.0))[1] > kstats.get("gram_gemm_sym", (0, 0.0))[1]:
+        # 128-row problems in fp16 (the chain runs in LDS): the apply X = P X0,
+        # bound by memory: X0 read, fp32 params read and written
+        dom_kind = "gram_gemm_apply"
+        dom_kernel = "muon::ns_gemm<_Float16, 128, false, 1, true>"
+        launches, dom_ms = kstats[dom_kind]
+        dom_work = sum(2.0 * m * n + 8.0 * m * n for m, n in probs if m <= 128) * steps
+        bound, unit, roof_peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = dom_work / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else None
     else:
         dom_kind = "gram_gemm_sym"
         tile = 256 if probs and probs[0][0] >= 512 else 128

@@ -358,8 +358,36 @@ static int run_gram(const StepCtx& c, const GroupSet& set) {
 
   std::vector<GemmArgs> v;
   if (fused) {
-    for (const Group* G : set)
-      if ((st = run_prep_gram(c, *G, R(*G, 0), scale(*G))) != MUON_OK) return st;
+    // X0 and R0 in one pass; then the whole chain in one launch, with the small
+    // matrices in LDS (the same products and roundings as the launches below);
+    // then X = P X0 with the apply fused, as below
+    GramChainBatch b{};
+    b.n = static_cast<int32_t>(set.size());
+    for (size_t gi = 0; gi < set.size(); ++gi) {
+      const Group& G = *set[gi];
+      if ((st = run_prep_gram(c, G, R(G, 0), scale(G))) != MUON_OK) return st;
+      const float s = scale(G);
+      GramChainArgs& x = b.g[gi];
+      x.R0 = R(G, 0);
+      x.r_ps = G.mp * G.mp;
+      x.P = Pb(G, 0);
+      x.p_ps = G.mp * G.mp;
+      x.qa = c.h->ns_a;
+      x.qb = c.h->ns_b / s;
+      x.qc = c.h->ns_c / (s * s);
+      x.steps = S;
+      x.count = G.count;
+      b.start[gi + 1] = b.start[gi] + G.count;
+    }
+    MUON_LAUNCH("gram_chain", c.s, launch_gram_chain(dt, b, c.s));
+    for (const Group* Gp : set) {
+      const Group& G = *Gp;
+      GemmArgs ga = apply_args(c, G);
+      set_full(ga, G, Pb(G, 0), G.mp * G.mp, G.mp, ws + G.x[0], G.mp * G.np, G.np, kext(G.m, dt), G.mp, G.np);
+      ga.alpha = 1.0f;
+      v.push_back(ga);
+    }
+    return launch_batch("gram_gemm_apply", c, tile, false, apply_epi(c), v);
   } else {
     for (const Group* G : set)
       if ((st = run_prep(c, *G)) != MUON_OK) return st;

@@ -988,6 +988,235 @@ hipError_t launch_update_gram(int dtype, const GemmBatch& b, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Single-tile-row groups (m <= 128, fp16), Gram method: the chain on the small
+// matrices, one workgroup per problem.
+//
+// R, Q, T and P (128 x 128 fp16, 32 KiB each) stay in LDS for every step, each
+// as two K planes of 128-byte rows, 16-byte chunks XOR-swizzled by the row (the
+// layout the MFMA operand reads of the other kernels use). Every product is
+// NT: R, Q and T are stored symmetric, so a row is also a column, and P is kept
+// transposed (rows of P^T) while it is the right operand of Q P; the last P is
+// stored as is, the left operand of P X0. Each product runs the MFMAs of the
+// 128-tile launch in the same k order and finishes with the same epilogue
+// arithmetic, then stores straight from the accumulators: a lane holds four
+// consecutive rows of one column, one 8-byte write of the transposed position,
+// plus 2-byte writes where the row-major position is needed (the mirror of a
+// symmetric result, and the last P), which is then copied out row-major for the
+// apply launch. (Fused here, the apply streamed X0 and the parameters from one
+// workgroup per CU, about 40% slower than its own launch with two.)
+template <typename T>
+__global__ __launch_bounds__(256) void gram_chain_kernel(GramChainBatch batch) {
+  using Gm = Geo<T, 128>;
+  static_assert(sizeof(T) == 2, "16-bit iterates only");
+  constexpr int WB = Gm::WB, HALF = Gm::HALF;                 // 2, 64
+  constexpr int PL = 128 * 128;                               // bytes of one K plane
+  constexpr int MAT = 2 * PL;                                 // bytes of one matrix
+  __shared__ __attribute__((aligned(1024))) char L[4 * MAT];
+  char* const Rm = L;
+  char* const Qm = L + MAT;
+  char* const Tm = L + 2 * MAT;
+  char* const Pm = L + 3 * MAT;
+
+  const int bid = static_cast<int>(blockIdx.x);
+  int g = 0;
+#pragma unroll
+  for (int q = 1; q < kBatchGroups; ++q)
+    if (q < batch.n && bid >= batch.start[q]) g = q;
+  const GramChainArgs& a = batch.g[g];
+  const int prob = bid - batch.start[g];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  using V = typename Gm::V;
+
+  // byte offset of element (r, k) of a matrix held as K planes
+  auto at = [](int r, int k) { return (k >> 6) * PL + r * 128 + ((((k & 63) >> 3) ^ swz(r)) << 4) + (k & 7) * 2; };
+
+  // ---- R0 (row-major, pitch 128) into R
+  {
+    const char* Rg = static_cast<const char*>(a.R0) + static_cast<int64_t>(prob) * a.r_ps * 2;
+    u16x8 rb[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int id = v * 256 + tid, r = id >> 4, c = id & 15;
+      rb[v] = *reinterpret_cast<const u16x8*>(Rg + r * 256 + c * 16);
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int id = v * 256 + tid, r = id >> 4, c = id & 15;
+      *reinterpret_cast<u16x8*>(Rm + (c >> 3) * PL + r * 128 + (((c & 7) ^ swz(r)) << 4)) = rb[v];
+    }
+  }
+
+  int aoff[WB][4], boff[WB][4];
+#pragma unroll
+  for (int i = 0; i < WB; ++i) {
+    const int ra = wm * HALF + i * 32 + (lane & 31);
+    const int rb = wn * HALF + i * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      aoff[i][ks] = ra * 128 + ((c ^ swz(ra)) << 4);
+      boff[i][ks] = rb * 128 + ((c ^ swz(rb)) << 4);
+    }
+  }
+
+  f32x16 acc[WB][WB];
+  // acc = A B^T over K = 128: A and B rows from LDS planes, k in increasing order
+  auto product = [&](const char* A, const char* B) {
+#pragma unroll
+    for (int i = 0; i < WB; ++i)
+#pragma unroll
+      for (int j = 0; j < WB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        V xa[WB], xb[WB];
+#pragma unroll
+        for (int i = 0; i < WB; ++i) xa[i] = *reinterpret_cast<const V*>(A + pl * PL + aoff[i][ks]);
+#pragma unroll
+        for (int j = 0; j < WB; ++j) xb[j] = *reinterpret_cast<const V*>(B + pl * PL + boff[j][ks]);
+#pragma unroll
+        for (int i = 0; i < WB; ++i)
+#pragma unroll
+          for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);        // one k step per scheduling region
+      }
+  };
+  // accumulator element (block i, j; register q * 4 + e) is row row0 + e, column
+  // col. The stores take the lane index through an opaque copy made per call:
+  // their many LDS addresses do not depend on the step, and hoisted out of the
+  // step loop they would all stay live at once.
+  auto opaque_lane = [&]() {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+  auto row0_of = [&](int ln, int i, int q) { return wm * HALF + i * 32 + q * 8 + (ln >> 5) * 4; };
+  auto col_of = [&](int ln, int j) { return wn * HALF + j * 32 + (ln & 31); };
+
+  // symmetric store of v = alpha acc + beta D + gamma I (D symmetric or none), as
+  // the symmetric launch stores it: the lower triangle (row >= column) of the
+  // accumulators, rounded, at its place and mirrored
+  auto store_sym = [&](char* dst, float alpha, float beta, const char* D, float gamma) {
+    const int ln = opaque_lane();
+#pragma unroll
+    for (int i = 0; i < WB; ++i)
+#pragma unroll
+      for (int j = 0; j < WB; ++j) {
+        const int col = col_of(ln, j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row0 = row0_of(ln, i, q);
+          if (row0 + 3 < col) continue;                      // upper part: not stored
+          float v[4];
+          u16x4 dv;
+          if (D != nullptr) dv = *reinterpret_cast<const u16x4*>(D + at(col, row0));   // D[row][col] = D[col][row]
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = alpha * acc[i][j][q * 4 + e];
+            if (D != nullptr) v[e] = __builtin_fmaf(beta, static_cast<float>(__builtin_bit_cast(T, (unsigned short)dv[e])), v[e]);
+            if (gamma != 0.0f && row0 + e == col) v[e] += gamma;
+          }
+          u16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[e])));
+          if (row0 >= col) {
+            *reinterpret_cast<u16x4*>(dst + at(col, row0)) = o;          // (col, row0 + e): mirror
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (row0 + e > col) *reinterpret_cast<unsigned short*>(dst + at(row0 + e, col)) = o[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (row0 + e >= col) {
+                *reinterpret_cast<unsigned short*>(dst + at(col, row0 + e)) = o[e];
+                if (row0 + e > col) *reinterpret_cast<unsigned short*>(dst + at(row0 + e, col)) = o[e];
+              }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  // full store of the rounded accumulators: transposed (row col holds column
+  // col) or as is
+  auto store_full = [&](char* dst, bool transposed) {
+    const int ln = opaque_lane();
+#pragma unroll
+    for (int i = 0; i < WB; ++i)
+#pragma unroll
+      for (int j = 0; j < WB; ++j) {
+        const int col = col_of(ln, j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row0 = row0_of(ln, i, q);
+          u16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(1.0f * acc[i][j][q * 4 + e])));
+          if (transposed) {
+            *reinterpret_cast<u16x4*>(dst + at(col, row0)) = o;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<unsigned short*>(dst + at(row0 + e, col)) = o[e];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
+  __syncthreads();                                 // R0 in LDS
+  const int S = a.steps;
+  for (int k = 0; k < S; ++k) {
+    product(Rm, Rm);                               // Q = qa I + qb R + qc R R
+    store_sym(Qm, a.qc, a.qb, Rm, a.qa);
+    if (k == 0) store_sym(Pm, a.qc, a.qb, Rm, a.qa);   // P = Q (symmetric: also P^T)
+    __syncthreads();
+    if (k > 0) {                                   // P <- Q P, P^T as the right operand
+      product(Qm, Pm);
+      __syncthreads();                             // every read of the old P done
+      store_full(Pm, k < S - 1);
+    }
+    if (k < S - 1) {
+      product(Rm, Qm);                             // T = R Q (Q symmetric)
+      store_sym(Tm, 1.0f, 0.0f, nullptr, 0.0f);
+      __syncthreads();
+      product(Qm, Tm);                             // R <- Q T (T symmetric); R is not read here
+      store_sym(Rm, 1.0f, 0.0f, nullptr, 0.0f);
+    }
+    __syncthreads();
+  }
+
+  // ---- the final P (row-major in LDS) out, row-major with pitch 128
+  {
+    char* Pg = static_cast<char*>(a.P) + static_cast<int64_t>(prob) * a.p_ps * 2;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int id = v * 256 + tid, r = id >> 4, c = id & 15;
+      *reinterpret_cast<u16x8*>(Pg + r * 256 + c * 16) =
+          *reinterpret_cast<const u16x8*>(Pm + (c >> 3) * PL + r * 128 + (((c & 7) ^ swz(r)) << 4));
+    }
+  }
+}
+
+hipError_t launch_gram_chain(int dtype, const GramChainBatch& b, hipStream_t s) {
+  if (b.n < 1 || b.n > kBatchGroups || b.start[0] != 0) return hipErrorInvalidValue;
+  for (int g = 0; g < b.n; ++g) {
+    const GramChainArgs& a = b.g[g];
+    if (a.steps < 1 || a.count < 0 || b.start[g + 1] - b.start[g] != a.count) return hipErrorInvalidValue;
+  }
+  if (b.start[b.n] <= 0) return hipSuccess;
+  if (dtype != MUON_DTYPE_F16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gram_chain_kernel<_Float16>, dim3(b.start[b.n]), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Single-tile-row groups (m <= 128, 16-bit iterates): X0 and its Gram matrix
 // R = alpha X0 X0^T in one pass.
 //

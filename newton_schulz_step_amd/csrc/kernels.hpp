@@ -56,6 +56,27 @@ hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmBatc
 // total_tiles = number of problems.
 hipError_t launch_update_gram(int dtype, const GemmBatch& b, hipStream_t s);
 
+// Single-tile-row groups (mp = 128, fp16), Gram method: the whole chain
+//   Q = qa I + qb R + qc R R;  P <- Q P (P = Q first);  T = R Q, R <- Q T
+// (stored symmetric, as the symmetric launches store them) for `steps` steps,
+// one workgroup per problem with R, Q, T and P held in LDS; the final P is
+// written row-major (pitch 128, p_ps elements apart) for the apply launch.
+// R0 (r_ps apart, pitch 128) is as the prep pass wrote it. Every product and
+// rounding matches the separate launches, so P is bit-identical to theirs.
+struct GramChainArgs {
+  const void* R0; int64_t r_ps;
+  void* P; int64_t p_ps;
+  float qa, qb, qc;
+  int32_t steps;
+  int32_t count;
+};
+struct GramChainBatch {
+  GramChainArgs g[kBatchGroups];
+  int32_t start[kBatchGroups + 1];
+  int32_t n;
+};
+hipError_t launch_gram_chain(int dtype, const GramChainBatch& b, hipStream_t s);
+
 // Single-tile-row groups (mp = 128, bf16/fp16): X0 = round(M * inv_norm) as the
 // X0 kernel writes it, and R = alpha X0 X0^T (stored symmetric) as the symmetric
 // launch computes it, in one pass; one block per problem.

@@ -208,6 +208,10 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
       G.x[1] = off; off = align256(off + xbytes);
       G.a = off; off = align256(off + sbytes);
       G.b = off; off = align256(off + sbytes);
+    } else if (G.mp == G.tile && h->ns_dtype != MUON_DTYPE_F32) {
+      // single tile row in 16-bit: the chain runs in LDS; R0 and the final P
+      G.a = off; off = align256(off + sbytes);      // R0
+      G.p[0] = off; off = align256(off + sbytes);   // P
     } else {
       G.a = off; off = align256(off + sbytes);      // R
       G.r2 = off; off = align256(off + sbytes);     // next R

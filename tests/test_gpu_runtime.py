@@ -77,7 +77,7 @@ def test_release_plans_and_many_tables(lib):
      {"expand_desc": 1, "momentum_sumsq": 1, "finalize_norm": 1, "prep_x0": 1, "gram_gemm_sym": 14, "gram_gemm_full": 4,
       "gram_gemm_apply": 1}),
     ("gram", "f16", [(128, 640, 0)],
-     {"expand_desc": 1, "momentum_sumsq": 1, "finalize_norm": 1, "prep_gram": 1, "gram_gemm_sym": 13, "gram_gemm_full": 4,
+     {"expand_desc": 1, "momentum_sumsq": 1, "finalize_norm": 1, "prep_gram": 1, "gram_chain": 1,
       "gram_gemm_apply": 1}),
 ])
 def test_profile_counts_the_launch_sequence(lib, method, ns_dtype, shapes, want):
