@@ -1012,6 +1012,7 @@ __global__ __launch_bounds__(256) void gram_chain_kernel(GramChainBatch batch) {
   constexpr int PL = 128 * 128;                               // bytes of one K plane
   constexpr int MAT = 2 * PL;                                 // bytes of one matrix
   __shared__ __attribute__((aligned(1024))) char L[4 * MAT];
+  __shared__ __attribute__((aligned(16))) char Dump[64 * 2];
   char* const Rm = L;
   char* const Qm = L + MAT;
   char* const Tm = L + 2 * MAT;
@@ -1072,21 +1073,24 @@ __global__ __launch_bounds__(256) void gram_chain_kernel(GramChainBatch batch) {
       for (int j = 0; j < WB; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    // every operand of the product is requested before the first MFMA (one wave
+    // per SIMD: the registers are there, and the reads overlap the MFMAs)
+    V xa[8][WB], xb[8][WB];
 #pragma unroll
-    for (int pl = 0; pl < 2; ++pl)
+    for (int t = 0; t < 8; ++t) {
+      const int pl = t >> 2, ks = t & 3;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        V xa[WB], xb[WB];
+      for (int i = 0; i < WB; ++i) xa[t][i] = *reinterpret_cast<const V*>(A + pl * PL + aoff[i][ks]);
 #pragma unroll
-        for (int i = 0; i < WB; ++i) xa[i] = *reinterpret_cast<const V*>(A + pl * PL + aoff[i][ks]);
+      for (int j = 0; j < WB; ++j) xb[t][j] = *reinterpret_cast<const V*>(B + pl * PL + boff[j][ks]);
+    }
+    __builtin_amdgcn_sched_barrier(0);             // keep the reads ahead of the MFMAs
 #pragma unroll
-        for (int j = 0; j < WB; ++j) xb[j] = *reinterpret_cast<const V*>(B + pl * PL + boff[j][ks]);
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int i = 0; i < WB; ++i)
+      for (int i = 0; i < WB; ++i)
 #pragma unroll
-          for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);        // one k step per scheduling region
-      }
+        for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[t][i], xb[t][j], acc[i][j]);
   };
   // accumulator element (block i, j; register q * 4 + e) is row row0 + e, column
   // col. The stores take the lane index through an opaque copy made per call:
@@ -1109,11 +1113,15 @@ __global__ __launch_bounds__(256) void gram_chain_kernel(GramChainBatch batch) {
     for (int i = 0; i < WB; ++i)
 #pragma unroll
       for (int j = 0; j < WB; ++j) {
+        // 32 x 32 block (br, bc) of the matrix, the same for the whole wave:
+        // above the diagonal nothing is stored; below it every element is
+        // strictly lower; only diagonal blocks test element by element
+        const int br = wm * WB + i, bc = wn * WB + j;
+        if (br < bc) continue;
         const int col = col_of(ln, j);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row0 = row0_of(ln, i, q);
-          if (row0 + 3 < col) continue;                      // upper part: not stored
           float v[4];
           u16x4 dv;
           if (D != nullptr) dv = *reinterpret_cast<const u16x4*>(D + at(col, row0));   // D[row][col] = D[col][row]
@@ -1121,26 +1129,26 @@ __global__ __launch_bounds__(256) void gram_chain_kernel(GramChainBatch batch) {
           for (int e = 0; e < 4; ++e) {
             v[e] = alpha * acc[i][j][q * 4 + e];
             if (D != nullptr) v[e] = __builtin_fmaf(beta, static_cast<float>(__builtin_bit_cast(T, (unsigned short)dv[e])), v[e]);
-            if (gamma != 0.0f && row0 + e == col) v[e] += gamma;
+            if (br == bc) v[e] = (gamma != 0.0f && row0 + e == col) ? v[e] + gamma : v[e];
           }
           u16x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[e])));
-          if (row0 >= col) {
+          if (br > bc) {
             *reinterpret_cast<u16x4*>(dst + at(col, row0)) = o;          // (col, row0 + e): mirror
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (row0 + e > col) *reinterpret_cast<unsigned short*>(dst + at(row0 + e, col)) = o[e];
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<unsigned short*>(dst + at(row0 + e, col)) = o[e];
           } else {
+            // diagonal block: an element that is not stored goes to the lane's
+            // own slot of a dump area instead (no divergent branches)
+            char* const dump = Dump + ln * 2;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (row0 + e >= col) {
-                *reinterpret_cast<unsigned short*>(dst + at(col, row0 + e)) = o[e];
-                if (row0 + e > col) *reinterpret_cast<unsigned short*>(dst + at(row0 + e, col)) = o[e];
-              }
+            for (int e = 0; e < 4; ++e) {
+              *reinterpret_cast<unsigned short*>(row0 + e >= col ? dst + at(col, row0 + e) : dump) = o[e];
+              *reinterpret_cast<unsigned short*>(row0 + e > col ? dst + at(row0 + e, col) : dump) = o[e];
+            }
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
   };
   // full store of the rounded accumulators: transposed (row col holds column
