@@ -143,6 +143,15 @@ def test_half_precision_gaussian(lib, method, ns_dtype):
     _check(lib, wl, method, ns_dtype, faithful=True, gaussian_exact_gate=LP_GATE)
 
 
+def test_gram_fp16_short_sides_not_powers_of_two(lib):
+    # the fp16 Gram state is scaled by 2^ceil(log2 m): m = 1408 (the expert
+    # shapes) takes 2048 and m = 600 takes 1024, neither equal to m; Gaussian
+    # inputs, against the exact and the storage-faithful oracle
+    wl = W.custom_workload([(1408, 2048, 0), (1000, 600, 0)], grad_dtype="bf16", wid=119,
+                           grad_kind="gaussian")
+    _check(lib, wl, "gram", "f16", faithful=True, gaussian_exact_gate=LP_GATE)
+
+
 @pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16"),
                                              ("standard", "f16")])
 def test_half_precision_lowrank(lib, method, ns_dtype):
