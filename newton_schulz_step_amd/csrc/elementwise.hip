@@ -161,7 +161,7 @@ hipError_t launch_finalize_norm(const double* partials, int64_t chunks, int n_pr
 
 // ---------------------------------------------------------------------------
 // X0 = round(M / (||M||_F + eps)) in canonical orientation (short side = rows),
-// written as X (mp x np, row-major). Each block covers a 64x64 tile. A matrix
+// written as X (mp x np, row-major), in 64x64 tiles. A matrix
 // stored as is goes straight through; one stored transposed is read in its
 // stored orientation (coalesced) and turned in LDS. Padding rows/columns are
 // written as zeros.
@@ -182,72 +182,114 @@ __device__ __forceinline__ void store4(T* dst, const float (&v)[4]) {
   }
 }
 
-// Thread t covers columns 4 (t % 16) .. + 3 of tile rows 16 k + t / 16, k = 0..3:
-// consecutive lanes read consecutive 16-byte pieces of a row, so one wave
-// instruction reads four whole 256-byte rows.
+// Every block moves 64 KB of momentum. A matrix stored as is is streamed in row
+// pieces: the block covers 16 rows x 1024 columns, wave w rows 4 w .. 4 w + 3, and
+// in round q (0..15) lane l reads columns 256 (q % 4) + 4 l .. + 3 of row q / 4 of
+// the wave's rows, so every wave instruction reads 1 KB of one row and each row
+// piece is 4 KB long. A matrix stored transposed goes through LDS in four 64x64
+// tiles down a tile column.
+
 template <typename T>
 __global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const ProblemDesc* probs, const float* inv_norm,
                                                       int m, int n, int mp, int np, T* X) {
   __shared__ float tile[64][65];
   const int tiles_j = np >> 6;
-  const int per = (mp >> 6) * tiles_j;
+  const int per_t = ((mp + 255) >> 8) * tiles_j;       // blocks of a transposed problem
+  const int pieces_j = (np + 1023) >> 10;
+  const int per_r = (mp >> 4) * pieces_j;              // blocks of a problem stored as is
+  const int per = max(per_t, per_r);
   const int p = blockIdx.x / per;
   const int t = blockIdx.x - p * per;
-  const int i0 = (t / tiles_j) * 64, j0 = (t % tiles_j) * 64;
   const ProblemDesc pd = probs[p];
   const float inv = inv_norm[p];
-  const int rr = threadIdx.x >> 4, c4 = (threadIdx.x & 15) * 4;
   T* Xp = X + p * static_cast<int64_t>(mp) * np;
 
   if (!pd.transposed) {
     // stored m x n: element (i, j) at src + i * n + j
+    if (t >= per_r) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r0 = (t / pieces_j) * 16 + 4 * w, c0 = (t % pieces_j) * 1024 + 4 * lane;
+    float v[16][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int gi = i0 + 16 * k + rr, gj = j0 + c4;
+    for (int q = 0; q < 16; ++q) {
+      const int gi = r0 + (q >> 2), gj = c0 + 256 * (q & 3);
       const int64_t base = pd.src_off + static_cast<int64_t>(gi) * n + gj;
-      float v[4];
       if (gi < m && gj + 4 <= n && (base & 3) == 0) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(M + base);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(M + base);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = w[e] * inv;
+        for (int e = 0; e < 4; ++e) v[q][e] = x[e];
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (gi < m && gj + e < n) ? M[base + e] * inv : 0.0f;
+        for (int e = 0; e < 4; ++e) v[q][e] = (gi < m && gj + e < n) ? M[base + e] : 0.0f;
       }
-      store4<T>(Xp + static_cast<int64_t>(gi) * np + gj, v);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int gi = r0 + (q >> 2), gj = c0 + 256 * (q & 3);
+      if (gj < np) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = v[q][e] * inv;
+        store4<T>(Xp + static_cast<int64_t>(gi) * np + gj, o);
+      }
     }
     return;
   }
 
-  // stored n x m: element (i, j) at src + j * m + i; stored row j0 + 16 k + rr holds
-  // canonical column j, and its columns i0 + c4 .. + 3 canonical rows
+  if (t >= per_t) return;
+  // stored n x m: element (i, j) at src + j * m + i. The block covers canonical rows
+  // i0 .. i0 + 255 (tiles q = 0..3 of 64 rows) and columns j0 .. j0 + 63: stored rows
+  // j0 .. j0 + 63, read in 1 KB pieces. All loads are issued first; each tile is
+  // then turned in LDS: stored row j0 + 16 k + rr holds canonical column j, and its
+  // elements i0 + 64 q + c4 .. + 3 canonical rows.
+  const int i0 = (t / tiles_j) * 256, j0 = (t % tiles_j) * 64;
+  const int nt = min(4, (mp - i0) >> 6);   // tiles of this block
+  const int rr = threadIdx.x >> 4, c4 = (threadIdx.x & 15) * 4;
+  float v[4][4][4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int sj = j0 + 16 * k + rr, si = i0 + c4;
-    const int64_t base = pd.src_off + static_cast<int64_t>(sj) * m + si;
-    if (sj < n && si + 4 <= m && (base & 3) == 0) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(M + base);
+  for (int q = 0; q < 4; ++q) {
+    if (q < nt) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tile[c4 + e][16 * k + rr] = w[e];
-    } else {
+      for (int k = 0; k < 4; ++k) {
+        const int sj = j0 + 16 * k + rr, si = i0 + 64 * q + c4;
+        const int64_t base = pd.src_off + static_cast<int64_t>(sj) * m + si;
+        if (sj < n && si + 4 <= m && (base & 3) == 0) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(M + base);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tile[c4 + e][16 * k + rr] = (sj < n && si + e < m) ? M[base + e] : 0.0f;
+          for (int e = 0; e < 4; ++e) v[q][k][e] = w[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[q][k][e] = (sj < n && si + e < m) ? M[base + e] : 0.0f;
+        }
+      }
     }
   }
-  __syncthreads();   // the transposed flag is the same for the whole block
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int r = 16 * k + rr;
-    float v[4];
+  for (int q = 0; q < 4; ++q) {
+    if (q < nt) {
+      if (q > 0) __syncthreads();   // the previous tile's reads are done
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = tile[r][c4 + e] * inv;
-    store4<T>(Xp + static_cast<int64_t>(i0 + r) * np + j0 + c4, v);
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[c4 + e][16 * k + rr] = v[q][k][e];
+      __syncthreads();   // the transposed flag is the same for the whole block
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 16 * k + rr;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = tile[r][c4 + e] * inv;
+        store4<T>(Xp + static_cast<int64_t>(i0 + 64 * q + r) * np + j0 + c4, o);
+      }
+    }
   }
 }
 
 hipError_t launch_prep_x0(int ns_dtype, const float* M, const ProblemDesc* probs, const float* inv_norm,
                           int n_problems, int m, int n, int mp, int np, void* X, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>(n_problems) * (mp / 64) * (np / 64);
+  const int64_t per = std::max<int64_t>(static_cast<int64_t>((mp + 255) / 256) * (np / 64),
+                                       static_cast<int64_t>(mp / 16) * ((np + 1023) / 1024));
+  const int64_t blocks = static_cast<int64_t>(n_problems) * per;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   switch (ns_dtype) {
