@@ -23,9 +23,10 @@
  *   M <- mu * M + G                                 (fp32 momentum, in place)
  *   Y  = M, transposed if it has more rows than columns
  *   X0 = Y / (||Y||_F + ns_eps)
- *   X  = NS(X0)  (ns_steps iterations; standard: A = X X^T, B = b A + c A A,
- *                 X <- a X + B X; gram: R = X0 X0^T, Q = a I + b R + c R R,
- *                 P <- Q P, R <- Q R Q, X = P X0)
+ *   X  = NS(X0)  (ns_steps iterations; standard: A = X X^T,
+ *                 B = a I + b A + c A A, X <- B X (= a X + b A X + c A A X);
+ *                 gram: R = X0 X0^T, Q = a I + b R + c R R, P <- Q P,
+ *                 R <- Q R Q, X = P X0)
  *   O  = X, transposed back
  *   p <- p * (1 - lr * weight_decay) - lr * O      (params, in place)
  *

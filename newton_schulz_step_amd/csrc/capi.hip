@@ -272,8 +272,10 @@ static int run_prep_gram(const StepCtx& c, const Group& G, void* R, float alpha)
 }
 
 // Standard quintic (DeepSpeed-Muon article, section 核心算子): per step
-//   A = X X^T;  B = b A + c A A;  X <- a X + B X,
-// the last step's epilogue applying p <- p * decay - lr * X.
+//   A = X X^T;  B = a I + b A + c A A;  X <- B X,
+// (a X + (b A + c A A) X with the a X term grouped into the stored B, as the
+// Gram form groups a I into Q), the last step's epilogue applying
+// p <- p * decay - lr * X.
 static int run_standard(const StepCtx& c, const GroupSet& set) {
   const int dt = c.h->ns_dtype;
   const int tile = set.front()->tile;
@@ -298,19 +300,19 @@ static int run_standard(const StepCtx& c, const GroupSet& set) {
       g1.alpha = 1.0f;
       v1.push_back(g1);
 
+      // B = a I + b A + c A A (the a X term grouped into B)
       GemmArgs g2{};
       set_sym(g2, G, A, A, kext(G.m, dt), G.mp, ss, B);
       g2.alpha = c.h->ns_c;
       g2.beta = c.h->ns_b;
+      g2.gamma = c.h->ns_a;
       g2.D = A; g2.d_ps = ss; g2.ldd = static_cast<int32_t>(G.mp);
       v2.push_back(g2);
 
-      // B X with X itself as the K x N operand; X is also the a X term
+      // B X with X itself as the K x N operand
       GemmArgs g3 = last ? apply_args(c, G) : GemmArgs{};
       set_full(g3, G, B, ss, G.mp, X[cur], xs, G.np, kext(G.m, dt), G.mp, G.np);
       g3.alpha = 1.0f;
-      g3.beta = c.h->ns_a;
-      g3.D = X[cur]; g3.d_ps = xs; g3.ldd = static_cast<int32_t>(G.np);
       if (!last) { g3.C = X[cur ^ 1]; g3.c_ps = xs; g3.ldc = static_cast<int32_t>(G.np); }
       if (fused && !last) {
         // one block per problem; the new X X^T goes to A (already consumed by B)

@@ -521,7 +521,7 @@ __device__ __forceinline__ void apply8(const GemmArgs& a, int64_t pidx, int64_t 
 // pass (D, params) is issued before any of them is used, and D of block i + 1 is
 // requested as soon as block i has consumed its own, so each pass waits for memory
 // at most once.
-template <typename T, int TILE, bool SYM, int EPI>
+template <typename T, int TILE, bool SYM, int EPI, bool HAS_D>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, int tj, char* lds0, char* lds1,
                                          f32x16 (&acc)[Geo<T, TILE>::WB][Geo<T, TILE>::WB]) {
   using Gm = Geo<T, TILE>;
@@ -559,7 +559,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
 
   T* C = static_cast<T*>(a.C);
   T* Ct = static_cast<T*>(a.Ct);
-  const T* D = static_cast<const T*>(a.D);
+  const T* D = HAS_D ? static_cast<const T*>(a.D) : nullptr;   // compiled out without a D term
   const bool need_col = APPLY ? (transposed != 0) : (Ct != nullptr);
 
   Pack8<T> dq[NR];
@@ -727,8 +727,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
 }
 
 // One launch covers up to kBatchGroups shape groups: block b belongs to the last
-// group g with start[g] <= b.
-template <typename T, int TILE, bool SYM, int EPI, bool NN>
+// group g with start[g] <= b. HAS_D: the launch has a beta D term (every group
+// of it); without, the epilogue is compiled with no D code at all.
+template <typename T, int TILE, bool SYM, int EPI, bool NN, bool HAS_D>
 __global__ __launch_bounds__(256) void ns_gemm(GemmBatch batch) {
   using Gm = Geo<T, TILE>;
   __shared__ __attribute__((aligned(1024))) char lds0[2 * Gm::OPB];
@@ -743,23 +744,23 @@ __global__ __launch_bounds__(256) void ns_gemm(GemmBatch batch) {
   decode_tile<SYM>(a, bid - batch.start[g], prob, ti, tj);
   f32x16 acc[Gm::WB][Gm::WB];
   mainloop<T, TILE, NN>(a, prob, ti, tj, lds0, lds1, acc);
-  epilogue<T, TILE, SYM, EPI>(a, prob, ti, tj, lds0, lds1, acc);
+  epilogue<T, TILE, SYM, EPI, HAS_D>(a, prob, ti, tj, lds0, lds1, acc);
 }
 
 // ---------------------------------------------------------------------------
 // Groups with a single tile row (m <= 128, 16-bit iterates): the update
-// X' = a X + B X and the next Gram matrix A' = X' X'^T in one pass.
+// X' = B X and the next Gram matrix A' = X' X'^T in one pass.
 //
 // One workgroup per problem keeps B in LDS and streams X one 128-column tile at a
-// time: each tile is the K x N operand of B X and also the a X term, so X is
-// read once; X' goes out to HBM and, rounded as stored, into LDS, where it is
+// time: each tile is the K x N operand of B X, so X is read once; X' goes out to HBM and, rounded as stored, into LDS, where it is
 // the operand of the tile's contribution to X' X'^T, accumulated in registers
 // over all tiles. Every output element sees the same products in the same k
 // order as the separate update and X X^T launches, so the results are
 // bit-identical to theirs.
 //
-// Arguments: P = B (mp x mp), Q = D = X (mp x np), C = X', Ct = A' (mp x mp,
-// stored symmetric); alpha, beta as in the update; tiles_n = np / 128.
+// Arguments: P = B (mp x mp, the a I term included), Q = X (mp x np), C = X',
+// Ct = A' (mp x mp, stored symmetric); alpha as in the update (no D term);
+// tiles_n = np / 128.
 template <typename T>
 __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
   using Gm = Geo<T, 128>;
@@ -894,8 +895,7 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
           for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], accC[i][j]);
       }
 
-    // epilogue: v = alpha acc + beta X (from the tile in LDS), rounded; to HBM and
-    // to the K-contiguous planes of X'
+    // epilogue: v = alpha acc, rounded; to HBM and to the K-contiguous planes of X'
 #pragma unroll
     for (int i = 0; i < WB; ++i) {
       asm volatile("" ::: "memory");
@@ -912,16 +912,9 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
         const int gi = wm * HALF + i * 32 + rr, gj = wn * HALF + cc;   // row (= k of X), column in tile
         const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
         const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
-        const int ksl = gi >> 6, kr = gi & 63, cb = gj * 2;
-        const u16x8 dq = *reinterpret_cast<const u16x8*>(Xs + ksl * XSB + kr * RB +
-                                                         (((cb >> 5) ^ nn_swz(kr)) << 5) + (cb & 31));
         T o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float v = a.alpha * (e < 4 ? s0[e] : s1[e - 4]);
-          v = __builtin_fmaf(a.beta, static_cast<float>(__builtin_bit_cast(T, static_cast<unsigned short>(dq[e]))), v);
-          o[e] = from_f32<T>(keep_f32(v));
-        }
+        for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(keep_f32(a.alpha * (e < 4 ? s0[e] : s1[e - 4])));
         st8<T>(Cg + static_cast<int64_t>(gi) * a.ldc + static_cast<int64_t>(jt) * 128 + gj, o);
         const int pl = gj >> 6, c = (gj & 63) >> 3;
         u16x8 w;
@@ -964,7 +957,7 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
   s.C = a.Ct; s.c_ps = a.ct_ps; s.ldc = a.ldct;
   s.Ct = a.Ct; s.ct_ps = a.ct_ps; s.ldct = a.ldct;
   s.alpha = 1.0f;
-  epilogue<T, 128, true, EPI_STORE>(s, prob, 0, 0, St, St + 2 * STG, accA);
+  epilogue<T, 128, true, EPI_STORE, false>(s, prob, 0, 0, St, St + 2 * STG, accA);
 }
 
 hipError_t launch_update_gram(int dtype, const GemmBatch& b, hipStream_t s) {
@@ -972,6 +965,7 @@ hipError_t launch_update_gram(int dtype, const GemmBatch& b, hipStream_t s) {
   for (int g = 0; g < b.n; ++g) {
     const GemmArgs& a = b.g[g];
     if (a.K != 128 || a.tiles_n < 1 || b.start[g + 1] - b.start[g] != a.total_tiles) return hipErrorInvalidValue;
+    if (a.D != nullptr || a.beta != 0.0f) return hipErrorInvalidValue;   // no D term
   }
   if (b.start[b.n] <= 0) return hipSuccess;
   switch (dtype) {
@@ -1366,7 +1360,7 @@ __global__ __launch_bounds__(256) void prep_gram_kernel(PrepGramArgs a) {
   s.Ct = a.R; s.ct_ps = s.c_ps; s.ldct = a.mp;
   s.alpha = a.alpha;
   char* st = reinterpret_cast<char*>(Ms);
-  epilogue<T, 128, true, EPI_STORE>(s, p, 0, 0, st, st + 2 * STG, acc);
+  epilogue<T, 128, true, EPI_STORE, false>(s, p, 0, 0, st, st + 2 * STG, acc);
 }
 
 hipError_t launch_prep_gram(int dtype, const PrepGramArgs& a, hipStream_t s) {
@@ -1388,7 +1382,7 @@ hipError_t launch_prep_gram(int dtype, const PrepGramArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // launchers
 
-template <typename T, int TILE, bool SYM, int EPI, bool NN>
+template <typename T, int TILE, bool SYM, int EPI, bool NN, bool HAS_D>
 static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
   if (b.n < 1 || b.n > kBatchGroups) return hipErrorInvalidValue;
   for (int g = 0; g < b.n; ++g) {
@@ -1396,20 +1390,25 @@ static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
     // the main loop runs whole pairs of 128-byte K slices
     if (a.K <= 0 || a.K % (2 * 128 / static_cast<int>(sizeof(T))) != 0) return hipErrorInvalidValue;
     if (b.start[g + 1] - b.start[g] != a.total_tiles || a.total_tiles < 0) return hipErrorInvalidValue;
+    if ((a.D != nullptr) != HAS_D) return hipErrorInvalidValue;   // one kind of epilogue per launch
   }
   if (b.start[0] != 0 || b.start[b.n] <= 0) return b.start[b.n] == 0 ? hipSuccess : hipErrorInvalidValue;
-  hipLaunchKernelGGL((ns_gemm<T, TILE, SYM, EPI, NN>), dim3(b.start[b.n]), dim3(256), 0, s, b);
+  hipLaunchKernelGGL((ns_gemm<T, TILE, SYM, EPI, NN, HAS_D>), dim3(b.start[b.n]), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
-// Symmetric launches take both operands K-contiguous (NT); full launches take the
-// second operand stored K x N (NN).
+// Symmetric launches take both operands K-contiguous (NT), with or without a D
+// term; full launches take the second operand stored K x N (NN) and have none.
 template <typename T, int TILE>
 static hipError_t launch_tile(bool sym, int epi, const GemmBatch& b, hipStream_t s) {
-  if (sym) return epi == EPI_STORE ? launch_t<T, TILE, true, EPI_STORE, false>(b, s) : hipErrorInvalidValue;
-  if (epi == EPI_APPLY) return launch_t<T, TILE, false, EPI_APPLY, true>(b, s);
-  if (epi == EPI_APPLY_BF16) return launch_t<T, TILE, false, EPI_APPLY_BF16, true>(b, s);
-  return launch_t<T, TILE, false, EPI_STORE, true>(b, s);
+  if (sym) {
+    if (epi != EPI_STORE) return hipErrorInvalidValue;
+    return b.g[0].D != nullptr ? launch_t<T, TILE, true, EPI_STORE, false, true>(b, s)
+                               : launch_t<T, TILE, true, EPI_STORE, false, false>(b, s);
+  }
+  if (epi == EPI_APPLY) return launch_t<T, TILE, false, EPI_APPLY, true, false>(b, s);
+  if (epi == EPI_APPLY_BF16) return launch_t<T, TILE, false, EPI_APPLY_BF16, true, false>(b, s);
+  return launch_t<T, TILE, false, EPI_STORE, true, false>(b, s);
 }
 
 template <typename T>

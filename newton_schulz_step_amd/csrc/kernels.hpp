@@ -29,7 +29,8 @@ struct GemmArgs {
   int32_t K;
   int32_t tiles_m, tiles_n, tiles_per_problem, total_tiles;
   float alpha, beta, gamma;
-  const void* D; int64_t d_ps; int32_t ldd;      // optional (beta term)
+  const void* D; int64_t d_ps; int32_t ldd;      // optional beta term: symmetric launches only,
+                                                 // and then in every group of the launch
   void* C; int64_t c_ps; int32_t ldc;            // optional row-major store
   void* Ct; int64_t ct_ps; int32_t ldct;         // optional transposed store (SYM: mirror, = C)
   // EPI_APPLY(_BF16): p <- p * decay - lr * v at the problem's stored position
@@ -50,10 +51,10 @@ struct GemmBatch {
 
 hipError_t launch_ns_gemm(int dtype, int tile, bool sym, int epi, const GemmBatch& b, hipStream_t s);
 
-// Single-tile-row groups (mp = 128, bf16/fp16): X' = alpha B X + beta X and
-// A' = X' X'^T (stored symmetric) in one pass, one block per problem. Per group:
-// P = B, Q = D = X, C = X', Ct = A', K = 128, tiles_n = np / 128,
-// total_tiles = number of problems.
+// Single-tile-row groups (mp = 128, bf16/fp16): X' = alpha B X and A' = X' X'^T
+// (stored symmetric) in one pass, one block per problem. Per group: P = B,
+// Q = X, C = X', Ct = A', K = 128, tiles_n = np / 128, total_tiles = number of
+// problems; D must be null and beta 0.
 hipError_t launch_update_gram(int dtype, const GemmBatch& b, hipStream_t s);
 
 // Single-tile-row groups (mp = 128, fp16), Gram method: the whole chain

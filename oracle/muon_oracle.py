@@ -19,9 +19,12 @@ Sources (pages, by title and section):
         lifecycles).
 
 Readings where the pages leave a step open (each also listed in the design notes):
-  * Newton-Schulz step form: A = X X^T, B = b A + c A A, X <- a X + B X, i.e. the
-    odd quintic p(x) = a x + b x^3 + c x^5 applied to every singular value; the
-    article's "maximise the slope at zero" matches p'(0) = a.
+  * Newton-Schulz step form: A = X X^T, B = a I + b A + c A A, X <- B X, i.e.
+    the odd quintic p(x) = a x + b x^3 + c x^5 applied to every singular value;
+    the article's "maximise the slope at zero" matches p'(0) = a. The article
+    fixes the polynomial, its coefficients and the bf16 precision, not how the
+    a X term is grouped; B carries a I, the grouping its Gram variant uses for
+    Q = a I + b R + c R R. In exact arithmetic this is a X + (b A + c A A) X.
   * X0 = Y / (||Y||_F + eps), eps = 1e-7; Y is transposed first when it has more
     rows than columns, and the result is transposed back.
   * Momentum: heavy ball, M <- mu M + G, no Nesterov term, no dampening.
@@ -44,7 +47,8 @@ Readings where the pages leave a step open (each also listed in the design notes
 Storage-faithful mode: the article runs the standard iteration in bf16 and the
 Gram iteration in fp16. `store` rounds (once, to nearest even, from float64) at
 each point where such an implementation stores a matrix; the arithmetic between
-those points stays float64. Standard: X0, A, B and X1..X4 are stored; X5 is not.
+those points stays float64. Standard: X0, A, B (a I included) and X1..X4 are
+stored; X5 is not.
 Gram: X0, R0, every Q, P and R, and the intermediate T = R Q are stored; P X0 is
 not. The Gram state may carry an exact power-of-two scale s (R is kept as
 s X X^T, and b, c become b/s, c/s^2); with s = 1 this is the plain recurrence.
@@ -111,10 +115,11 @@ def newton_schulz_standard(X0: np.ndarray, steps: int = NS_STEPS,
     a, b, c = coeffs
     sym = _symmetric(store)
     X = store(X0)
+    eye = np.eye(X0.shape[0])
     for k in range(steps):
         A = sym(X @ X.T)
-        B = sym(b * A + c * (A @ A))
-        X_next = a * X + B @ X
+        B = sym(a * eye + b * A + c * (A @ A))
+        X_next = B @ X
         X = X_next if k == steps - 1 else store(X_next)
     return X
 

@@ -216,8 +216,8 @@ def _hadamard(n):
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_faithful_standard_on_hadamard_reduces_to_scalars(fmt):
     """Rows of a Hadamard matrix: X_k = t_k H, A_k = n t_k^2 I, B_k = beta_k I, so the
-    stored iteration is a scalar one. Pins the storage points (X0, A, B, X1..X4
-    stored; X5 not) of the faithful mode."""
+    stored iteration is a scalar one. Pins the storage points (X0, A, B = a I +
+    b A + c A A, X1..X4 stored; X5 not) of the faithful mode."""
     m, n = 16, 64
     H = _hadamard(n)[:m]
     rnd = lambda z: float(rounding.round_to(z, fmt))
@@ -225,8 +225,8 @@ def test_faithful_standard_on_hadamard_reduces_to_scalars(fmt):
     t = rnd(1.0 / np.sqrt(m * n))      # eps = 0: X0 = H / ||H||_F, entries exact
     for k in range(5):
         alpha = rnd(n * t * t)
-        beta = rnd(b * alpha + c * alpha * alpha)
-        t_next = a * t + beta * t
+        beta = rnd(a + b * alpha + c * alpha * alpha)
+        t_next = beta * t
         t = t_next if k == 4 else rnd(t_next)
     O = oracle.orthogonalise(H, "standard", eps=0.0, store_fmt=fmt)
     assert np.array_equal(O, t * H)
@@ -268,8 +268,8 @@ def test_faithful_row_scaled_hadamard_is_per_row_scalars(fmt):
     t = np.array([rnd(di / nu) for di in d])
     for k in range(5):
         al = np.array([rnd(n * ti * ti) for ti in t])
-        be = np.array([rnd(b * x + c * x * x) for x in al])
-        nxt = a * t + be * t
+        be = np.array([rnd(a + b * x + c * x * x) for x in al])
+        nxt = be * t
         t = nxt if k == 4 else np.array([rnd(x) for x in nxt])
     O = oracle.orthogonalise(d[:, None] * H, "standard", eps=0.0, store_fmt=fmt)
     assert np.array_equal(O, t[:, None] * H)
@@ -325,7 +325,7 @@ def test_faithful_symmetric_storage_is_a_fixed_order_evaluation():
         A_fo = _fixed_order_matmul(X, X.T)
         assert np.array_equal(A_fo, A_fo.T)
         assert np.array_equal(A, rnd(A_fo)), k
-        B_fo = b * A + c * _fixed_order_matmul(A, A)
+        B_fo = a * np.eye(6) + b * A + c * _fixed_order_matmul(A, A)
         assert np.array_equal(B_fo, B_fo.T)
         assert np.array_equal(B, rnd(B_fo)), k
         if k < 4:
