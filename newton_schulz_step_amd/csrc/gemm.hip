@@ -67,6 +67,14 @@ template <> struct Mfma<float> {
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
+// Products are issued with the K x N operand first, so a 32 x 32 accumulator
+// block holds the transposed tile block: register 4 q + e of lane l is row l % 32,
+// column 8 q + 4 (l / 32) + e. Four consecutive columns of one row go to the
+// epilogue staging area in one 16-byte write.
+__device__ __forceinline__ void stage4(float* dst, const f32x16& acc, int q) {
+  *reinterpret_cast<f32x4*>(dst) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+}
+
 // Pair swizzle of the K x N operand (rows of 32-byte pairs in LDS): pair p of K row
 // kr is stored at pair slot p ^ nn_swz(kr). A 16-bit transposed read takes, per
 // half wave, two adjacent pairs (2q, 2q + 1) from four consecutive K rows; the
@@ -343,7 +351,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, int prob, int ti, in
 #pragma unroll
     for (int i = 0; i < WB; ++i)
 #pragma unroll
-      for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], acc[i][j]);
+      for (int j = 0; j < WB; ++j) Mfma<T>::run(xb[j], xa[i], acc[i][j]);   // transposed block, see epilogue
   };
   // scheduling of one sub-step: its nw LDS writes and global loads, then its NRD
   // operand reads, each paired with MFMAs; then a fence
@@ -587,8 +595,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
 #pragma unroll
     for (int j = 0; j < WB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        stg[srow((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), j * 32 + (lane & 31))] = acc[i][j][r];
+      for (int q = 0; q < 4; ++q) stage4(stg + srow(lane & 31, j * 32 + q * 8 + (lane >> 5) * 4), acc[i][j], q);
     lds_order();
 
     // ---- row pass: each lane finishes one 8-column chunk at a time
@@ -892,7 +899,7 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
 #pragma unroll
         for (int i = 0; i < WB; ++i)
 #pragma unroll
-          for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], accC[i][j]);
+          for (int j = 0; j < WB; ++j) Mfma<T>::run(xb[j], xa[i], accC[i][j]);
       }
 
     // epilogue: v = alpha acc, rounded; to HBM and to the K-contiguous planes of X'
@@ -902,8 +909,7 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
 #pragma unroll
       for (int j = 0; j < WB; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          stg[srow((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), j * 32 + (lane & 31))] = accC[i][j][r];
+        for (int q = 0; q < 4; ++q) stage4(stg + srow(lane & 31, j * 32 + q * 8 + (lane >> 5) * 4), accC[i][j], q);
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -938,7 +944,7 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
 #pragma unroll
         for (int i = 0; i < WB; ++i)
 #pragma unroll
-          for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], accA[i][j]);
+          for (int j = 0; j < WB; ++j) Mfma<T>::run(xb[j], xa[i], accA[i][j]);
       }
   };
 
@@ -1347,7 +1353,7 @@ __global__ __launch_bounds__(256) void prep_gram_kernel(PrepGramArgs a) {
 #pragma unroll
         for (int i = 0; i < WB; ++i)
 #pragma unroll
-          for (int j = 0; j < WB; ++j) Mfma<T>::run(xa[i], xb[j], acc[i][j]);
+          for (int j = 0; j < WB; ++j) Mfma<T>::run(xb[j], xa[i], acc[i][j]);
       }
     __syncthreads();                       // products done before the tile buffers are reused
   };
