@@ -371,7 +371,7 @@ def dominant_roofline(wl, method, ns_dtype, h, kstats, steps):
         dom_kind = "ns_gemm_update"
         tile = 256 if probs and probs[0][0] >= 512 else 128
         dt_name = {"bf16": "__bf16", "f16": "_Float16", "f32": "float"}[ns_dtype]
-        dom_kernel = f"muon::ns_gemm<{dt_name}, {tile}, false, 0, true>"
+        dom_kernel = f"muon::ns_gemm<{dt_name}, {tile}, false, 0, true, false>"
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
         dom_flops = sum(2.0 * m * m * n for m, n in probs) * (h.ns_steps - 1) * steps
         achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
@@ -379,7 +379,7 @@ def dominant_roofline(wl, method, ns_dtype, h, kstats, steps):
         # 128-row problems in fp16 (the chain runs in LDS): the apply X = P X0,
         # bound by memory: X0 read, fp32 params read and written
         dom_kind = "gram_gemm_apply"
-        dom_kernel = "muon::ns_gemm<_Float16, 128, false, 1, true>"
+        dom_kernel = "muon::ns_gemm<_Float16, 128, false, 1, true, false>"
         launches, dom_ms = kstats[dom_kind]
         dom_work = sum(2.0 * m * n + 8.0 * m * n for m, n in probs if m <= 128) * steps
         bound, unit, roof_peak = "hbm", "GB/s", HBM_PEAK_GBS
@@ -387,7 +387,7 @@ def dominant_roofline(wl, method, ns_dtype, h, kstats, steps):
     else:
         dom_kind = "gram_gemm_sym"
         tile = 256 if probs and probs[0][0] >= 512 else 128
-        dom_kernel = f"muon::ns_gemm<{'_Float16' if ns_dtype == 'f16' else 'float'}, {tile}, true, 0, false>"
+        dom_kernel = f"muon::ns_gemm<{'_Float16' if ns_dtype == 'f16' else 'float'}, {tile}, true, 0, false, HAS_D>"
         launches, dom_ms = kstats.get(dom_kind, (0, 0.0))
         dom_flops = sum(1.0 * m * m * n + 13.0 * m ** 3 for m, n in probs) * steps
         achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else None
@@ -498,8 +498,8 @@ def main() -> int:
     args = ap.parse_args()
     workload = args.workload if args.workload is not None else 3
     if args.summarize_mfma:
-        symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0ELb1EEEvNS_9GemmBatchE" if args.method == "standard"
-                  else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0ELb0EEEvNS_9GemmBatchE")
+        symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0ELb1ELb0EEEvNS_9GemmBatchE" if args.method == "standard"
+                  else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0ELb0ELb0EEEvNS_9GemmBatchE")
         rec = summarize_mfma(args.summarize_mfma, symbol)
         run = (f"python3 $REPO/bench.py --workload {workload} --method {args.method} "
                "--steps 2 --warmup 1 --no-cpu-baseline")
@@ -516,8 +516,8 @@ def main() -> int:
         return 0
     if args.summarize_counters:
         ns_dtype = "bf16" if args.method == "standard" else "f16"
-        symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0ELb1EEEvNS_9GemmBatchE" if ns_dtype == "bf16"
-                  else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0ELb0EEEvNS_9GemmBatchE")
+        symbol = ("_ZN4muon7ns_gemmIDF16bLi256ELb0ELi0ELb1ELb0EEEvNS_9GemmBatchE" if ns_dtype == "bf16"
+                  else "_ZN4muon7ns_gemmIDF16_Li256ELb1ELi0ELb0ELb0EEEvNS_9GemmBatchE")
         rec = summarize_counters(*args.summarize_counters, copy_bytes=1 << 32, symbol=symbol,
                                  workload=workload, method=args.method)
         with open(traffic_path(workload, args.method), "w") as f:
