@@ -564,11 +564,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
     whi = pd.hi;
   }
   const int m = a.m_valid, n = a.n_valid;
+  // the launch's scalars, read once
+  const float alpha = a.alpha, beta = a.beta, gamma = a.gamma;
+  const int64_t c_ps = a.c_ps, ct_ps = a.ct_ps, d_ps = a.d_ps;
+  const int ldc = a.ldc, ldct = a.ldct, ldd = a.ldd;
 
+  // Store launches always write C; symmetric ones also its mirror Ct, full ones
+  // never (the launcher checks both), so the column pass is known at compile time
   T* C = static_cast<T*>(a.C);
   T* Ct = static_cast<T*>(a.Ct);
   const T* D = HAS_D ? static_cast<const T*>(a.D) : nullptr;   // compiled out without a D term
-  const bool need_col = APPLY ? (transposed != 0) : (Ct != nullptr);
+  const bool need_col = APPLY ? (transposed != 0) : SYM;
 
   Pack8<T> dq[NR];
   auto load_d = [&](int i) {
@@ -578,7 +584,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       const int q = lane + 64 * t;
       const int gi = gi_w + i * 32 + q / CPR;
       const int gj = gj_w + (q % CPR) * 8;
-      dq[t].load(D + static_cast<int64_t>(prob) * a.d_ps + static_cast<int64_t>(gi) * a.ldd + gj);
+      dq[t].load(D + static_cast<int64_t>(prob) * d_ps + static_cast<int64_t>(gi) * ldd + gj);
     }
   };
   load_d(0);
@@ -608,15 +614,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
       const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { v[e] = a.alpha * s0[e]; v[e + 4] = a.alpha * s1[e]; }
+      for (int e = 0; e < 4; ++e) { v[e] = alpha * s0[e]; v[e + 4] = alpha * s1[e]; }
       if (D != nullptr) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(a.beta, dq[t].get(e), v[e]);
+        for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(beta, dq[t].get(e), v[e]);
       }
-      if (a.gamma != 0.0f) {
+      if (gamma != 0.0f) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (gi == gj + e) v[e] += a.gamma;
+          if (gi == gj + e) v[e] += gamma;
       }
       float4* sp = reinterpret_cast<float4*>(stg + srow(rr, cc));
       if constexpr (APPLY) {
@@ -628,14 +634,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
         T o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(keep_f32(v[e]));
-        if (C != nullptr) {
-          T* cp = C + static_cast<int64_t>(prob) * a.c_ps + static_cast<int64_t>(gi) * a.ldc + gj;
-          if (!diag || gi >= gj + 7) {
-            st8<T>(cp, o);
-          } else {
-            for (int e = 0; e < 8; ++e)
-              if (gi >= gj + e) cp[e] = o[e];
-          }
+        T* cp = C + static_cast<int64_t>(prob) * c_ps + static_cast<int64_t>(gi) * ldc + gj;
+        if (!diag || gi >= gj + 7) {
+          st8<T>(cp, o);
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (gi >= gj + e) cp[e] = o[e];
         }
         if (need_col) {
           sp[0] = make_float4(to_f32(o[0]), to_f32(o[1]), to_f32(o[2]), to_f32(o[3]));
@@ -720,7 +724,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
           T o[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(stg[srow(r8 + e, cc)]);
-          T* cp = Ct + static_cast<int64_t>(prob) * a.ct_ps + static_cast<int64_t>(gj) * a.ldct + gi;
+          T* cp = Ct + static_cast<int64_t>(prob) * ct_ps + static_cast<int64_t>(gj) * ldct + gi;
           if (!diag || gi > gj) {
             st8<T>(cp, o);
           } else {
@@ -1397,6 +1401,8 @@ static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
     if (a.K <= 0 || a.K % (2 * 128 / static_cast<int>(sizeof(T))) != 0) return hipErrorInvalidValue;
     if (b.start[g + 1] - b.start[g] != a.total_tiles || a.total_tiles < 0) return hipErrorInvalidValue;
     if ((a.D != nullptr) != HAS_D) return hipErrorInvalidValue;   // one kind of epilogue per launch
+    // store launches write C, and its mirror Ct exactly when symmetric
+    if (EPI == EPI_STORE && (a.C == nullptr || (a.Ct != nullptr) != SYM)) return hipErrorInvalidValue;
   }
   if (b.start[0] != 0 || b.start[b.n] <= 0) return b.start[b.n] == 0 ? hipSuccess : hipErrorInvalidValue;
   hipLaunchKernelGGL((ns_gemm<T, TILE, SYM, EPI, NN, HAS_D>), dim3(b.start[b.n]), dim3(256), 0, s, b);
