@@ -72,7 +72,8 @@ enum {
   MUON_ERR_NULL = 1,        /* a required pointer is NULL */
   MUON_ERR_BAD_METHOD = 2,  /* ns_method is neither STANDARD nor GRAM */
   MUON_ERR_BAD_SHAPE = 3,   /* rows/cols < 1, split_rows < 0 or not dividing rows,
-                               n_entries < 0, or a size beyond the limits below */
+                               split_cols < 0 or not dividing cols, n_entries < 0,
+                               or a size beyond the limits below */
   MUON_ERR_RANGE = 4,       /* offset < 0 or offset + rows*cols > numel */
   MUON_ERR_OVERLAP = 5,     /* two entries overlap, or two buffers overlap */
   MUON_ERR_ALIGN = 6,       /* an offset not a multiple of 8 elements, or a buffer
@@ -109,12 +110,18 @@ enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 };
  * split_rows = 0 orthogonalises the whole matrix; split_rows = k > 0 cuts it
  * into rows/k blocks of k consecutive rows, each orthogonalised on its own with
  * its own norm (the "Muon Split" per-head orthogonalisation the article's TL;DR
- * mentions). */
+ * mentions). split_cols = k > 0 cuts it the same way into cols/k blocks of k
+ * consecutive columns: the per-head blocks of a projection whose input side
+ * holds the heads, as an attention output projection (rows x cols, y = W x)
+ * does. With both set the blocks are the split_rows x split_cols tiles, taken
+ * row of blocks by row of blocks. A block is read and written in place, with
+ * the matrix's row pitch (cols). */
 typedef struct {
   int64_t offset;
   int64_t rows;
   int64_t cols;
   int64_t split_rows;
+  int64_t split_cols;
 } muon_matrix_t;
 
 /* Hyperparameters of the Muon group. Fill with muon_default_hyper() first. */
@@ -273,13 +280,15 @@ int muon_unpack(void* const* dsts, const void* packed, int64_t numel, const muon
  * each owner's matrices out in its packed buffer, layer by layer. */
 
 /* One Muon-target matrix of the model: stored rows x cols (row-major),
- * split_rows as in muon_matrix_t, and the index of the layer it belongs to. */
+ * split_rows and split_cols as in muon_matrix_t, and the index of the layer it
+ * belongs to. */
 typedef struct {
   int64_t rows;
   int64_t cols;
   int64_t split_rows;
   int32_t layer;
   int32_t reserved;  /* set to 0 */
+  int64_t split_cols;
 } muon_param_t;
 
 /* Where a matrix went: its owner and its element offset in that owner's

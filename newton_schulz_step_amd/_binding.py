@@ -46,7 +46,8 @@ class MuonError(RuntimeError):
 
 class MuonMatrix(ctypes.Structure):
     _fields_ = [("offset", ctypes.c_int64), ("rows", ctypes.c_int64),
-                ("cols", ctypes.c_int64), ("split_rows", ctypes.c_int64)]
+                ("cols", ctypes.c_int64), ("split_rows", ctypes.c_int64),
+                ("split_cols", ctypes.c_int64)]
 
 
 class MuonHyper(ctypes.Structure):
@@ -64,7 +65,8 @@ class MuonWindow(ctypes.Structure):
 
 class MuonParam(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("split_rows", ctypes.c_int64),
-                ("layer", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("layer", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("split_cols", ctypes.c_int64)]
 
 
 class MuonAssign(ctypes.Structure):
@@ -178,11 +180,12 @@ def hyper(**kw) -> MuonHyper:
 
 
 def table(entries: Iterable[Sequence[int]]):
-    """ctypes array of muon_matrix_t from (offset, rows, cols[, split_rows]) tuples."""
-    rows = [tuple(e) + (0,) * (4 - len(e)) for e in entries]
+    """ctypes array of muon_matrix_t from (offset, rows, cols[, split_rows[,
+    split_cols]]) tuples."""
+    rows = [tuple(e) + (0,) * (5 - len(e)) for e in entries]
     arr = (MuonMatrix * max(len(rows), 1))()
-    for i, (o, r, c, s) in enumerate(rows):
-        arr[i] = MuonMatrix(o, r, c, s)
+    for i, (o, r, c, s, sc) in enumerate(rows):
+        arr[i] = MuonMatrix(o, r, c, s, sc)
     return arr, len(rows)
 
 
@@ -389,15 +392,15 @@ def ns_flops(m: int, n: int, method="standard", steps: int = 5) -> int:
 def plan_owners(params: Sequence[Sequence[int]], n_owners: int, method="standard",
                 steps: int = 5, align: int = 64):
     """Owner plan (muon_plan_owners) for matrices given as (rows, cols, split_rows,
-    layer). Returns (assign, owners): assign[i] = (owner, offset); owners[o] =
-    dict(numel, max_layer_numel, ns_flops, n_matrices, table), where `table` is
-    the owner's muon_step table [(offset, rows, cols, split_rows), ...] in
-    packed order, and `index` the matching input indices."""
-    rows = [tuple(p) for p in params]
+    layer[, split_cols]). Returns (assign, owners): assign[i] = (owner, offset);
+    owners[o] = dict(numel, max_layer_numel, ns_flops, n_matrices, table), where
+    `table` is the owner's muon_step table [(offset, rows, cols, split_rows,
+    split_cols), ...] in packed order, and `index` the matching input indices."""
+    rows = [tuple(p) + (0,) * (5 - len(p)) for p in params]
     n = len(rows)
     arr = (MuonParam * max(n, 1))()
-    for i, (r, c, s, layer) in enumerate(rows):
-        arr[i] = MuonParam(r, c, s, layer, 0)
+    for i, (r, c, s, layer, sc) in enumerate(rows):
+        arr[i] = MuonParam(r, c, s, layer, 0, sc)
     out_a = (MuonAssign * max(n, 1))()
     out_o = (MuonOwner * max(n_owners, 1))()
     _check(load().muon_plan_owners(arr, n, n_owners, _method_code(method), steps, align, out_a,
@@ -409,7 +412,8 @@ def plan_owners(params: Sequence[Sequence[int]], n_owners: int, method="standard
         owners.append({"numel": out_o[o].numel, "max_layer_numel": out_o[o].max_layer_numel,
                        "ns_flops": out_o[o].ns_flops, "n_matrices": out_o[o].n_matrices,
                        "index": idx,
-                       "table": [(assign[i][1], rows[i][0], rows[i][1], rows[i][2]) for i in idx]})
+                       "table": [(assign[i][1], rows[i][0], rows[i][1], rows[i][2], rows[i][4])
+                                 for i in idx]})
     return assign, owners
 
 

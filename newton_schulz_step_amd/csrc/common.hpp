@@ -24,12 +24,17 @@ namespace muon {
 // src_off + e; the step applies its update to e in [lo, hi) only, at params
 // index p_base + e (the whole problem at src_off + e for an ordinary step; a
 // window of a matrix that straddles a parameter partition otherwise).
+// Block element (r, c) of a problem (stored orientation) is at src_off + r * ld +
+// c in grads / momentum / update_out and at p_base + r * ld + c in params; its
+// local index r * ld + c is applied when lo <= index < hi.
 struct ProblemDesc {
   int64_t src_off;
   int64_t p_base;
   int64_t lo, hi;
   int32_t transposed;  // 1: stored rows x cols with rows > cols, canonical = stored^T
-  int32_t pad[3];
+  int32_t ld;          // row pitch in elements (the matrix's cols)
+  int32_t w;           // stored width (block cols); ld == w: the block is contiguous
+  int32_t pad;
 };
 
 // ---------------------------------------------------------------------------

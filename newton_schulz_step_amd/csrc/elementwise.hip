@@ -25,14 +25,17 @@ __global__ __launch_bounds__(256) void expand_desc_kernel(DescChunk c, ProblemDe
   const int64_t nblk = r.nblk_t >> 1;
   for (int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; b < nblk;
        b += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t first = b * r.size;
+    const int64_t bi = b / r.ncb;
+    const int64_t first = bi * r.rstep + (b - bi * r.ncb) * r.cstep;   // matrix flat index of element 0
     ProblemDesc d;
     d.src_off = r.offset + first;
     d.p_base = r.p0 + first;
-    d.lo = min(max(r.lo - first, int64_t(0)), r.size);
-    d.hi = min(max(r.hi - first, int64_t(0)), r.size);
+    d.lo = min(max(r.lo - first, int64_t(0)), r.span);
+    d.hi = min(max(r.hi - first, int64_t(0)), r.span);
     d.transposed = r.nblk_t & 1;
-    d.pad[0] = d.pad[1] = d.pad[2] = 0;
+    d.ld = r.ld;
+    d.w = r.w;
+    d.pad = 0;
     out[r.first + b] = d;
   }
 }
@@ -59,7 +62,10 @@ hipError_t launch_expand_desc(const EntryRec* entries, int n, ProblemDesc* out, 
 
 // One block of kMomThreads threads updates kMomChunk consecutive elements of one
 // problem, four per thread (one 16-byte momentum vector): many small blocks keep
-// the most reads and writes in flight across the HBM channels.
+// the most reads and writes in flight across the HBM channels. A problem's
+// elements are taken in its stored row-major order; a block narrower than its
+// matrix (a column block) steps from the end of one of its rows to the next
+// row's start, ld - w elements further.
 // The squares are summed in float64: the update does not depend on the scale of
 // M, and the square of an entry above ~1.8e19 overflows float32.
 template <int GDT>
@@ -72,16 +78,32 @@ __global__ __launch_bounds__(kMomThreads) void momentum_sumsq_kernel(float* M, c
   const int64_t c = b - p * chunks;
   const int64_t first = c * kMomChunk;                      // first element of the block within the problem
   const int len = static_cast<int>(min<int64_t>(kMomChunk, per_problem - first));
-  // a multiple of 8 elements, except for split blocks whose size is not
-  // (those take the element path: the vector path needs 16-byte momentum)
-  const int64_t start = probs[p].src_off + first;
+  const ProblemDesc pd = probs[p];
   const int tid = threadIdx.x;
   const int e0 = tid * 4;
+  // the thread's first element: stored address i0, column c0 of a w-wide row
+  // (w = INT_MAX for a contiguous problem: its rows run into each other)
+  int64_t i0;
+  int c0, w;
+  if (pd.ld == pd.w) {
+    i0 = pd.src_off + first + e0;
+    c0 = 0;
+    w = 0x7fffffff;
+  } else {
+    const int64_t e = first + e0;
+    const int64_t r = e / pd.w;
+    c0 = static_cast<int>(e - r * pd.w);
+    i0 = pd.src_off + r * pd.ld + c0;
+    w = pd.w;
+  }
   double ss = 0.0;
-  if (e0 + 4 <= len && ((start + e0) & 3) == 0) {
+  // the vector path needs 4 elements in one row and 16-byte aligned momentum
+  // (a block's rows need not be: a split block or column block whose width is
+  // not a multiple of 4, or a matrix at an offset that is not)
+  if (e0 + 4 <= len && c0 + 4 <= w && (i0 & 3) == 0) {
     float g[4];
-    load_grad4<GDT>(G, start + e0, g);
-    f32x4* mp = reinterpret_cast<f32x4*>(M + start + e0);
+    load_grad4<GDT>(G, i0, g);
+    f32x4* mp = reinterpret_cast<f32x4*>(M + i0);
     f32x4 m = *mp;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -89,12 +111,18 @@ __global__ __launch_bounds__(kMomThreads) void momentum_sumsq_kernel(float* M, c
       ss += static_cast<double>(m[e]) * m[e];
     }
     *mp = m;
-  } else {
+  } else if (e0 < len) {
+    int64_t i = i0;
+    int c = c0;
     for (int e = e0; e < min(e0 + 4, len); ++e) {
-      const int64_t i = start + e;
       const float m = mu * M[i] + grad_to_f32<GDT>(G, i);
       M[i] = m;
       ss += static_cast<double>(m) * m;
+      ++i;
+      if (++c == w) {   // next row of the block
+        c = 0;
+        i += pd.ld - w;
+      }
     }
   }
   ss = wave_sum_d(ss);
@@ -205,7 +233,7 @@ __global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const Prob
   T* Xp = X + p * static_cast<int64_t>(mp) * np;
 
   if (!pd.transposed) {
-    // stored m x n: element (i, j) at src + i * n + j
+    // stored m x n: element (i, j) at src + i * ld + j
     if (t >= per_r) return;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r0 = (t / pieces_j) * 16 + 4 * w, c0 = (t % pieces_j) * 1024 + 4 * lane;
@@ -213,7 +241,7 @@ __global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const Prob
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int gi = r0 + (q >> 2), gj = c0 + 256 * (q & 3);
-      const int64_t base = pd.src_off + static_cast<int64_t>(gi) * n + gj;
+      const int64_t base = pd.src_off + static_cast<int64_t>(gi) * pd.ld + gj;
       if (gi < m && gj + 4 <= n && (base & 3) == 0) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(M + base);
 #pragma unroll
@@ -237,7 +265,7 @@ __global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const Prob
   }
 
   if (t >= per_t) return;
-  // stored n x m: element (i, j) at src + j * m + i. The block covers canonical rows
+  // stored n x m: element (i, j) at src + j * ld + i. The block covers canonical rows
   // i0 .. i0 + 255 (tiles q = 0..3 of 64 rows) and columns j0 .. j0 + 63: stored rows
   // j0 .. j0 + 63, read in 1 KB pieces. All loads are issued first; each tile is
   // then turned in LDS: stored row j0 + 16 k + rr holds canonical column j, and its
@@ -252,7 +280,7 @@ __global__ __launch_bounds__(256) void prep_x0_kernel(const float* M, const Prob
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int sj = j0 + 16 * k + rr, si = i0 + 64 * q + c4;
-        const int64_t base = pd.src_off + static_cast<int64_t>(sj) * m + si;
+        const int64_t base = pd.src_off + static_cast<int64_t>(sj) * pd.ld + si;
         if (sj < n && si + 4 <= m && (base & 3) == 0) {
           const f32x4 w = *reinterpret_cast<const f32x4*>(M + base);
 #pragma unroll

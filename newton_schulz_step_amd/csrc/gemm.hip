@@ -552,12 +552,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   const int gj_w = tj * TILE + wn * HALF;   // first column
   const bool diag = SYM && (ti == tj);
 
-  int transposed = 0;
+  int transposed = 0, ld = 0;
   int64_t src = 0, pb = 0, wlo = 0, whi = 0;
   constexpr bool APPLY = (EPI == EPI_APPLY || EPI == EPI_APPLY_BF16);
   if constexpr (APPLY) {
     const ProblemDesc pd = a.probs[prob];
     transposed = pd.transposed;
+    ld = pd.ld;
     src = pd.src_off;
     pb = pd.p_base;
     wlo = pd.lo;
@@ -650,7 +651,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
     if (!(APPLY && !transposed) && i + 1 < WB) load_d(i + 1);
 
     if (APPLY && !transposed) {
-      // stored m x n: canonical (gi, gj) is stored element gi * n + gj. Each lane
+      // stored m x n: canonical (gi, gj) is local index gi * ld + gj. Each lane
       // reads back the chunks it wrote; parameters are loaded PB chunks at a time,
       // all of a batch before any is used.
 #pragma unroll
@@ -661,7 +662,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
         for (int u = 0; u < PB; ++u) {
           const int q = lane + 64 * (b + u);
           const int gi = gi_w + i * 32 + q / CPR, gj = gj_w + (q % CPR) * 8;
-          const int64_t e = static_cast<int64_t>(gi) * n + gj;
+          const int64_t e = static_cast<int64_t>(gi) * ld + gj;
           pvec[u] = gi < m && gj + 8 <= n && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
           if (pvec[u]) load_p8<EPI>(a.params, pb + e, p0[u], p1[u]);
         }
@@ -676,7 +677,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
             const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) { v[e] = s0[e]; v[e + 4] = s1[e]; }
-            const int64_t e = static_cast<int64_t>(gi) * n + gj;
+            const int64_t e = static_cast<int64_t>(gi) * ld + gj;
             apply8<EPI>(a, pb + e, src + e, e, min(8, n - gj), wlo, whi, v, p0[u], p1[u], pvec[u]);
           }
         }
@@ -688,7 +689,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
     if (need_col) {
       lds_order();
       if constexpr (APPLY) {
-        // stored n x m: canonical (gi, gj) is stored element gj * m + gi
+        // stored n x m: canonical (gi, gj) is local index gj * ld + gi
 #pragma unroll
         for (int b = 0; b < NC; b += PB) {
           f32x4 c0[PB], c1[PB];
@@ -697,7 +698,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
           for (int u = 0; u < PB; ++u) {
             const int q = lane + 64 * (b + u);
             const int gi = gi_w + i * 32 + (q & 3) * 8, gj = gj_w + (q >> 2);
-            const int64_t e = static_cast<int64_t>(gj) * m + gi;
+            const int64_t e = static_cast<int64_t>(gj) * ld + gi;
             cvec[u] = gj < n && gi + 8 <= m && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
             if (cvec[u]) load_p8<EPI>(a.params, pb + e, c0[u], c1[u]);
           }
@@ -710,7 +711,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
               float w[8];
 #pragma unroll
               for (int e = 0; e < 8; ++e) w[e] = stg[srow(r8 + e, cc)];
-              const int64_t e = static_cast<int64_t>(gj) * m + gi;
+              const int64_t e = static_cast<int64_t>(gj) * ld + gi;
               apply8<EPI>(a, pb + e, src + e, e, min(8, m - gi), wlo, whi, w, c0[u], c1[u], cvec[u]);
             }
           }
@@ -1267,7 +1268,7 @@ __global__ __launch_bounds__(256) void prep_gram_kernel(PrepGramArgs a) {
     bool ok, vec;
     if (!pd.transposed) {                 // row r, columns jt*128 + hh*64 ..
       const int k0 = jt * 128 + hh * 64;
-      base = pd.src_off + static_cast<int64_t>(r) * n + k0;
+      base = pd.src_off + static_cast<int64_t>(r) * pd.ld + k0;
       ok = r < m;
       vec = ok && k0 + 64 <= n && (base & 3) == 0;
 #pragma unroll
@@ -1282,7 +1283,7 @@ __global__ __launch_bounds__(256) void prep_gram_kernel(PrepGramArgs a) {
       }
     } else {                              // stored row jt*128 + r, elements hh*64 ..
       const int kk = jt * 128 + r, i0 = hh * 64;
-      base = pd.src_off + static_cast<int64_t>(kk) * m + i0;
+      base = pd.src_off + static_cast<int64_t>(kk) * pd.ld + i0;
       ok = kk < n;
       vec = ok && i0 + 64 <= m && (base & 3) == 0;
 #pragma unroll

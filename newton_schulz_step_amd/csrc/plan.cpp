@@ -64,16 +64,22 @@ int validate(const muon_matrix_t* table, int32_t n_entries, const muon_hyper_t* 
     if (e.rows < 1 || e.cols < 1) { err = "rows and cols must be >= 1" + at; return MUON_ERR_BAD_SHAPE; }
     if (e.split_rows < 0) { err = "split_rows < 0" + at; return MUON_ERR_BAD_SHAPE; }
     if (e.split_rows > 0 && e.rows % e.split_rows != 0) { err = "split_rows does not divide rows" + at; return MUON_ERR_BAD_SHAPE; }
+    if (e.split_cols < 0) { err = "split_cols < 0" + at; return MUON_ERR_BAD_SHAPE; }
+    if (e.split_cols > 0 && e.cols % e.split_cols != 0) { err = "split_cols does not divide cols" + at; return MUON_ERR_BAD_SHAPE; }
     const int64_t pr = e.split_rows > 0 ? e.split_rows : e.rows;
-    const int64_t m = std::min(pr, e.cols), n = std::max(pr, e.cols);
-    if (m > MUON_MAX_SHORT_SIDE || n > MUON_MAX_LONG_SIDE) { err = "matrix beyond the size limits" + at; return MUON_ERR_BAD_SHAPE; }
+    const int64_t pc = e.split_cols > 0 ? e.split_cols : e.cols;
+    const int64_t m = std::min(pr, pc), n = std::max(pr, pc);
+    if (m > MUON_MAX_SHORT_SIDE || n > MUON_MAX_LONG_SIDE || e.cols > MUON_MAX_LONG_SIDE) {
+      err = "matrix beyond the size limits" + at;
+      return MUON_ERR_BAD_SHAPE;
+    }
     // running totals, compared without overflow: rows <= (limit - elements) / cols
     if (e.rows > (MUON_MAX_TABLE_ELEMENTS - elements) / e.cols) {
       err = "the table holds more than MUON_MAX_TABLE_ELEMENTS elements" + at;
       return MUON_ERR_BAD_SHAPE;
     }
     elements += e.rows * e.cols;
-    problems += e.rows / pr;
+    problems += (e.rows / pr) * (e.cols / pc);
     if (problems > MUON_MAX_PROBLEMS) { err = "the table expands to more than MUON_MAX_PROBLEMS problems" + at; return MUON_ERR_BAD_SHAPE; }
     if (e.offset < 0) { err = "offset < 0" + at; return MUON_ERR_RANGE; }
     if (e.offset > INT64_MAX - MUON_MAX_TABLE_ELEMENTS) { err = "offset beyond the addressable range" + at; return MUON_ERR_RANGE; }
@@ -115,11 +121,20 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
   std::map<std::pair<int64_t, int64_t>, int> gid;
   std::vector<std::vector<HostProblem>> per_group;
   std::vector<std::pair<int, size_t>> entry_pos;   // (group, index of its first problem in the group)
+  // block geometry of entry i: pr x pc blocks, nrb x ncb of them
+  struct Geom { int64_t pr, pc, nrb, ncb; };
+  auto geom = [&](const muon_matrix_t& e) {
+    Geom q;
+    q.pr = e.split_rows > 0 ? e.split_rows : e.rows;
+    q.pc = e.split_cols > 0 ? e.split_cols : e.cols;
+    q.nrb = e.rows / q.pr;
+    q.ncb = e.cols / q.pc;
+    return q;
+  };
   for (int32_t i = 0; i < n_entries; ++i) {
     const muon_matrix_t& e = table[i];
-    const int64_t pr = e.split_rows > 0 ? e.split_rows : e.rows;
-    const int64_t nblk = e.rows / pr;
-    const int64_t m = std::min(pr, e.cols), n = std::max(pr, e.cols);
+    const Geom q = geom(e);
+    const int64_t m = std::min(q.pr, q.pc), n = std::max(q.pr, q.pc);
     const auto key = std::make_pair(m, n);
     auto it = gid.find(key);
     int g;
@@ -134,21 +149,22 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
       g = it->second;
     }
     entry_pos.emplace_back(g, per_group[g].size());
-    for (int64_t b = 0; b < nblk; ++b) {
+    const int64_t span = (q.pr - 1) * e.cols + q.pc;   // a block's last local index + 1
+    for (int64_t b = 0; b < q.nrb * q.ncb; ++b) {
       HostProblem p;
-      const int64_t first = b * pr * e.cols;       // entry flat index of the block's element 0
-      const int64_t size = pr * e.cols;
+      const int64_t first = (b / q.ncb) * q.pr * e.cols + (b % q.ncb) * q.pc;   // matrix flat index of element 0
       p.src_off = e.offset + first;
-      p.transposed = pr > e.cols ? 1 : 0;
+      p.ld = static_cast<int32_t>(e.cols);
+      p.transposed = q.pr > q.pc ? 1 : 0;
       p.entry = i;
       if (windows == nullptr) {
         p.lo = 0;
-        p.hi = size;
+        p.hi = span;
         p.p_base = p.src_off;
       } else {
         const muon_window_t& w = windows[i];
-        p.lo = std::min(std::max(w.lo - first, int64_t(0)), size);
-        p.hi = std::min(std::max(w.hi - first, int64_t(0)), size);
+        p.lo = std::min(std::max(w.lo - first, int64_t(0)), span);
+        p.hi = std::min(std::max(w.hi - first, int64_t(0)), span);
         p.p_base = w.param_offset - w.lo + first;
       }
       per_group[g].push_back(p);
@@ -165,10 +181,15 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
   }
   for (int32_t i = 0; i < n_entries; ++i) {
     const muon_matrix_t& e = table[i];
-    const int64_t pr = e.split_rows > 0 ? e.split_rows : e.rows;
+    const Geom q = geom(e);
     EntryRec r{};
     r.offset = e.offset;
-    r.size = pr * e.cols;
+    r.rstep = q.pr * e.cols;
+    r.span = (q.pr - 1) * e.cols + q.pc;
+    r.cstep = static_cast<int32_t>(q.pc);
+    r.ncb = static_cast<int32_t>(q.ncb);
+    r.ld = static_cast<int32_t>(e.cols);
+    r.w = static_cast<int32_t>(q.pc);
     if (windows == nullptr) {
       r.lo = 0;
       r.hi = e.rows * e.cols;
@@ -179,7 +200,7 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
       r.p0 = windows[i].param_offset - windows[i].lo;
     }
     r.first = L.groups[entry_pos[i].first].first + static_cast<int32_t>(entry_pos[i].second);
-    r.nblk_t = static_cast<int32_t>(((e.rows / pr) << 1) | (pr > e.cols ? 1 : 0));
+    r.nblk_t = static_cast<int32_t>(((q.nrb * q.ncb) << 1) | (q.pr > q.pc ? 1 : 0));
     L.entries.push_back(r);
   }
   // momentum blocks: each problem is cut into blocks of kMomChunk elements; the

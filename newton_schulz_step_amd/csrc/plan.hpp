@@ -13,10 +13,13 @@
 
 namespace muon {
 
+// A problem is a block of a matrix: block element (r, c) is stored at src_off +
+// r * ld + c (ld = the matrix's cols), and its local index is r * ld + c.
 struct HostProblem {
   int64_t src_off;
-  int64_t p_base;      // params index of local flat element 0
-  int64_t lo, hi;      // local flat elements whose update is applied
+  int64_t p_base;      // params index of local index 0
+  int64_t lo, hi;      // local indices whose update is applied
+  int32_t ld;
   int32_t transposed;
   int32_t entry;
 };
@@ -35,16 +38,22 @@ struct Group {
   size_t r2 = 0, p[2] = {0, 0}, t = 0;   // gram: next R, P (ping-pong), R Q
 };
 
-// What the descriptor kernel needs to write the problems of one table entry:
-// problem b (b < nblk) of the entry is problem first + b of the layout, with
-// src_off = offset + b * size, p_base = p0 + b * size, and the part of [lo, hi)
-// (flat in the matrix) that falls in [b * size, (b + 1) * size), shifted to the
-// block.
+// What the descriptor kernel needs to write the problems of one table entry.
+// Problem b (b < nblk) of the entry is problem first + b of the layout: block
+// (b / ncb, b % ncb) of the matrix, whose element 0 is flat element
+// f = (b / ncb) * rstep + (b % ncb) * cstep of the matrix; src_off = offset + f,
+// p_base = p0 + f, and [lo, hi) (flat in the matrix) shifted by f and clamped to
+// [0, span], span = the block's last local index + 1.
 struct EntryRec {
   int64_t offset;   // element offset of the matrix in grads / momentum
-  int64_t size;     // elements of one problem (block rows x cols)
+  int64_t rstep;    // flat elements between vertically adjacent blocks (block rows x cols)
+  int64_t span;     // (block rows - 1) x cols + block cols
   int64_t lo, hi;   // elements of the flattened matrix whose update is applied
   int64_t p0;       // params index of flat element 0 of the matrix
+  int32_t cstep;    // block cols
+  int32_t ncb;      // blocks per row of blocks
+  int32_t ld;       // the matrix's cols
+  int32_t w;        // stored block width (block cols)
   int32_t first;    // layout index of the entry's first problem
   int32_t nblk_t;   // problems of the entry << 1 | transposed
 };

@@ -61,12 +61,23 @@ int plan_owners(const muon_param_t* params, int32_t n_params, int32_t n_owners, 
       err = "split_rows must be 0 or divide rows" + at;
       return MUON_ERR_BAD_SHAPE;
     }
+    if (p.split_cols < 0 || (p.split_cols > 0 && p.cols % p.split_cols != 0)) {
+      err = "split_cols must be 0 or divide cols" + at;
+      return MUON_ERR_BAD_SHAPE;
+    }
     if (p.layer < 0) { err = "layer < 0" + at; return MUON_ERR_BAD_SHAPE; }
     const int64_t pr = p.split_rows > 0 ? p.split_rows : p.rows;
-    const int64_t m = std::min(pr, p.cols), n = std::max(pr, p.cols);
-    if (m > MUON_MAX_SHORT_SIDE || n > MUON_MAX_LONG_SIDE) { err = "matrix beyond the size limits" + at; return MUON_ERR_BAD_SHAPE; }
+    const int64_t pc = p.split_cols > 0 ? p.split_cols : p.cols;
+    const int64_t m = std::min(pr, pc), n = std::max(pr, pc);
+    if (m > MUON_MAX_SHORT_SIDE || n > MUON_MAX_LONG_SIDE || p.cols > MUON_MAX_LONG_SIDE) {
+      err = "matrix beyond the size limits" + at;
+      return MUON_ERR_BAD_SHAPE;
+    }
     const int64_t f = ns_flops(m, n, method, steps);
-    if (f < 0 || !mul_ok(f, p.rows / pr, cost[i])) { err = "FLOP count overflows int64" + at; return MUON_ERR_RANGE; }
+    if (f < 0 || !mul_ok(f, (p.rows / pr) * (p.cols / pc), cost[i])) {
+      err = "FLOP count overflows int64" + at;
+      return MUON_ERR_RANGE;
+    }
     size[i] = p.rows * p.cols;
   }
 

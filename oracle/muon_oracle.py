@@ -40,7 +40,9 @@ Readings where the pages leave a step open (each also listed in the design notes
     alpha = -lr).
   * Per-head split ("Muon Split" in the article's TL;DR): split_rows = k cuts a
     matrix into rows/k blocks of k rows; each block is its own problem, with its
-    own norm.
+    own norm. split_cols = k cuts it into cols/k blocks of k columns the same way
+    (the heads of a projection whose input side holds them); with both, the
+    blocks are the split_rows x split_cols tiles.
   * AdamW: bias-corrected moments, eps added outside the square root, decoupled
     weight decay applied before the moment step (the article's AdamW mode).
 
@@ -180,15 +182,22 @@ def orthogonalise(Y: np.ndarray, method: str = "standard", steps: int = NS_STEPS
     return O.T if transposed else O
 
 
-def problem_blocks(rows: int, cols: int, split_rows: int):
-    """(first row, row count) of each independent problem of one entry."""
-    if split_rows <= 0:
-        return [(0, rows)]
-    return [(r, split_rows) for r in range(0, rows, split_rows)]
+def problem_blocks(rows: int, cols: int, split_rows: int, split_cols: int = 0):
+    """(first row, row count, first column, column count) of each independent
+    problem of one entry, row of blocks by row of blocks."""
+    pr = split_rows if split_rows > 0 else rows
+    pc = split_cols if split_cols > 0 else cols
+    return [(r, pr, c, pc) for r in range(0, rows, pr) for c in range(0, cols, pc)]
+
+
+def _entry(e):
+    """(offset, rows, cols, split_rows, split_cols) of a 4- or 5-field table entry."""
+    off, rows, cols, split_rows = e[:4]
+    return off, rows, cols, split_rows, (e[4] if len(e) > 4 else 0)
 
 
 def muon_step(params: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
-              table: Sequence[Tuple[int, int, int, int]], lr: float = 0.02,
+              table: Sequence[Sequence[int]], lr: float = 0.02,
               mu: float = 0.95, weight_decay: float = 0.0, method: str = "standard",
               steps: int = NS_STEPS, coeffs: Tuple[float, float, float] = (NS_A, NS_B, NS_C),
               eps: float = NS_EPS, store_fmt: Optional[str] = None,
@@ -196,8 +205,9 @@ def muon_step(params: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
     """One Muon step over a packed buffer described by `table`.
 
     params/grads/momentum: flat arrays of the packed buffer ([DM]: one contiguous
-    buffer per owner). table: (offset, rows, cols, split_rows) per entry, each
-    matrix row-major at `offset` ([DS]: grads are recovered by reshape(p.shape)).
+    buffer per owner). table: (offset, rows, cols, split_rows[, split_cols]) per
+    entry, each matrix row-major at `offset` ([DS]: grads are recovered by
+    reshape(p.shape)).
     Returns float64 copies of the new params, new momentum and the update O
     (zero outside the entries). `entries` restricts the work to those entries.
     [DS] 核心算子: p <- p * (1 - lr * wd), then p <- p - lr * O.
@@ -208,35 +218,36 @@ def muon_step(params: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
     O_all = np.zeros_like(p)
     idx = range(len(table)) if entries is None else entries
     for i in idx:
-        off, rows, cols, split = table[i]
+        off, rows, cols, split_r, split_c = _entry(table[i])
         span = slice(off, off + rows * cols)
         M[span] = momentum_update(M[span], G[span], mu)
         Mm = M[span].reshape(rows, cols)
         O = np.empty((rows, cols))
-        for r0, nr in problem_blocks(rows, cols, split):
-            O[r0:r0 + nr] = orthogonalise(Mm[r0:r0 + nr], method, steps, coeffs, eps,
-                                          store_fmt)
+        for r0, nr, c0, nc in problem_blocks(rows, cols, split_r, split_c):
+            O[r0:r0 + nr, c0:c0 + nc] = orthogonalise(Mm[r0:r0 + nr, c0:c0 + nc], method, steps,
+                                                      coeffs, eps, store_fmt)
         O_all[span] = O.ravel()
         p[span] = p[span] * (1.0 - lr * weight_decay)
         p[span] = p[span] - lr * O_all[span]
     return {"params": p, "momentum": M, "update": O_all}
 
 
-def partition_windows(table: Sequence[Tuple[int, int, int, int]], start: int,
+def partition_windows(table: Sequence[Sequence[int]], start: int,
                       stop: int) -> List[Tuple[int, int, int]]:
     """(lo, hi, param_offset) per entry for the holder of the flat partition
     [start, stop) of the full layout: the part of each matrix (flattened in
     stored row-major order) that falls in the partition, and where it sits in
     the partition. (0, 0, 0) for a matrix the partition does not touch."""
     out = []
-    for off, rows, cols, _s in table:
+    for e in table:
+        off, rows, cols = e[:3]
         a, b = max(start, off), min(stop, off + rows * cols)
         out.append((a - off, b - off, a - start) if a < b else (0, 0, 0))
     return out
 
 
 def window_step(partition: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
-                table: Sequence[Tuple[int, int, int, int]],
+                table: Sequence[Sequence[int]],
                 windows: Sequence[Tuple[int, int, int]], lr: float = 0.02,
                 weight_decay: float = 0.0, **kw) -> Dict[str, np.ndarray]:
     """One Muon step for the holder of a flat parameter partition.
@@ -254,7 +265,8 @@ def window_step(partition: np.ndarray, grads: np.ndarray, momentum: np.ndarray,
     full = muon_step(np.zeros(len(momentum)), grads, momentum, table, lr=0.0, **kw)
     part = np.asarray(partition, dtype=np.float64).copy()
     O = full["update"]
-    for (off, _r, _c, _s), (lo, hi, po) in zip(table, windows):
+    for e, (lo, hi, po) in zip(table, windows):
+        off = e[0]
         if hi <= lo:
             continue
         span = slice(po, po + hi - lo)
@@ -278,15 +290,15 @@ def adamw_step(p: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, lr: f
     return p, m, v
 
 
-def pack(arrays: Sequence[np.ndarray], table: Sequence[Tuple[int, int, int, int]],
+def pack(arrays: Sequence[np.ndarray], table: Sequence[Sequence[int]],
          numel: int, dtype=np.float32) -> np.ndarray:
     """[DM] packed buffer: each matrix copied row-major to its offset; gaps zero."""
     out = np.zeros(numel, dtype=dtype)
-    for arr, (off, rows, cols, _s) in zip(arrays, table):
+    for arr, e in zip(arrays, table):
+        off, rows, cols = e[:3]
         out[off:off + rows * cols] = np.asarray(arr).reshape(rows * cols)
     return out
 
 
-def unpack(packed: np.ndarray, table: Sequence[Tuple[int, int, int, int]]):
-    return [packed[off:off + rows * cols].reshape(rows, cols).copy()
-            for off, rows, cols, _s in table]
+def unpack(packed: np.ndarray, table: Sequence[Sequence[int]]):
+    return [packed[e[0]:e[0] + e[1] * e[2]].reshape(e[1], e[2]).copy() for e in table]

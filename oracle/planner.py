@@ -49,10 +49,11 @@ def ns_flops(m: int, n: int, method: str = "standard", steps: int = 5) -> int:
 
 
 def matrix_flops(rows: int, cols: int, split_rows: int, method: str = "standard",
-                 steps: int = 5) -> int:
+                 steps: int = 5, split_cols: int = 0) -> int:
     """FLOPs of one matrix: its problems (the whole matrix, or each split block)."""
     pr = split_rows if split_rows > 0 else rows
-    return (rows // pr) * ns_flops(min(pr, cols), max(pr, cols), method, steps)
+    pc = split_cols if split_cols > 0 else cols
+    return (rows // pr) * (cols // pc) * ns_flops(min(pr, pc), max(pr, pc), method, steps)
 
 
 def lpt(costs: Sequence[int], sizes: Sequence[int], n_owners: int) -> List[int]:
@@ -72,11 +73,12 @@ def lpt(costs: Sequence[int], sizes: Sequence[int], n_owners: int) -> List[int]:
 
 def plan_owners(params: Sequence[Tuple[int, int, int, int]], n_owners: int,
                 method: str = "standard", steps: int = 5, align: int = 64) -> Dict:
-    """params: (rows, cols, split_rows, layer) per matrix. Returns
+    """params: (rows, cols, split_rows, layer[, split_cols]) per matrix. Returns
     {"assign": [(owner, offset)], "owners": [dict(numel, max_layer_numel,
     ns_flops, n_matrices)]}."""
-    costs = [matrix_flops(r, c, s, method, steps) for r, c, s, _l in params]
-    sizes = [r * c for r, c, _s, _l in params]
+    costs = [matrix_flops(q[0], q[1], q[2], method, steps, q[4] if len(q) > 4 else 0)
+             for q in params]
+    sizes = [q[0] * q[1] for q in params]
     owner = lpt(costs, sizes, n_owners)
     offset = [0] * len(params)
     owners = []

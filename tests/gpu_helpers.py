@@ -33,8 +33,16 @@ def run_step(nss, params, grads, mom, tab, h, shadow=False, dev="cuda:0", steps=
     return out
 
 
+def block_grid(e):
+    """(first row, rows, first column, cols) of each independent block of a
+    workload entry: split_rows x split_cols tiles (0 = the whole side)."""
+    pr = e.split_rows or e.rows
+    pc = e.split_cols or e.cols
+    return [(r, pr, c, pc) for r in range(0, e.rows, pr) for c in range(0, e.cols, pc)]
+
+
 def entry_slices(tab):
-    return [slice(o, o + r * c) for o, r, c, _ in tab]
+    return [slice(o, o + r * c) for o, r, c, *_ in tab]
 
 
 def outside_mask(tab, n):

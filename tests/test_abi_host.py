@@ -71,6 +71,11 @@ def test_workspace_size_validation(lib):
     assert _ws([(0, 4, -1, 0)])[0] == nss.ERR_BAD_SHAPE
     assert _ws([(0, 12, 4, 5)])[0] == nss.ERR_BAD_SHAPE          # split does not divide rows
     assert _ws([(0, 12, 4, -2)])[0] == nss.ERR_BAD_SHAPE
+    assert _ws([(0, 4, 12, 0, 5)])[0] == nss.ERR_BAD_SHAPE       # split_cols does not divide cols
+    assert _ws([(0, 4, 12, 0, -3)])[0] == nss.ERR_BAD_SHAPE
+    assert _ws([(0, 4, 12, 0, 13)])[0] == nss.ERR_BAD_SHAPE
+    assert _ws([(0, 8, 12, 4, 6)])[0] == nss.OK                  # a grid of 4 x 6 tiles
+    assert _ws([(0, 2, (1 << 24) + 8, 0, 8)])[0] == nss.ERR_BAD_SHAPE   # row pitch beyond the long side
     assert _ws([(0, 20000, 20000, 0)])[0] == nss.ERR_BAD_SHAPE   # short side beyond the limit
     assert _ws([(-8, 4, 4, 0)])[0] == nss.ERR_RANGE
     assert _ws([(4, 4, 4, 0)])[0] == nss.ERR_ALIGN
@@ -82,6 +87,23 @@ def test_workspace_size_validation(lib):
     assert _ws([(0, 4, 4, 0)], lr=float("nan"))[0] == nss.ERR_BAD_HYPER
     st, msg = _ws([(0, 4, 4, 0)], ns_method=7)
     assert "standard" in msg and "gram" in msg
+
+
+def test_column_split_layout(lib):
+    # a 4096 x 4096 matrix split into 32 column blocks has the same problems
+    # (32 of canonical shape 128 x 4096) as the same matrix split by rows, so
+    # the same workspace; a grid has one problem per tile
+    for method, dt in (("standard", "bf16"), ("gram", "f16")):
+        kw = dict(ns_method=method, ns_dtype=dt)
+        by_rows = nss.workspace_size([(0, 4096, 4096, 128)], nss.hyper(**kw))
+        by_cols = nss.workspace_size([(0, 4096, 4096, 0, 128)], nss.hyper(**kw))
+        assert by_rows == by_cols
+        grid = nss.workspace_size([(0, 512, 768, 256, 384)], nss.hyper(**kw))
+        tiles = nss.workspace_size([(i * 256 * 384, 256, 384, 0) for i in range(4)], nss.hyper(**kw))
+        assert grid == tiles
+    # the problem limit counts column blocks too
+    st, msg = _ws([(0, 1 << 13, 1 << 12, 1, 1)])
+    assert st == nss.ERR_BAD_SHAPE and "MUON_MAX_PROBLEMS" in msg
 
 
 def test_table_wide_limits(lib):
@@ -244,24 +266,29 @@ def test_random_tables_get_the_status_of_their_one_violation(lib):
     # call); valid ones go through the host-only muon_workspace_size.
     rng = np.random.default_rng(77)
     h = nss.hyper(ns_method="standard", ns_dtype="bf16")
-    kinds = ["none", "zero_rows", "bad_split", "misaligned", "duplicate", "short", "negative"]
+    kinds = ["none", "zero_rows", "bad_split", "misaligned", "duplicate", "short", "negative",
+             "bad_col_split"]
     want = {"none": nss.OK, "zero_rows": nss.ERR_BAD_SHAPE, "bad_split": nss.ERR_BAD_SHAPE,
             "misaligned": nss.ERR_ALIGN, "duplicate": nss.ERR_OVERLAP, "short": nss.ERR_RANGE,
-            "negative": nss.ERR_RANGE}
-    for case in range(600):
+            "negative": nss.ERR_RANGE, "bad_col_split": nss.ERR_BAD_SHAPE}
+    for case in range(640):
         ents, cur = [], 0
         for _ in range(int(rng.integers(1, 7))):
             r, c = int(rng.integers(1, 300)), int(rng.integers(1, 300))
             divs = [d for d in range(1, r + 1) if r % d == 0]
+            cdivs = [d for d in range(1, c + 1) if c % d == 0]
             split = int(rng.choice(divs)) if rng.random() < 0.3 else 0
+            csplit = int(rng.choice(cdivs)) if rng.random() < 0.3 else 0
             cur += 8 * int(rng.integers(1, 4))
-            ents.append([cur, r, c, split])
+            ents.append([cur, r, c, split, csplit])
             cur = (cur + r * c + 7) // 8 * 8
         numel = cur + 8 * int(rng.integers(1, 4))
         kind = kinds[case % len(kinds)]
         k = int(rng.integers(len(ents)))
         if kind == "zero_rows":
             ents[k][1], ents[k][3] = 0, 0
+        elif kind == "bad_col_split":
+            ents[k][4] = ents[k][2] + 1 if rng.random() < 0.5 else -1
         elif kind == "bad_split":
             ents[k][3] = ents[k][1] + 1
         elif kind == "misaligned":

@@ -22,7 +22,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import rel, to_device, top_subspace_err
+from gpu_helpers import block_grid, rel, to_device, top_subspace_err
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
 
@@ -49,16 +49,12 @@ def _device_inputs(wl, sample, dev):
     return params, grads, mom, host
 
 
-def _blocks(e):
-    return [(0, e.rows)] if e.split_rows == 0 else \
-        [(r, e.split_rows) for r in range(0, e.rows, e.split_rows)]
-
-
 def _run(nss, wid, method, ns_dtype, sample):
+    """wid: a workload number, or a Workload."""
     import torch
     dev = "cuda:0"
-    wl = W.workload(wid)
-    print(f"[case] workload {wid} ({wl.title}) {method}/{ns_dtype} sample {sample}", flush=True)
+    wl = W.workload(wid) if isinstance(wid, int) else wid
+    print(f"[case] workload {wl.wid} ({wl.title}) {method}/{ns_dtype} sample {sample}", flush=True)
     params, grads, mom, host = _device_inputs(wl, sample, dev)
     upd = torch.zeros_like(params)
     h = nss.hyper(ns_method=method, ns_dtype=ns_dtype, grad_dtype="bf16", lr=wl.lr,
@@ -75,12 +71,12 @@ def _run(nss, wid, method, ns_dtype, sample):
         M = mom[sl].cpu().numpy().reshape(e.rows, e.cols)
         g, p0 = host[i]
         g64 = W.grad_as_f64(wl, g.ravel())
-        tab = [(0, e.rows, e.cols, e.split_rows)]
+        tab = [(0, e.rows, e.cols, e.split_rows, e.split_cols)]
         t0 = time.time()
         kw = dict(lr=wl.lr, mu=wl.momentum, weight_decay=wl.weight_decay, method=method)
         ref = oracle.muon_step(p0.ravel(), g64, np.zeros(g64.size), tab, store_fmt=ns_dtype, **kw)
         exact = oracle.muon_step(p0.ravel(), g64, np.zeros(g64.size), tab, **kw)
-        print(f"  entry {i} {e.rows}x{e.cols}/{e.split_rows}: oracle {time.time() - t0:.1f} s",
+        print(f"  entry {i} {e.rows}x{e.cols}/{e.split_rows}/{e.split_cols}: oracle {time.time() - t0:.1f} s",
               flush=True)
         Of = ref["update"].reshape(e.rows, e.cols)
         Oe = exact["update"].reshape(e.rows, e.cols)
@@ -94,9 +90,10 @@ def _run(nss, wid, method, ns_dtype, sample):
         p0d = p0.astype(np.float64)
         ea = rel(P - p0d, p0d * decay - np.float64(np.float32(wl.lr)) * O - p0d)
         worst_sub = 0.0
-        for r0, nr in _blocks(e):
-            Mb, Ob, Oeb = Me[r0:r0 + nr], O[r0:r0 + nr], Oe[r0:r0 + nr]
-            if nr > e.cols:
+        for r0, nr, c0, nc in block_grid(e):
+            bs = (slice(r0, r0 + nr), slice(c0, c0 + nc))
+            Mb, Ob, Oeb = Me[bs], O[bs], Oe[bs]
+            if nr > nc:
                 Mb, Ob, Oeb = Mb.T, Ob.T, Oeb.T
             worst_sub = max(worst_sub, top_subspace_err(Ob, Oeb, Mb))
         print(f"  entry {i}: O vs faithful {eo:.2e}, O vs exact {ex_o:.2e} (faithful vs exact "
@@ -131,6 +128,16 @@ def test_moe_experts(lib, method, ns_dtype):
 @pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
 def test_per_head_split(lib, method, ns_dtype):
     _run(lib, 5, method, ns_dtype, sample=[0, 127])
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_per_head_output_projection_by_columns(lib, method, ns_dtype):
+    # the output projection's heads are its input (column) side: a 4096 x 4096
+    # o_proj split into 32 column blocks of 4096 x 128, each read and written in
+    # place with the matrix's row pitch, next to a q/k/v-style row-split matrix
+    # that lands in the same shape group
+    wl = W.custom_workload([(4096, 4096, 128, 0), (4096, 4096, 0, 128)], wid=180)
+    _run(lib, wl, method, ns_dtype, sample=[1])
 
 
 def test_per_head_adamw_part(lib):

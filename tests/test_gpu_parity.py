@@ -33,7 +33,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import (entry_slices, outside_mask, rel, run_step, to_device,
+from gpu_helpers import (block_grid, entry_slices, outside_mask, rel, run_step, to_device,
                          top_subspace_err)
 
 pytestmark = pytest.mark.gpu
@@ -67,7 +67,7 @@ def _check(nss, wl, method, ns_dtype, faithful, gaussian_exact_gate=None, subspa
     params, grads, mom = W.host_inputs(wl)
     tab = wl.table()
     print(f"[case] {wl.title} method={method} ns_dtype={ns_dtype} shapes="
-          f"{[(e.rows, e.cols, e.split_rows) for e in wl.entries]}", flush=True)
+          f"{[(e.rows, e.cols, e.split_rows, e.split_cols) for e in wl.entries]}", flush=True)
     gpu = run_step(nss, params, grads, mom, tab, _hyper(nss, wl, method, ns_dtype), shadow=shadow)
     g64 = W.grad_as_f64(wl, grads)
     kw = dict(lr=wl.lr, mu=wl.momentum, weight_decay=wl.weight_decay, method=method)
@@ -82,7 +82,7 @@ def _check(nss, wl, method, ns_dtype, faithful, gaussian_exact_gate=None, subspa
         em = rel(gpu["momentum"][sl], exact["momentum"][sl])
         dp = rel(gpu["params"][sl] - params[sl], ref["params"][sl] - params[sl])
         ea = _apply_err(gpu["params"][sl], params[sl], gpu["update"][sl], wl.lr, wl.weight_decay)
-        print(f"  entry {i} {e.rows}x{e.cols}/{e.split_rows}: O {eo:.2e} M {em:.2e} dp {dp:.2e} "
+        print(f"  entry {i} {e.rows}x{e.cols}/{e.split_rows}/{e.split_cols}: O {eo:.2e} M {em:.2e} dp {dp:.2e} "
               f"apply {ea:.2e}")
         assert em <= MOM_GATE and ea <= FP32_GATE, (i, em, ea)
         if gram_lowrank:
@@ -95,14 +95,13 @@ def _check(nss, wl, method, ns_dtype, faithful, gaussian_exact_gate=None, subspa
         if gaussian_exact_gate is not None:
             assert rel(gpu["update"][sl], exact["update"][sl]) <= gaussian_exact_gate
         if subspace or gram_lowrank:
-            blocks = [(0, e.rows)] if e.split_rows == 0 else \
-                [(r, e.split_rows) for r in range(0, e.rows, e.split_rows)]
             Mm = exact["momentum"][sl].reshape(e.rows, e.cols)
             Og = gpu["update"][sl].reshape(e.rows, e.cols).astype(np.float64)
             Oe = exact["update"][sl].reshape(e.rows, e.cols)
-            for r0, nr in blocks:
-                Mb, Ogb, Oeb = Mm[r0:r0 + nr], Og[r0:r0 + nr], Oe[r0:r0 + nr]
-                if nr > e.cols:     # left singular vectors of the short side
+            for r0, nr, c0, nc in block_grid(e):
+                bs = (slice(r0, r0 + nr), slice(c0, c0 + nc))
+                Mb, Ogb, Oeb = Mm[bs], Og[bs], Oe[bs]
+                if nr > nc:         # left singular vectors of the short side
                     Mb, Ogb, Oeb = Mb.T, Ogb.T, Oeb.T
                 es = top_subspace_err(Ogb, Oeb, Mb, k=min(16, min(Mb.shape)))
                 assert es <= LP_GATE, (i, r0, es)
@@ -508,6 +507,65 @@ def test_empty_table_and_small_workspace(lib):
     lib.step(p, g, m, tab2, h, ws=torch.empty(need2, dtype=torch.uint8, device=dev))
     torch.cuda.synchronize()
     assert not torch.equal(p[:3520], p0[:3520]) and torch.equal(p[3520:3584], p0[3520:3584])
+
+
+# --------------------------------------------------------------------------- column and grid splits
+
+# Blocks read and written in place with the matrix's row pitch: tall column
+# blocks (stored transposed), wide ones, widths that are not a multiple of 8 or
+# 4 (the element paths), a split_rows x split_cols grid, and a whole matrix in
+# the same shape group as column blocks (contiguous and pitched problems in one
+# launch).
+COL_SHAPES = [(256, 384, 0, 128), (96, 640, 0, 128), (300, 72, 0, 24), (200, 36, 0, 12),
+              (20, 15, 0, 5), (512, 768, 256, 384), (128, 256, 0, 0)]
+
+
+@pytest.mark.parametrize("method,ns_dtype,grad_dtype", [
+    ("standard", "f32", "f32"), ("standard", "bf16", "bf16"), ("gram", "f16", "bf16")])
+def test_column_and_grid_splits(lib, method, ns_dtype, grad_dtype):
+    wl = W.custom_workload(COL_SHAPES, grad_dtype=grad_dtype, ns_dtype=ns_dtype, wid=114)
+    _check(lib, wl, method, ns_dtype, faithful=ns_dtype != "f32", subspace=ns_dtype != "f32")
+
+
+def _gather_blocks(wl, arrays):
+    """The blocks of the one entry of `wl`, each as its own contiguous matrix,
+    packed back to back; returns the packed arrays and their table."""
+    (e,), off = wl.entries, wl.offsets[0]
+    tab, outs, cur = [], [], 0
+    for r0, nr, c0, nc in block_grid(e):
+        tab.append((cur, nr, nc, 0))
+        cur += nr * nc
+    for a in arrays:
+        whole = a[off:off + e.rows * e.cols].reshape(e.rows, e.cols)
+        outs.append(np.concatenate([whole[r0:r0 + nr, c0:c0 + nc].ravel()
+                                    for r0, nr, c0, nc in block_grid(e)]))
+    return outs, tab
+
+
+def _scatter_blocks(wl, packed):
+    (e,), off = wl.entries, wl.offsets[0]
+    whole = np.empty((e.rows, e.cols), packed.dtype)
+    cur = 0
+    for r0, nr, c0, nc in block_grid(e):
+        whole[r0:r0 + nr, c0:c0 + nc] = packed[cur:cur + nr * nc].reshape(nr, nc)
+        cur += nr * nc
+    return whole.ravel()
+
+
+@pytest.mark.parametrize("shape", [(384, 512, 0, 128), (512, 768, 256, 384), (60, 100, 0, 20)])
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_column_split_equals_separate_entries(lib, method, ns_dtype, shape):
+    # a column (or grid) block read in place is the same problem as its values
+    # stored as a matrix of their own: the same bits come out
+    wl = W.custom_workload([shape], wid=115)
+    params, grads, mom = W.host_inputs(wl)
+    h = _hyper(lib, wl, method, ns_dtype)
+    print(f"[case] column split == separate entries {shape} {method}", flush=True)
+    a = _dev_step(lib, params, grads, mom, wl.table(), h)
+    (ps, gs, ms), tab = _gather_blocks(wl, (params, grads, mom))
+    b = _dev_step(lib, ps, gs, ms, tab, h)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, _scatter_blocks(wl, y))
 
 
 # --------------------------------------------------------------------------- pack / unpack

@@ -47,7 +47,7 @@ def test_owner_plan_equals_single_owner(lib, method, ns_dtype, n_owners):
         if info["n_matrices"] == 0:
             continue
         idx, otab = info["index"], info["table"]
-        assert all(off + r * c <= info["numel"] for off, r, c, _s in otab)
+        assert all(off + r * c <= info["numel"] for off, r, c, *_ in otab)
         covered += idx
         print(f"[owner {o}] {len(idx)} matrices, {info['numel']} elements, "
               f"{info['ns_flops'] / 1e12:.2f} TFLOP", flush=True)

@@ -35,7 +35,7 @@ def _inputs(wl, seed):
     params, grads, _ = W.host_inputs(wl)
     tab = wl.table()
     inside = np.zeros(wl.numel, bool)
-    for off, r, c, _s in tab:
+    for off, r, c, *_ in tab:
         inside[off:off + r * c] = True
     params[~inside] = CANARY
     # a momentum carried over from an earlier step
@@ -88,7 +88,7 @@ def _check_union(wl, params, mom, tab, inside, whole, holders):
         got[a:b] = hd["partition"]
         shadow[a:b] = hd["shadow"]
         listed = np.zeros(wl.numel, bool)
-        for off, r, c, _s in hd["table"]:
+        for off, r, c, *_ in hd["table"]:
             listed[off:off + r * c] = True
         assert np.array_equal(hd["momentum"][listed], whole["momentum"][listed])
         assert np.array_equal(hd["momentum"][~listed], mom[~listed])
@@ -195,3 +195,28 @@ def test_window_full_size_straddle(nss):
     cuts = [wl.offsets[0] + 2048 * 5632 // 3 + 8, wl.offsets[1] + 777 * 2048 + 1]
     holders = _run_holders(nss, wl, params, grads, mom, tab, cuts, h)
     _check_union(wl, params, mom, tab, inside, whole, holders)
+
+
+COL_SHAPES = [(256, 384, 0, 128), (300, 72, 0, 24), (512, 768, 256, 384), (60, 100, 0, 20)]
+
+
+@pytest.mark.parametrize("method,ns_dtype", [("standard", "bf16"), ("gram", "f16")])
+def test_window_union_with_column_splits(nss, method, ns_dtype):
+    # partition boundaries inside column and grid blocks: a window covers part
+    # of some rows of a block, whose rows are ld elements apart in the matrix
+    wl = W.custom_workload(COL_SHAPES, grad_dtype="bf16", ns_dtype=ns_dtype, wid=174,
+                           grad_kind="gaussian" if method == "gram" else "")
+    params, grads, mom, tab, inside = _inputs(wl, 5)
+    h = _hyper(nss, wl, method, ns_dtype)
+    print(f"[case] window union with column splits {method} {ns_dtype}", flush=True)
+    offs = wl.offsets
+    cuts = sorted([
+        offs[0] + 100 * 384 + 200 + 3,    # mid-row, inside column block 1
+        offs[1] + 77 * 72 + 30,           # inside column block 1 of a 24-wide split
+        offs[2] + 300 * 768 + 500,        # inside grid block (1, 1)
+        offs[3] + 7 * 100 + 45,           # inside a 20-wide block, unaligned
+    ])
+    whole = run_step(nss, params, grads, mom, tab, h, shadow=True)
+    holders = _run_holders(nss, wl, params, grads, mom, tab, cuts, h)
+    _check_union(wl, params, mom, tab, inside, whole, holders)
+    _check_oracle(wl, params, grads, mom, holders, method, ns_dtype, 3e-2)

@@ -393,10 +393,12 @@ def test_faithful_modes_stay_near_exact_on_gaussian():
 # --------------------------------------------------------------------------- full step
 
 def _table(shapes, align=8):
+    """shapes: (rows, cols, split_rows[, split_cols])."""
     offs, cur, tab = [], 0, []
-    for r, c, s in shapes:
+    for sh in shapes:
+        r, c = sh[0], sh[1]
         cur = (cur + align - 1) // align * align
-        tab.append((cur, r, c, s))
+        tab.append((cur,) + tuple(sh))
         cur += r * c
     return tab, cur
 
@@ -466,6 +468,95 @@ def test_split_equals_separate_entries():
     g2[:k * cols] *= 100.0
     c2 = oracle.muon_step(p0, g2, np.zeros(n), tab_split)
     assert rel(c2["update"][:k * cols], a["update"][:k * cols]) < 1e-7
+
+
+def _blocks_as_entries(rows, cols, pr, pc):
+    """Table of the pr x pc blocks of a rows x cols matrix stored as separate
+    contiguous matrices, and the index map taking those packed elements to
+    the matrix's flat positions."""
+    idx = np.arange(rows * cols).reshape(rows, cols)
+    tab, order, cur = [], [], 0
+    for r0 in range(0, rows, pr):
+        for c0 in range(0, cols, pc):
+            tab.append((cur, pr, pc, 0))
+            order.append(idx[r0:r0 + pr, c0:c0 + pc].ravel())
+            cur += pr * pc
+    return tab, np.concatenate(order)
+
+
+@pytest.mark.parametrize("method", ["standard", "gram"])
+@pytest.mark.parametrize("shape", [(10, 12, 0, 4), (12, 10, 0, 5), (8, 12, 4, 6)])
+def test_column_and_grid_split_equal_separate_entries(method, shape):
+    # a column block (or a split_rows x split_cols tile) is its own problem: its
+    # values, copied out as a matrix of their own, give the same update, and the
+    # blocks' momenta and weights move as the copies' do
+    rng = np.random.default_rng(18)
+    rows, cols, sr, sc = shape
+    n = rows * cols
+    p0, g, m0 = rng.standard_normal(n), rng.standard_normal(n), rng.standard_normal(n)
+    kw = dict(lr=0.03, weight_decay=0.1, mu=0.9, method=method)
+    a = oracle.muon_step(p0, g, m0, [(0, rows, cols, sr, sc)], **kw)
+    tab, order = _blocks_as_entries(rows, cols, sr or rows, sc or cols)
+    b = oracle.muon_step(p0[order], g[order], m0[order], tab, **kw)
+    for key in ("params", "momentum", "update"):
+        assert np.allclose(a[key][order], b[key], rtol=0, atol=1e-13), key
+    # every block has its own norm: scaling one block's gradient and momentum
+    # leaves the update of every block unchanged
+    s = np.ones((rows, cols))
+    s[:sr or rows, :sc or cols] = 100.0
+    c = oracle.muon_step(p0, g * s.ravel(), m0 * s.ravel(), [(0, rows, cols, sr, sc)], **kw)
+    assert rel(c["update"], a["update"]) < 1e-7
+
+
+@pytest.mark.parametrize("method", ["standard", "gram"])
+def test_column_split_is_the_row_split_of_the_transpose(method):
+    # polar(B^T) = polar(B)^T, and the iteration runs on the short side either
+    # way: splitting W by columns gives the transpose of splitting W^T by rows
+    rng = np.random.default_rng(19)
+    rows, cols, k = 9, 24, 6
+    W = rng.standard_normal((rows, cols))
+    Wt = np.ascontiguousarray(W.T)
+    a = oracle.muon_step(np.zeros(W.size), W.ravel(), np.zeros(W.size), [(0, rows, cols, 0, k)],
+                         mu=0.0, method=method)
+    b = oracle.muon_step(np.zeros(W.size), Wt.ravel(), np.zeros(W.size), [(0, cols, rows, k)],
+                         mu=0.0, method=method)
+    Oa = a["update"].reshape(rows, cols)
+    Ob = b["update"].reshape(cols, rows)
+    assert np.allclose(Oa, Ob.T, rtol=0, atol=1e-13)
+    # each 9 x 6 block is close to a matrix with orthonormal columns after five
+    # quintic steps (singular values in the coefficients' band, not all 1)
+    for c0 in range(0, cols, k):
+        sv = np.linalg.svd(Oa[:, c0:c0 + k], compute_uv=False)
+        assert sv.min() > 0.6 and sv.max() < 1.25
+
+
+def test_column_split_flops_and_windows():
+    from oracle import planner
+    # a column-split o_proj costs what its row-split transpose costs; a grid
+    # costs one problem per tile
+    assert planner.matrix_flops(4096, 4096, 0, split_cols=128) == planner.matrix_flops(4096, 4096, 128)
+    assert planner.matrix_flops(512, 768, 256, split_cols=384) == 4 * planner.ns_flops(256, 384)
+    # windows are flat in the matrix whatever the split: every element of a
+    # column-split matrix falls in exactly one holder's window
+    tab, n = _table([(6, 10, 0, 5), (12, 4, 0, 2), (8, 8, 4, 4)])
+    seen = np.zeros(n, int)
+    for a, b in _holders(n, [7, 33, 61, 100]):
+        for (off, r, c, *_), (lo, hi, po) in zip(tab, oracle.partition_windows(tab, a, b)):
+            if hi > lo:
+                assert a + po == off + lo
+                seen[off + lo:off + hi] += 1
+    for off, r, c, *_ in tab:
+        assert np.all(seen[off:off + r * c] == 1)
+    # and the holders' windows together carry the whole step's update
+    rng = np.random.default_rng(20)
+    p0, g, m0 = rng.standard_normal(n), rng.standard_normal(n), rng.standard_normal(n)
+    kw = dict(lr=0.03, weight_decay=0.1, mu=0.9, method="standard")
+    whole = oracle.muon_step(p0, g, m0, tab, **kw)
+    got = p0.copy()
+    for a, b in _holders(n, [7, 33, 61, 100]):
+        got[a:b] = oracle.window_step(p0[a:b], g, m0, tab, oracle.partition_windows(tab, a, b),
+                                      **kw)["partition"]
+    assert np.array_equal(got, whole["params"])
 
 
 def test_pack_unpack_roundtrip():

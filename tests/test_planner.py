@@ -109,16 +109,19 @@ def test_lpt_within_graham_bound():
         assert got * 3 * n <= (4 * n - 1) * _optimum(costs, n)
 
 
-POOL = [(2048, 2048, 0), (5632, 2048, 0), (2048, 5632, 0), (4096, 4096, 0), (11008, 4096, 0),
-        (4096, 11008, 0), (1024, 128, 128), (384, 200, 0), (8, 8, 0), (1, 1, 0), (257, 33, 0),
-        (512, 64, 64), (64, 4096, 0)]
+# (rows, cols, split_rows, split_cols)
+POOL = [(2048, 2048, 0, 0), (5632, 2048, 0, 0), (2048, 5632, 0, 0), (4096, 4096, 0, 0),
+        (11008, 4096, 0, 0), (4096, 11008, 0, 0), (1024, 128, 128, 0), (384, 200, 0, 0),
+        (8, 8, 0, 0), (1, 1, 0, 0), (257, 33, 0, 0), (512, 64, 64, 0), (64, 4096, 0, 0),
+        (4096, 4096, 0, 128), (2048, 640, 0, 64), (512, 768, 256, 384)]
 
 
 def _random_model(rng, n):
+    """(rows, cols, split_rows, layer, split_cols) per matrix."""
     out = []
     for _ in range(n):
-        r, c, s = POOL[int(rng.integers(len(POOL)))]
-        out.append((r, c, s, int(rng.integers(0, 4))))
+        r, c, s, sc = POOL[int(rng.integers(len(POOL)))]
+        out.append((r, c, s, int(rng.integers(0, 4)), sc))
     return out
 
 
@@ -146,7 +149,8 @@ def test_plan_layout_invariants():
                        for i in range(len(model)) if assign[i][0] == o)
         assert info["n_matrices"] == len(spans)
         assert [s[3] for s in spans] == info["index"]
-        assert info["table"] == [(s[0], model[s[3]][0], model[s[3]][1], model[s[3]][2]) for s in spans]
+        assert info["table"] == [(s[0], model[s[3]][0], model[s[3]][1], model[s[3]][2], model[s[3]][4])
+                                 for s in spans]
         for (a0, a1, la, _), (b0, b1, lb, _) in zip(spans, spans[1:]):
             assert a1 <= b0 and la <= lb           # no overlap; layers in order
         assert all(s[0] % 64 == 0 for s in spans)
@@ -156,7 +160,7 @@ def test_plan_layout_invariants():
             lo, hi = per_layer.get(layer, (a, b))
             per_layer[layer] = (min(lo, a), max(hi, b))
         assert info["max_layer_numel"] == max((b - a for a, b in per_layer.values()), default=0)
-        flops = sum(ref.matrix_flops(*model[s[3]][:3]) for s in spans)
+        flops = sum(ref.matrix_flops(*model[s[3]][:3], split_cols=model[s[3]][4]) for s in spans)
         assert info["ns_flops"] == flops
         seen.update(s[3] for s in spans)
     assert seen == set(range(len(model)))

@@ -43,6 +43,7 @@ class Entry:
     rows: int
     cols: int
     split_rows: int = 0  # 0: whole matrix; k > 0: rows/k independent k-row blocks
+    split_cols: int = 0  # k > 0: cols/k independent k-column blocks (with split_rows: tiles)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -80,9 +81,10 @@ class Workload:
     def muon_elements(self) -> int:
         return sum(e.rows * e.cols for e in self.entries)
 
-    def table(self) -> List[Tuple[int, int, int, int]]:
-        """(offset, rows, cols, split_rows) per entry, in packing order."""
-        return [(o, e.rows, e.cols, e.split_rows)
+    def table(self) -> List[Tuple[int, ...]]:
+        """(offset, rows, cols, split_rows) per entry, in packing order, with
+        split_cols as a fifth field for entries split by columns."""
+        return [(o, e.rows, e.cols, e.split_rows) + ((e.split_cols,) if e.split_cols else ())
                 for o, e in zip(self.offsets, self.entries)]
 
 
@@ -141,12 +143,13 @@ def workload(wid: int) -> Workload:
     return WORKLOADS[wid]()
 
 
-def custom_workload(shapes: Sequence[Tuple[int, int, int]], grad_dtype: str = "bf16",
+def custom_workload(shapes: Sequence[Tuple[int, ...]], grad_dtype: str = "bf16",
                     ns_dtype: str = "bf16", wid: int = 100, lr: float = 0.02,
                     momentum: float = 0.95, weight_decay: float = 0.1,
                     grad_kind: str = "") -> Workload:
-    """A workload from explicit (rows, cols, split_rows) triples (used for ragged cases)."""
-    ents = tuple(Entry(f"m{i}", r, c, s) for i, (r, c, s) in enumerate(shapes))
+    """A workload from explicit (rows, cols, split_rows[, split_cols]) shapes (used
+    for ragged cases)."""
+    ents = tuple(Entry(f"m{i}", *sh) for i, sh in enumerate(shapes))
     return Workload(wid, "custom", ents, grad_dtype, ns_dtype, lr, momentum, weight_decay,
                     grad_kind=grad_kind)
 
