@@ -35,6 +35,8 @@
 // transposed) position, for the elements of the problem's window (the whole
 // problem in an ordinary step).
 // Global loads of the epilogue (D, params) are issued in batches ahead of use.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -432,18 +434,11 @@ template <> struct Pack8<float> {
 
 // Parameter access of the apply epilogues: fp32 (EPI_APPLY) or bf16 words
 // (EPI_APPLY_BF16), as floats. The 8-element forms need pidx a multiple of 8.
-template <int EPI>
-__device__ __forceinline__ void load_p8(const void* params, int64_t pidx, f32x4& p0, f32x4& p1) {
-  if constexpr (EPI == EPI_APPLY_BF16) {
-    const u16x8 w = *reinterpret_cast<const u16x8*>(static_cast<const unsigned short*>(params) + pidx);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { p0[e] = bf16_bits_to_f32(w[e]); p1[e] = bf16_bits_to_f32(w[e + 4]); }
-  } else {
-    const f32x4* pp = reinterpret_cast<const f32x4*>(static_cast<const float*>(params) + pidx);
-    p0 = pp[0];
-    p1 = pp[1];
-  }
-}
+// ParamPack holds 8 parameters as loaded; they are converted where used, so a
+// load can stay in flight until then.
+template <int EPI> struct ParamPackT { using type = Pack8<float>; };
+template <> struct ParamPackT<EPI_APPLY_BF16> { using type = Pack8<__bf16>; };
+template <int EPI> using ParamPack = typename ParamPackT<EPI>::type;
 
 template <int EPI>
 __device__ __forceinline__ void store_p8(void* params, int64_t pidx, const f32x4& o0, const f32x4& o1) {
@@ -471,22 +466,30 @@ __device__ __forceinline__ void store_p1(void* params, int64_t i, float v) {
   else static_cast<float*>(params)[i] = v;
 }
 
+// The launch's apply scalars, read once per workgroup.
+struct ApplyScalars {
+  void* params;
+  float* update_out;
+  unsigned short* shadow;
+  float decay, lr;
+};
+
 // One run of up to 8 consecutive stored elements e0 .. e0 + cnt - 1 of a problem:
 // v goes to update_out at uidx (every element), and p <- p * decay - lr * v, with
 // the optional bf16 copy of the new p (shadow, fp32 params only), to the params
 // at pidx for the elements inside the problem's window [lo, hi). `vec`: a whole
 // run inside the window with pidx a multiple of 8 and uidx of 4, whose params
-// the caller has loaded into p0, p1; anything else takes the scalar path.
+// the caller has loaded into pp; anything else takes the scalar path.
 template <int EPI>
-__device__ __forceinline__ void apply8(const GemmArgs& a, int64_t pidx, int64_t uidx, int64_t e0, int cnt,
-                                       int64_t lo, int64_t hi, const float (&v)[8], const f32x4& p0,
-                                       const f32x4& p1, bool vec) {
+__device__ __forceinline__ void apply8(const ApplyScalars& a, int64_t pidx, int64_t uidx, int64_t e0, int cnt,
+                                       int64_t lo, int64_t hi, const float (&v)[8], const ParamPack<EPI>& pp,
+                                       bool vec) {
   if (vec) {
     f32x4 o0, o1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      o0[e] = p0[e] * a.decay - a.lr * v[e];
-      o1[e] = p1[e] * a.decay - a.lr * v[e + 4];
+      o0[e] = pp.get(e) * a.decay - a.lr * v[e];
+      o1[e] = pp.get(e + 4) * a.decay - a.lr * v[e + 4];
     }
     store_p8<EPI>(a.params, pidx, o0, o1);
     if (a.update_out) {
@@ -537,8 +540,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   constexpr int CPR = HALF / 8;          // 8-column chunks per staged row
   constexpr int NR = 32 * CPR / 64;      // row-pass tasks per lane
   constexpr int NC = HALF * 4 / 64;      // column-pass tasks per lane
-  constexpr int PB = NR < 4 ? NR : 4;    // apply: chunks whose parameters are loaded together
-  static_assert(NR % PB == 0 && NC % PB == 0, "apply batches");
+  static_assert(NR == NC, "apply: one chunk count for either pass");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -554,6 +556,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
 
   int transposed = 0, ld = 0;
   int64_t src = 0, pb = 0, wlo = 0, whi = 0;
+  ApplyScalars as{};
   constexpr bool APPLY = (EPI == EPI_APPLY || EPI == EPI_APPLY_BF16);
   if constexpr (APPLY) {
     const ProblemDesc pd = a.probs[prob];
@@ -563,7 +566,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
     pb = pd.p_base;
     wlo = pd.lo;
     whi = pd.hi;
+    as = ApplyScalars{a.params, a.update_out, a.shadow, a.decay, a.lr};
   }
+  // (32-bit iterates: no registers to spare for them; read where used)
+  auto scalars = [&]() -> ApplyScalars {
+    if constexpr (sizeof(T) == 2) return as;
+    else return ApplyScalars{a.params, a.update_out, a.shadow, a.decay, a.lr};
+  };
   const int m = a.m_valid, n = a.n_valid;
   // the launch's scalars, read once
   const float alpha = a.alpha, beta = a.beta, gamma = a.gamma;
@@ -590,6 +599,51 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   };
   load_d(0);
 
+  // Apply: the parameters of the wave's chunks of a 32-row block, as loaded.
+  // Block i + 1's are requested before block i's stores: loads and stores
+  // share one in-order counter, so a load issued after a store could not be
+  // waited for without waiting for the store too.
+  // (32-bit iterates: the main loop leaves no room for a second block's
+  // parameters, which are then requested right before they are used)
+  constexpr bool PF_AHEAD = sizeof(T) == 2;
+  ParamPack<EPI == EPI_STORE ? EPI_APPLY : EPI> pq[2][NR];
+  bool pv[2][NR];
+  // chunk t of block i: canonical (gi, gj), 8 elements along a row (stored as
+  // is) or down a column (stored transposed), local index e of the first
+  auto chunk = [&](int i, int t, int& gi, int& gj, int64_t& e) {
+    const int q = lane + 64 * t;
+    if (!transposed) {
+      gi = gi_w + i * 32 + q / CPR;
+      gj = gj_w + (q % CPR) * 8;
+      e = static_cast<int64_t>(gi) * ld + gj;
+    } else {
+      gi = gi_w + i * 32 + (q & 3) * 8;
+      gj = gj_w + (q >> 2);
+      e = static_cast<int64_t>(gj) * ld + gi;
+    }
+  };
+  // a chunk that is not loaded reads the launch's descriptors instead (in
+  // bounds, never used), at a byte offset from the parameters
+  using PElem = typename std::conditional<EPI == EPI_APPLY_BF16, __bf16, float>::type;
+  const char* pbytes = static_cast<const char*>(a.params);
+  const int64_t dummy_off = static_cast<int64_t>(reinterpret_cast<uintptr_t>(a.probs) -
+                                                 reinterpret_cast<uintptr_t>(a.params));
+  auto load_params = [&](int i) {
+    if constexpr (APPLY) {
+#pragma unroll
+      for (int t = 0; t < NR; ++t) {
+        int gi, gj;
+        int64_t e;
+        chunk(i, t, gi, gj, e);
+        const bool whole = transposed ? (gj < n && gi + 8 <= m) : (gi < m && gj + 8 <= n);
+        pv[i & 1][t] = whole && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
+        // unconditional, so the compiler can count what is in flight
+        pq[i & 1][t].load(reinterpret_cast<const PElem*>(pbytes + (pv[i & 1][t] ? (pb + e) * int64_t(sizeof(PElem))
+                                                                                  : dummy_off)));
+      }
+    }
+  };
+
   // Each wave stages into its own part of LDS, and one wave's LDS accesses are
   // performed in program order, so after the first block (whose staging area the
   // other waves may still be reading operands from) only the compiler has to be
@@ -597,25 +651,41 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   auto lds_order = []() { asm volatile("" ::: "memory"); };
 #pragma unroll
   for (int i = 0; i < WB; ++i) {
-    if (i == 0) __syncthreads();   // every wave is past its last main-loop LDS read
-    else lds_order();
+    if (i == 0) {
+      __syncthreads();                 // every wave is past its last main-loop LDS read
+      if (PF_AHEAD) load_params(0);    // (after the barrier: the main loop's registers are free)
+    } else {
+      lds_order();
+    }
 #pragma unroll
     for (int j = 0; j < WB; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) stage4(stg + srow(lane & 31, j * 32 + q * 8 + (lane >> 5) * 4), acc[i][j], q);
     lds_order();
 
-    // ---- row pass: each lane finishes one 8-column chunk at a time
+    if (!PF_AHEAD) load_params(i);
+    else if (i + 1 < WB) load_params(i + 1);   // before this block's stores
+
+    // ---- row pass: each lane finishes one 8-column chunk at a time (and
+    // applies it, for a matrix stored as is); the next chunk's staged values
+    // are read before this one is finished, so the LDS latency overlaps it
+    auto stage_rd = [&](int t, f32x4 (&x)[2]) {
+      const int q = lane + 64 * t;
+      const int rr = q / CPR, cc = (q % CPR) * 8;
+      x[0] = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
+      x[1] = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
+    };
+    f32x4 sv[2][2];
+    stage_rd(0, sv[0]);
 #pragma unroll
     for (int t = 0; t < NR; ++t) {
+      if (t + 1 < NR) stage_rd(t + 1, sv[(t + 1) & 1]);
       const int q = lane + 64 * t;
       const int rr = q / CPR, cc = (q % CPR) * 8;
       const int gi = gi_w + i * 32 + rr, gj = gj_w + cc;
       float v[8];
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { v[e] = alpha * s0[e]; v[e + 4] = alpha * s1[e]; }
+      for (int e = 0; e < 4; ++e) { v[e] = alpha * sv[t & 1][0][e]; v[e + 4] = alpha * sv[t & 1][1][e]; }
       if (D != nullptr) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(beta, dq[t].get(e), v[e]);
@@ -627,10 +697,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       }
       float4* sp = reinterpret_cast<float4*>(stg + srow(rr, cc));
       if constexpr (APPLY) {
-        // the value itself goes back to the staging area (for the apply below,
-        // or for the column pass of a transposed matrix)
-        sp[0] = make_float4(v[0], v[1], v[2], v[3]);
-        sp[1] = make_float4(v[4], v[5], v[6], v[7]);
+        if (!transposed) {
+          // stored m x n: canonical (gi, gj) is local index gi * ld + gj
+          if (gi < m && gj < n) {
+            const int64_t e = static_cast<int64_t>(gi) * ld + gj;
+            apply8<EPI>(scalars(), pb + e, src + e, e, min(8, n - gj), wlo, whi, v, pq[i & 1][t], pv[i & 1][t]);
+          }
+        } else {
+          // the value goes back to the staging area for the column pass
+          sp[0] = make_float4(v[0], v[1], v[2], v[3]);
+          sp[1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
       } else {
         T o[8];
 #pragma unroll
@@ -648,42 +725,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
         }
       }
     }
-    if (!(APPLY && !transposed) && i + 1 < WB) load_d(i + 1);
-
-    if (APPLY && !transposed) {
-      // stored m x n: canonical (gi, gj) is local index gi * ld + gj. Each lane
-      // reads back the chunks it wrote; parameters are loaded PB chunks at a time,
-      // all of a batch before any is used.
-#pragma unroll
-      for (int b = 0; b < NR; b += PB) {
-        f32x4 p0[PB], p1[PB];
-        bool pvec[PB];
-#pragma unroll
-        for (int u = 0; u < PB; ++u) {
-          const int q = lane + 64 * (b + u);
-          const int gi = gi_w + i * 32 + q / CPR, gj = gj_w + (q % CPR) * 8;
-          const int64_t e = static_cast<int64_t>(gi) * ld + gj;
-          pvec[u] = gi < m && gj + 8 <= n && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
-          if (pvec[u]) load_p8<EPI>(a.params, pb + e, p0[u], p1[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < PB; ++u) {
-          const int q = lane + 64 * (b + u);
-          const int rr = q / CPR, cc = (q % CPR) * 8;
-          const int gi = gi_w + i * 32 + rr, gj = gj_w + cc;
-          if (gi < m && gj < n) {
-            float v[8];
-            const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
-            const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { v[e] = s0[e]; v[e + 4] = s1[e]; }
-            const int64_t e = static_cast<int64_t>(gi) * ld + gj;
-            apply8<EPI>(a, pb + e, src + e, e, min(8, n - gj), wlo, whi, v, p0[u], p1[u], pvec[u]);
-          }
-        }
-      }
-      if (i + 1 < WB) load_d(i + 1);
-    }
+    if (i + 1 < WB) load_d(i + 1);
 
     // ---- column pass
     if (need_col) {
@@ -691,29 +733,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       if constexpr (APPLY) {
         // stored n x m: canonical (gi, gj) is local index gj * ld + gi
 #pragma unroll
-        for (int b = 0; b < NC; b += PB) {
-          f32x4 c0[PB], c1[PB];
-          bool cvec[PB];
+        for (int t = 0; t < NC; ++t) {
+          int gi, gj;
+          int64_t e;
+          chunk(i, t, gi, gj, e);
+          const int q = lane + 64 * t;
+          const int r8 = (q & 3) * 8, cc = q >> 2;
+          if (gj < n && gi < m) {
+            float w[8];
 #pragma unroll
-          for (int u = 0; u < PB; ++u) {
-            const int q = lane + 64 * (b + u);
-            const int gi = gi_w + i * 32 + (q & 3) * 8, gj = gj_w + (q >> 2);
-            const int64_t e = static_cast<int64_t>(gj) * ld + gi;
-            cvec[u] = gj < n && gi + 8 <= m && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
-            if (cvec[u]) load_p8<EPI>(a.params, pb + e, c0[u], c1[u]);
-          }
-#pragma unroll
-          for (int u = 0; u < PB; ++u) {
-            const int q = lane + 64 * (b + u);
-            const int r8 = (q & 3) * 8, cc = q >> 2;
-            const int gi = gi_w + i * 32 + r8, gj = gj_w + cc;
-            if (gj < n && gi < m) {
-              float w[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) w[e] = stg[srow(r8 + e, cc)];
-              const int64_t e = static_cast<int64_t>(gj) * ld + gi;
-              apply8<EPI>(a, pb + e, src + e, e, min(8, m - gi), wlo, whi, w, c0[u], c1[u], cvec[u]);
-            }
+            for (int u = 0; u < 8; ++u) w[u] = stg[srow(r8 + u, cc)];
+            apply8<EPI>(scalars(), pb + e, src + e, e, min(8, m - gi), wlo, whi, w, pq[i & 1][t], pv[i & 1][t]);
           }
         }
       } else {
