@@ -56,6 +56,27 @@ __device__ __forceinline__ float keep_f32(float x) {
   return x;
 }
 
+// N values (N even) rounded to T, nearest even, as from_f32 rounds them; the
+// 16-bit types convert two per instruction
+template <typename T, int N>
+__device__ __forceinline__ void rne(const float (&v)[N], T (&o)[N]) {
+  static_assert(N % 2 == 0, "pairs");
+  if constexpr (sizeof(T) == 2) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef T t2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int p = 0; p < N / 2; ++p) {
+      const f2 x = {keep_f32(v[2 * p]), keep_f32(v[2 * p + 1])};
+      const t2 y = __builtin_convertvector(x, t2);
+      o[2 * p] = y[0];
+      o[2 * p + 1] = y[1];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) o[e] = from_f32<T>(keep_f32(v[e]));
+  }
+}
+
 __device__ __forceinline__ unsigned short bf16_bits(float x) {
   __bf16 b = static_cast<__bf16>(x);
   return __builtin_bit_cast(unsigned short, b);

@@ -203,9 +203,11 @@ __device__ __forceinline__ void store4(T* dst, const float (&v)[4]) {
     for (int e = 0; e < 4; ++e) w[e] = v[e];
     *reinterpret_cast<f32x4*>(dst) = w;
   } else {
+    T r[4];
+    rne<T, 4>(v, r);
     u16x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[e])));
+    for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(unsigned short, r[e]);
     *reinterpret_cast<u16x4*>(dst) = w;
   }
 }

@@ -502,9 +502,14 @@ __device__ __forceinline__ void apply8(const ApplyScalars& a, int64_t pidx, int6
     }
     if constexpr (EPI == EPI_APPLY) {
       if (a.shadow) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[e] = o0[e]; x[e + 4] = o1[e]; }
+        __bf16 r[8];
+        rne<__bf16, 8>(x, r);
         u16x8 sh;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { sh[e] = bf16_bits(o0[e]); sh[e + 4] = bf16_bits(o1[e]); }
+        for (int e = 0; e < 8; ++e) sh[e] = __builtin_bit_cast(unsigned short, r[e]);
         *reinterpret_cast<u16x8*>(a.shadow + pidx) = sh;
       }
     }
@@ -710,8 +715,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
         }
       } else {
         T o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(keep_f32(v[e]));
+        rne<T, 8>(v, o);
         T* cp = C + static_cast<int64_t>(prob) * c_ps + static_cast<int64_t>(gi) * ldc + gj;
         if (!diag || gi >= gj + 7) {
           st8<T>(cp, o);
@@ -752,9 +756,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
           const int q = lane + 64 * t;
           const int r8 = (q & 3) * 8, cc = q >> 2;
           const int gi = gi_w + i * 32 + r8, gj = gj_w + cc;
-          T o[8];
+          float w[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(stg[srow(r8 + e, cc)]);
+          for (int e = 0; e < 8; ++e) w[e] = stg[srow(r8 + e, cc)];
+          T o[8];
+          rne<T, 8>(w, o);
           T* cp = Ct + static_cast<int64_t>(prob) * ct_ps + static_cast<int64_t>(gj) * ldct + gi;
           if (!diag || gi > gj) {
             st8<T>(cp, o);
@@ -953,9 +959,11 @@ __global__ __launch_bounds__(256) void ns_update_gram(GemmBatch batch) {
         const int gi = wm * HALF + i * 32 + rr, gj = wn * HALF + cc;   // row (= k of X), column in tile
         const f32x4 s0 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
         const f32x4 s1 = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
-        T o[8];
+        float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(keep_f32(a.alpha * (e < 4 ? s0[e] : s1[e - 4])));
+        for (int e = 0; e < 8; ++e) v[e] = a.alpha * (e < 4 ? s0[e] : s1[e - 4]);
+        T o[8];
+        rne<T, 8>(v, o);
         st8<T>(Cg + static_cast<int64_t>(gi) * a.ldc + static_cast<int64_t>(jt) * 128 + gj, o);
         const int pl = gj >> 6, c = (gj & 63) >> 3;
         u16x8 w;
@@ -1166,9 +1174,11 @@ __global__ __launch_bounds__(256) void gram_chain_kernel(GramChainBatch batch) {
             if (D != nullptr) v[e] = __builtin_fmaf(beta, static_cast<float>(__builtin_bit_cast(T, (unsigned short)dv[e])), v[e]);
             if (br == bc) v[e] = (gamma != 0.0f && row0 + e == col) ? v[e] + gamma : v[e];
           }
+          T r[4];
+          rne<T, 4>(v, r);
           u16x4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[e])));
+          for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(unsigned short, r[e]);
           if (br > bc) {
             *reinterpret_cast<u16x4*>(dst + at(col, row0)) = o;          // (col, row0 + e): mirror
 #pragma unroll
@@ -1198,10 +1208,14 @@ __global__ __launch_bounds__(256) void gram_chain_kernel(GramChainBatch batch) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row0 = row0_of(ln, i, q);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = 1.0f * acc[i][j][q * 4 + e];
+          T r[4];
+          rne<T, 4>(v, r);
           u16x4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            o[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(1.0f * acc[i][j][q * 4 + e])));
+          for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(unsigned short, r[e]);
           if (transposed) {
             *reinterpret_cast<u16x4*>(dst + at(col, row0)) = o;
           } else {
@@ -1366,9 +1380,14 @@ __global__ __launch_bounds__(256) void prep_gram_kernel(PrepGramArgs a) {
     T* dst = Xg + static_cast<int64_t>(r) * a.np + jt * 128 + hh * 64;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = v[c * 8 + e];
+      T rx[8];
+      rne<T, 8>(x, rx);
       u16x8 w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = __builtin_bit_cast(unsigned short, from_f32<T>(keep_f32(v[c * 8 + e])));
+      for (int e = 0; e < 8; ++e) w[e] = __builtin_bit_cast(unsigned short, rx[e]);
       *reinterpret_cast<u16x8*>(dst + c * 8) = w;
       *reinterpret_cast<u16x8*>(Ns + hh * SLB + r * 128 + ((c ^ swz(r)) << 4)) = w;
     }
