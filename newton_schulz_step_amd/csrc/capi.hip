@@ -66,11 +66,14 @@ static bool single_row(const Group& G) { return G.mp == G.tile; }
 
 static std::vector<GroupSet> group_sets(const Layout& L) {
   std::vector<GroupSet> sets;
-  for (int kind = 0; kind < 3; ++kind) {
-    const int tile = kind == 0 ? 256 : 128;
+  for (int kind = 0; kind < 4; ++kind) {
+    // 256-tiles with 256- or 128-tile symmetric launches; 128-tiles with more
+    // than one tile row; single-tile-row groups
+    const int tile = kind < 2 ? 256 : 128;
     GroupSet all;
     for (const Group& G : L.groups)
-      if (G.tile == tile && (kind == 0 || single_row(G) == (kind == 2))) all.push_back(&G);
+      if (G.tile == tile && (kind >= 2 ? single_row(G) == (kind == 3) : G.sym_tile == (kind == 0 ? 256 : 128)))
+        all.push_back(&G);
     std::stable_sort(all.begin(), all.end(), [](const Group* x, const Group* y) { return x->n > y->n; });
     for (size_t i = 0; i < all.size(); i += kBatchGroups)
       sets.emplace_back(all.begin() + i, all.begin() + std::min(all.size(), i + kBatchGroups));
@@ -202,7 +205,11 @@ static GemmArgs apply_args(const StepCtx& c, const Group& G) {
 // (lower tiles, mirrored); both operands K-contiguous.
 static void set_sym(GemmArgs& g, const Group& G, const void* P, const void* Q, int64_t K, int64_t ldpq, int64_t pq_ps,
                     void* C) {
-  const int T = static_cast<int>(G.mp / G.tile);
+  // tiles of G.sym_tile up to m (rounded up): with 128-tiles in a 256-padded
+  // buffer, the padding beyond them is never written, and never read into a
+  // valid result either (every K loop stops at m rounded to 128, and the full
+  // launches' extra rows are output rows that nothing reads)
+  const int T = static_cast<int>((G.m + G.sym_tile - 1) / G.sym_tile);
   g.P = P; g.p_ps = pq_ps; g.ldp = static_cast<int32_t>(ldpq);
   g.Q = Q; g.q_ps = pq_ps; g.ldq = static_cast<int32_t>(ldpq);
   g.K = static_cast<int32_t>(K);
@@ -245,6 +252,21 @@ static int launch_batch(const char* kind, const StepCtx& c, int tile, bool sym, 
   return MUON_OK;
 }
 
+// Groups whose symmetric launches use smaller tiles than their full launches
+// leave the padding rows of their m x m results unwritten; the full launches
+// read them as operand rows (of results nobody reads), so they are zeroed once
+// per call: rows round_up(m, sym_tile) .. mp - 1 of every problem's buffer.
+static int zero_sym_padding(const StepCtx& c, const Group& G, size_t off) {
+  if (G.sym_tile == G.tile) return MUON_OK;
+  const int64_t esz = element_size(c.h->ns_dtype);
+  const int64_t r0 = (G.m + G.sym_tile - 1) / G.sym_tile * G.sym_tile;
+  if (r0 >= G.mp) return MUON_OK;
+  MUON_LAUNCH("zero_padding", c.s,
+              launch_zero_regions(c.ws + off + r0 * G.mp * esz, G.mp * G.mp * esz, (G.mp - r0) * G.mp * esz, G.count,
+                                  c.s));
+  return MUON_OK;
+}
+
 // X0 of every problem of the group (canonical m x n, row-major).
 static int run_prep(const StepCtx& c, const Group& G) {
   const float* invn = reinterpret_cast<const float*>(c.ws + c.P->L.off_invnorm) + G.first;
@@ -283,8 +305,10 @@ static int run_standard(const StepCtx& c, const GroupSet& set) {
   const bool fused = single_row(*set.front()) && dt != MUON_DTYPE_F32;
   char* ws = c.ws;
   int st;
-  for (const Group* G : set)
+  for (const Group* G : set) {
     if ((st = fused ? run_prep_gram(c, *G, ws + G->a, 1.0f) : run_prep(c, *G)) != MUON_OK) return st;
+    if ((st = zero_sym_padding(c, *G, G->b)) != MUON_OK) return st;   // B: the full launches' left operand
+  }
   int cur = 0;
   for (int k = 0; k < c.h->ns_steps; ++k) {
     const bool last = (k == c.h->ns_steps - 1);
@@ -323,8 +347,8 @@ static int run_standard(const StepCtx& c, const GroupSet& set) {
       v3.push_back(g3);
     }
     if (!fused)
-      if ((st = launch_batch("ns_gemm_xxt", c, tile, true, EPI_STORE, v1)) != MUON_OK) return st;
-    if ((st = launch_batch("ns_gemm_poly", c, tile, true, EPI_STORE, v2)) != MUON_OK) return st;
+      if ((st = launch_batch("ns_gemm_xxt", c, set.front()->sym_tile, true, EPI_STORE, v1)) != MUON_OK) return st;
+    if ((st = launch_batch("ns_gemm_poly", c, set.front()->sym_tile, true, EPI_STORE, v2)) != MUON_OK) return st;
     if (!last) {
       if (fused) {
         const GemmBatch b = make_batch(v3);
@@ -391,8 +415,12 @@ static int run_gram(const StepCtx& c, const GroupSet& set) {
     }
     return launch_batch("gram_gemm_apply", c, tile, false, apply_epi(c), v);
   } else {
-    for (const Group* G : set)
+    for (const Group* G : set) {
       if ((st = run_prep(c, *G)) != MUON_OK) return st;
+      // every Q is the left operand of a full launch: the first one is written to P
+      if ((st = zero_sym_padding(c, *G, G->p[0])) != MUON_OK) return st;
+      if ((st = zero_sym_padding(c, *G, G->b)) != MUON_OK) return st;
+    }
     for (const Group* Gp : set) {
       const Group& G = *Gp;
       GemmArgs r0{};
@@ -400,7 +428,7 @@ static int run_gram(const StepCtx& c, const GroupSet& set) {
       r0.alpha = scale(G);
       v.push_back(r0);
     }
-    if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
+    if ((st = launch_batch("gram_gemm_sym", c, set.front()->sym_tile, true, EPI_STORE, v)) != MUON_OK) return st;
   }
 
   int rc = 0, pc = 0;
@@ -420,7 +448,7 @@ static int run_gram(const StepCtx& c, const GroupSet& set) {
       gq.D = R(G, rc); gq.d_ps = ss; gq.ldd = static_cast<int32_t>(G.mp);
       v.push_back(gq);
     }
-    if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
+    if ((st = launch_batch("gram_gemm_sym", c, set.front()->sym_tile, true, EPI_STORE, v)) != MUON_OK) return st;
     if (k > 0) {
       // P <- Q P, P row-major as the K x N operand
       v.clear();
@@ -447,7 +475,7 @@ static int run_gram(const StepCtx& c, const GroupSet& set) {
         gt.alpha = 1.0f;
         v.push_back(gt);
       }
-      if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
+      if ((st = launch_batch("gram_gemm_sym", c, set.front()->sym_tile, true, EPI_STORE, v)) != MUON_OK) return st;
       // R <- Q T (symmetric: lower tiles, mirrored)
       v.clear();
       for (const Group* Gp : set) {
@@ -457,7 +485,7 @@ static int run_gram(const StepCtx& c, const GroupSet& set) {
         gr.alpha = 1.0f;
         v.push_back(gr);
       }
-      if ((st = launch_batch("gram_gemm_sym", c, tile, true, EPI_STORE, v)) != MUON_OK) return st;
+      if ((st = launch_batch("gram_gemm_sym", c, set.front()->sym_tile, true, EPI_STORE, v)) != MUON_OK) return st;
       rc ^= 1;
     }
   }

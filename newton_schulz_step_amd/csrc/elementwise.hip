@@ -423,6 +423,31 @@ __global__ __launch_bounds__(256) void copy_batch_kernel(CopyBatch b) {
   for (int64_t k = done + t0; k < it.bytes; k += stride) d[k] = s[k];
 }
 
+// ---------------------------------------------------------------------------
+// zeros over `count` regions of `bytes` bytes, `stride` bytes apart (16-byte
+// aligned, bytes a multiple of 16)
+
+__global__ __launch_bounds__(256) void zero_regions_kernel(char* base, int64_t stride, int64_t n16, int64_t count) {
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t tstride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t p = blockIdx.y; p < count; p += gridDim.y) {
+    uint4* d = reinterpret_cast<uint4*>(base + p * stride);
+    for (int64_t k = t0; k < n16; k += tstride) d[k] = uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+hipError_t launch_zero_regions(void* base, int64_t stride, int64_t bytes, int64_t count, hipStream_t s) {
+  if (count <= 0 || bytes <= 0) return hipSuccess;
+  if (((reinterpret_cast<uintptr_t>(base) | static_cast<uint64_t>(stride) | static_cast<uint64_t>(bytes)) & 15) != 0)
+    return hipErrorInvalidValue;
+  const int64_t n16 = bytes >> 4;
+  const int64_t gx = std::min<int64_t>((n16 + 255) / 256, 64);
+  const int64_t gy = std::min<int64_t>(count, 65535);
+  hipLaunchKernelGGL(zero_regions_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)), dim3(256), 0, s,
+                     static_cast<char*>(base), stride, n16, count);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_batch(const CopyItem* items, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   CopyBatch b;

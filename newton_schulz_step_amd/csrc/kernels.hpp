@@ -109,6 +109,10 @@ hipError_t launch_adamw(int grad_dtype, float* p, const void* g, float* m, float
                         float beta1, float beta2, float step_size, float inv_bc2, float eps,
                         float decay, hipStream_t s);
 
+// Zeros over `count` regions of `bytes` bytes, `stride` bytes apart (the base,
+// stride and bytes multiples of 16).
+hipError_t launch_zero_regions(void* base, int64_t stride, int64_t bytes, int64_t count, hipStream_t s);
+
 struct CopyItem { const void* src; void* dst; int64_t bytes; };
 constexpr int kCopyBatch = 64;
 hipError_t launch_copy_batch(const CopyItem* items, int n, hipStream_t s);

@@ -28,6 +28,14 @@ int tile_for(int64_t m, int64_t count) {
   return count * t * (t + 1) / 2 >= 384 ? 256 : 128;
 }
 
+// The symmetric launches only need tiles up to m rounded to 128 (their K
+// loops stop there too), so with 128-tiles a short side of 1408 costs 66 tiles
+// of 128^2 instead of 21 of 256^2 (84 of 128^2); the full launches keep
+// 256-tiles, whose operand reuse the 128-tiles lack.
+int sym_tile_for(int64_t m, int tile) {
+  return (tile == 256 && m % 256 != 0 && m % 256 <= 128) ? 128 : tile;
+}
+
 static int64_t round_up(int64_t v, int64_t q) { return (v + q - 1) / q * q; }
 static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -173,6 +181,7 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
   for (size_t g = 0; g < L.groups.size(); ++g) {
     Group& G = L.groups[g];
     G.tile = tile_for(G.m, static_cast<int64_t>(per_group[g].size()));
+    G.sym_tile = sym_tile_for(G.m, G.tile);
     G.mp = round_up(G.m, G.tile);
     G.np = round_up(G.n, G.tile);
     L.groups[g].first = static_cast<int>(L.problems.size());

@@ -29,6 +29,7 @@ struct HostProblem {
 struct Group {
   int64_t m = 0, n = 0, mp = 0, np = 0;
   int tile = 0;
+  int sym_tile = 0;                  // tile edge of the symmetric (m x m) launches
   int first = 0, count = 0;          // problems [first, first + count) of the plan
   int64_t chunks = 0;                // momentum blocks per problem (ceil(m n / kMomChunk))
   size_t partial_first = 0;          // index of the group's first per-block partial sum
@@ -89,5 +90,8 @@ Layout build_layout(const muon_matrix_t* table, int32_t n_entries, const muon_hy
 
 // Tile edge used for a group of `count` problems whose short side is m.
 int tile_for(int64_t m, int64_t count);
+// Tile edge of the group's symmetric launches: 128 where the last row of
+// 256-tiles would be at most half used (the full launches keep 256-tiles).
+int sym_tile_for(int64_t m, int tile);
 
 }  // namespace muon
