@@ -527,6 +527,60 @@ __device__ __forceinline__ void apply8(const ApplyScalars& a, int64_t pidx, int6
   }
 }
 
+// Apply: the parameters of one 32-row block of a wave's outputs, as loaded
+// (chunk t: 8 elements along a row of a problem stored as is, or down a column
+// of one stored transposed), and whether each chunk takes the vector path.
+// Every load is issued, so the compiler can count what is in flight: a chunk
+// that is not applied reads the launch's descriptors instead (in bounds,
+// never used), at a byte offset from the parameters, which keeps it a global
+// load.
+template <typename T, int TILE, int EPI>
+struct ParamBlock {
+  static constexpr int CPR = Geo<T, TILE>::HALF / 8;
+  static constexpr int NR = 32 * CPR / 64;
+  ParamPack<EPI> pq[NR];
+  bool pv[NR];
+};
+
+template <typename T, int TILE, int EPI>
+__device__ __forceinline__ void chunk_at(const ProblemDesc& pd, int ti, int tj, int i, int t, int& gi, int& gj,
+                                         int64_t& e) {
+  using Gm = Geo<T, TILE>;
+  constexpr int HALF = Gm::HALF, CPR = HALF / 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gi_w = ti * TILE + (wave >> 1) * HALF, gj_w = tj * TILE + (wave & 1) * HALF;
+  const int q = lane + 64 * t;
+  if (!pd.transposed) {
+    gi = gi_w + i * 32 + q / CPR;
+    gj = gj_w + (q % CPR) * 8;
+    e = static_cast<int64_t>(gi) * pd.ld + gj;
+  } else {
+    gi = gi_w + i * 32 + (q & 3) * 8;
+    gj = gj_w + (q >> 2);
+    e = static_cast<int64_t>(gj) * pd.ld + gi;
+  }
+}
+
+template <typename T, int TILE, int EPI>
+__device__ __forceinline__ void load_param_block(const GemmArgs& a, const ProblemDesc& pd, int ti, int tj, int i,
+                                                 ParamBlock<T, TILE, EPI>& b) {
+  using PElem = typename std::conditional<EPI == EPI_APPLY_BF16, __bf16, float>::type;
+  const char* pbytes = static_cast<const char*>(a.params);
+  const int64_t dummy_off = static_cast<int64_t>(reinterpret_cast<uintptr_t>(a.probs) -
+                                                 reinterpret_cast<uintptr_t>(a.params));
+  const int m = a.m_valid, n = a.n_valid;
+#pragma unroll
+  for (int t = 0; t < ParamBlock<T, TILE, EPI>::NR; ++t) {
+    int gi, gj;
+    int64_t e;
+    chunk_at<T, TILE, EPI>(pd, ti, tj, i, t, gi, gj, e);
+    const bool whole = pd.transposed ? (gj < n && gi + 8 <= m) : (gi < m && gj + 8 <= n);
+    b.pv[t] = whole && (((pd.p_base + e) & 7) | ((pd.src_off + e) & 3)) == 0 && e >= pd.lo && e + 8 <= pd.hi;
+    b.pq[t].load(reinterpret_cast<const PElem*>(pbytes + (b.pv[t] ? (pd.p_base + e) * int64_t(sizeof(PElem))
+                                                                    : dummy_off)));
+  }
+}
+
 // Epilogue: v = alpha acc + beta D + gamma I, stored (or applied) as the launch asks.
 // The beta D term is one explicit fused multiply-add, fma(beta, D, alpha acc), so
 // every kernel that forms it rounds it the same way.
@@ -563,14 +617,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   int64_t src = 0, pb = 0, wlo = 0, whi = 0;
   ApplyScalars as{};
   constexpr bool APPLY = (EPI == EPI_APPLY || EPI == EPI_APPLY_BF16);
+  ProblemDesc pdv{};
   if constexpr (APPLY) {
-    const ProblemDesc pd = a.probs[prob];
-    transposed = pd.transposed;
-    ld = pd.ld;
-    src = pd.src_off;
-    pb = pd.p_base;
-    wlo = pd.lo;
-    whi = pd.hi;
+    pdv = a.probs[prob];
+    transposed = pdv.transposed;
+    ld = pdv.ld;
+    src = pdv.src_off;
+    pb = pdv.p_base;
+    wlo = pdv.lo;
+    whi = pdv.hi;
     as = ApplyScalars{a.params, a.update_out, a.shadow, a.decay, a.lr};
   }
   // (32-bit iterates: no registers to spare for them; read where used)
@@ -611,42 +666,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   // (32-bit iterates: the main loop leaves no room for a second block's
   // parameters, which are then requested right before they are used)
   constexpr bool PF_AHEAD = sizeof(T) == 2;
-  ParamPack<EPI == EPI_STORE ? EPI_APPLY : EPI> pq[2][NR];
-  bool pv[2][NR];
-  // chunk t of block i: canonical (gi, gj), 8 elements along a row (stored as
-  // is) or down a column (stored transposed), local index e of the first
-  auto chunk = [&](int i, int t, int& gi, int& gj, int64_t& e) {
-    const int q = lane + 64 * t;
-    if (!transposed) {
-      gi = gi_w + i * 32 + q / CPR;
-      gj = gj_w + (q % CPR) * 8;
-      e = static_cast<int64_t>(gi) * ld + gj;
-    } else {
-      gi = gi_w + i * 32 + (q & 3) * 8;
-      gj = gj_w + (q >> 2);
-      e = static_cast<int64_t>(gj) * ld + gi;
-    }
-  };
-  // a chunk that is not loaded reads the launch's descriptors instead (in
-  // bounds, never used), at a byte offset from the parameters
-  using PElem = typename std::conditional<EPI == EPI_APPLY_BF16, __bf16, float>::type;
-  const char* pbytes = static_cast<const char*>(a.params);
-  const int64_t dummy_off = static_cast<int64_t>(reinterpret_cast<uintptr_t>(a.probs) -
-                                                 reinterpret_cast<uintptr_t>(a.params));
+  constexpr int PEPI = EPI == EPI_STORE ? EPI_APPLY : EPI;
+  ParamBlock<T, TILE, PEPI> pblk[2];
+  auto chunk = [&](int i, int t, int& gi, int& gj, int64_t& e) { chunk_at<T, TILE, PEPI>(pdv, ti, tj, i, t, gi, gj, e); };
   auto load_params = [&](int i) {
-    if constexpr (APPLY) {
-#pragma unroll
-      for (int t = 0; t < NR; ++t) {
-        int gi, gj;
-        int64_t e;
-        chunk(i, t, gi, gj, e);
-        const bool whole = transposed ? (gj < n && gi + 8 <= m) : (gi < m && gj + 8 <= n);
-        pv[i & 1][t] = whole && (((pb + e) & 7) | ((src + e) & 3)) == 0 && e >= wlo && e + 8 <= whi;
-        // unconditional, so the compiler can count what is in flight
-        pq[i & 1][t].load(reinterpret_cast<const PElem*>(pbytes + (pv[i & 1][t] ? (pb + e) * int64_t(sizeof(PElem))
-                                                                                  : dummy_off)));
-      }
-    }
+    if constexpr (APPLY) load_param_block<T, TILE, PEPI>(a, pdv, ti, tj, i, pblk[i & 1]);
   };
 
   // Each wave stages into its own part of LDS, and one wave's LDS accesses are
@@ -706,7 +730,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
           // stored m x n: canonical (gi, gj) is local index gi * ld + gj
           if (gi < m && gj < n) {
             const int64_t e = static_cast<int64_t>(gi) * ld + gj;
-            apply8<EPI>(scalars(), pb + e, src + e, e, min(8, n - gj), wlo, whi, v, pq[i & 1][t], pv[i & 1][t]);
+            apply8<EPI>(scalars(), pb + e, src + e, e, min(8, n - gj), wlo, whi, v, pblk[i & 1].pq[t], pblk[i & 1].pv[t]);
           }
         } else {
           // the value goes back to the staging area for the column pass
@@ -747,7 +771,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
             float w[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) w[u] = stg[srow(r8 + u, cc)];
-            apply8<EPI>(scalars(), pb + e, src + e, e, min(8, m - gi), wlo, whi, w, pq[i & 1][t], pv[i & 1][t]);
+            apply8<EPI>(scalars(), pb + e, src + e, e, min(8, m - gi), wlo, whi, w, pblk[i & 1].pq[t], pblk[i & 1].pv[t]);
           }
         }
       } else {
