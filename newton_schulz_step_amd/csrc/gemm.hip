@@ -612,6 +612,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   const int gi_w = ti * TILE + wm * HALF;   // first row of this wave's outputs
   const int gj_w = tj * TILE + wn * HALF;   // first column
   const bool diag = SYM && (ti == tj);
+  // no element of the tile needs the diagonal tests (the gamma I term, the
+  // lower-triangle store): off the diagonal of a symmetric launch, or any tile
+  // of a full launch
+  const bool plain = !SYM || !diag;   // (full launches have no gamma: the launcher checks)
 
   int transposed = 0, ld = 0;
   int64_t src = 0, pb = 0, wlo = 0, whi = 0;
@@ -704,55 +708,67 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       x[0] = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc));
       x[1] = *reinterpret_cast<const f32x4*>(stg + srow(rr, cc) + 4);
     };
-    f32x4 sv[2][2];
-    stage_rd(0, sv[0]);
+    // A tile off the diagonal of a symmetric launch (and any full launch
+    // without a gamma I term) needs no per-element test, so its chunks run as
+    // one branch-free block the scheduler can interleave.
+    auto row_pass = [&](auto PLAIN) {
+      constexpr bool PL = decltype(PLAIN)::value;
+      f32x4 sv[2][2];
+      stage_rd(0, sv[0]);
 #pragma unroll
-    for (int t = 0; t < NR; ++t) {
-      if (t + 1 < NR) stage_rd(t + 1, sv[(t + 1) & 1]);
-      const int q = lane + 64 * t;
-      const int rr = q / CPR, cc = (q % CPR) * 8;
-      const int gi = gi_w + i * 32 + rr, gj = gj_w + cc;
-      float v[8];
+      for (int t = 0; t < NR; ++t) {
+        if (t + 1 < NR) stage_rd(t + 1, sv[(t + 1) & 1]);
+        const int q = lane + 64 * t;
+        const int rr = q / CPR, cc = (q % CPR) * 8;
+        const int gi = gi_w + i * 32 + rr, gj = gj_w + cc;
+        float v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { v[e] = alpha * sv[t & 1][0][e]; v[e + 4] = alpha * sv[t & 1][1][e]; }
-      if (D != nullptr) {
+        for (int e = 0; e < 4; ++e) { v[e] = alpha * sv[t & 1][0][e]; v[e + 4] = alpha * sv[t & 1][1][e]; }
+        if (D != nullptr) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(beta, dq[t].get(e), v[e]);
-      }
-      if (gamma != 0.0f) {
+          for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(beta, dq[t].get(e), v[e]);
+        }
+        if constexpr (!PL) {
+          if (gamma != 0.0f) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (gi == gj + e) v[e] += gamma;
-      }
-      float4* sp = reinterpret_cast<float4*>(stg + srow(rr, cc));
-      if constexpr (APPLY) {
-        if (!transposed) {
-          // stored m x n: canonical (gi, gj) is local index gi * ld + gj
-          if (gi < m && gj < n) {
-            const int64_t e = static_cast<int64_t>(gi) * ld + gj;
-            apply8<EPI>(scalars(), pb + e, src + e, e, min(8, n - gj), wlo, whi, v, pblk[i & 1].pq[t], pblk[i & 1].pv[t]);
+            for (int e = 0; e < 8; ++e)
+              if (gi == gj + e) v[e] += gamma;
+          }
+        }
+        float4* sp = reinterpret_cast<float4*>(stg + srow(rr, cc));
+        if constexpr (APPLY) {
+          if (!transposed) {
+            // stored m x n: canonical (gi, gj) is local index gi * ld + gj
+            if (gi < m && gj < n) {
+              const int64_t e = static_cast<int64_t>(gi) * ld + gj;
+              apply8<EPI>(scalars(), pb + e, src + e, e, min(8, n - gj), wlo, whi, v, pblk[i & 1].pq[t],
+                          pblk[i & 1].pv[t]);
+            }
+          } else {
+            // the value goes back to the staging area for the column pass
+            sp[0] = make_float4(v[0], v[1], v[2], v[3]);
+            sp[1] = make_float4(v[4], v[5], v[6], v[7]);
           }
         } else {
-          // the value goes back to the staging area for the column pass
-          sp[0] = make_float4(v[0], v[1], v[2], v[3]);
-          sp[1] = make_float4(v[4], v[5], v[6], v[7]);
-        }
-      } else {
-        T o[8];
-        rne<T, 8>(v, o);
-        T* cp = C + static_cast<int64_t>(prob) * c_ps + static_cast<int64_t>(gi) * ldc + gj;
-        if (!diag || gi >= gj + 7) {
-          st8<T>(cp, o);
-        } else {
-          for (int e = 0; e < 8; ++e)
-            if (gi >= gj + e) cp[e] = o[e];
-        }
-        if (need_col) {
-          sp[0] = make_float4(to_f32(o[0]), to_f32(o[1]), to_f32(o[2]), to_f32(o[3]));
-          sp[1] = make_float4(to_f32(o[4]), to_f32(o[5]), to_f32(o[6]), to_f32(o[7]));
+          T o[8];
+          rne<T, 8>(v, o);
+          T* cp = C + static_cast<int64_t>(prob) * c_ps + static_cast<int64_t>(gi) * ldc + gj;
+          if (PL || !diag || gi >= gj + 7) {
+            st8<T>(cp, o);
+          } else {
+            for (int e = 0; e < 8; ++e)
+              if (gi >= gj + e) cp[e] = o[e];
+          }
+          if (need_col) {
+            sp[0] = make_float4(to_f32(o[0]), to_f32(o[1]), to_f32(o[2]), to_f32(o[3]));
+            sp[1] = make_float4(to_f32(o[4]), to_f32(o[5]), to_f32(o[6]), to_f32(o[7]));
+          }
         }
       }
-    }
+    };
+    if constexpr (!SYM) row_pass(std::true_type{});
+    else if (plain) row_pass(std::true_type{});
+    else row_pass(std::false_type{});
     if (i + 1 < WB) load_d(i + 1);
 
     // ---- column pass
@@ -775,24 +791,29 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
           }
         }
       } else {
+        auto col_pass = [&](auto PLAIN) {
+          constexpr bool PL = decltype(PLAIN)::value;
 #pragma unroll
-        for (int t = 0; t < NC; ++t) {
-          const int q = lane + 64 * t;
-          const int r8 = (q & 3) * 8, cc = q >> 2;
-          const int gi = gi_w + i * 32 + r8, gj = gj_w + cc;
-          float w[8];
+          for (int t = 0; t < NC; ++t) {
+            const int q = lane + 64 * t;
+            const int r8 = (q & 3) * 8, cc = q >> 2;
+            const int gi = gi_w + i * 32 + r8, gj = gj_w + cc;
+            float w[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) w[e] = stg[srow(r8 + e, cc)];
-          T o[8];
-          rne<T, 8>(w, o);
-          T* cp = Ct + static_cast<int64_t>(prob) * ct_ps + static_cast<int64_t>(gj) * ldct + gi;
-          if (!diag || gi > gj) {
-            st8<T>(cp, o);
-          } else {
-            for (int e = 0; e < 8; ++e)
-              if (gi + e > gj) cp[e] = o[e];
+            for (int e = 0; e < 8; ++e) w[e] = stg[srow(r8 + e, cc)];
+            T o[8];
+            rne<T, 8>(w, o);
+            T* cp = Ct + static_cast<int64_t>(prob) * ct_ps + static_cast<int64_t>(gj) * ldct + gi;
+            if (PL || !diag || gi > gj) {
+              st8<T>(cp, o);
+            } else {
+              for (int e = 0; e < 8; ++e)
+                if (gi + e > gj) cp[e] = o[e];
+            }
           }
-        }
+        };
+        if (plain) col_pass(std::true_type{});   // (symmetric launches only)
+        else col_pass(std::false_type{});
       }
     }
   }
@@ -1475,6 +1496,7 @@ static hipError_t launch_t(const GemmBatch& b, hipStream_t s) {
     if (a.K <= 0 || a.K % (2 * 128 / static_cast<int>(sizeof(T))) != 0) return hipErrorInvalidValue;
     if (b.start[g + 1] - b.start[g] != a.total_tiles || a.total_tiles < 0) return hipErrorInvalidValue;
     if ((a.D != nullptr) != HAS_D) return hipErrorInvalidValue;   // one kind of epilogue per launch
+    if (!SYM && a.gamma != 0.0f) return hipErrorInvalidValue;      // gamma I: symmetric launches only
     // store launches write C, and its mirror Ct exactly when symmetric
     if (EPI == EPI_STORE && (a.C == nullptr || (a.Ct != nullptr) != SYM)) return hipErrorInvalidValue;
   }

@@ -28,7 +28,7 @@ struct GemmArgs {
   const void* Q; int64_t q_ps; int32_t ldq;
   int32_t K;
   int32_t tiles_m, tiles_n, tiles_per_problem, total_tiles;
-  float alpha, beta, gamma;
+  float alpha, beta, gamma;                      // gamma: symmetric launches only
   const void* D; int64_t d_ps; int32_t ldd;      // optional beta term: symmetric launches only,
                                                  // and then in every group of the launch
   void* C; int64_t c_ps; int32_t ldc;            // optional row-major store
