@@ -609,6 +609,22 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
   // 8 * (bits 3-4 of r), which keeps 8-column chunks contiguous and puts the rows
   // r, r + 8, r + 16, r + 24 that one column-pass read gathers in different banks
   auto srow = [&](int r, int c) { return r * SP + (c ^ (((r >> 3) & 3) << 3)); };
+  // The mirror of a 16-bit symmetric store goes through a 16-bit copy of the
+  // rounded block, laid over the wave's own float staging: row r at byte
+  // r * 2 HALF, its 32-byte chunks (16 columns) permuted by h16(r). The row
+  // pass writes row r's bytes only after the float rows beneath them have been
+  // read (16-bit row r lies below float row r). A transposed read then takes 4
+  // rows x 16 columns per 16 lanes; the 8 rows one half wave reads land in 8
+  // different chunk slots (HALF = 128) or in 4 slots x 2 row parities (HALF =
+  // 64), so each read spreads over all banks.
+  constexpr bool TR_MIRROR = sizeof(T) == 2 && SYM && EPI == EPI_STORE;
+  constexpr int RP16 = HALF * 2;         // 16-bit staging row pitch (bytes)
+  auto h16 = [](int r) {
+    if constexpr (HALF == 128) return (r & 3) | (((r >> 3) & 1) << 2);
+    else return ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
+  };
+  auto soff16 = [&](int r, int c) { return r * RP16 + (((c >> 4) ^ h16(r)) << 5) + (c & 15) * 2; };
+  char* stg16 = reinterpret_cast<char*>(stg);
   const int gi_w = ti * TILE + wm * HALF;   // first row of this wave's outputs
   const int gj_w = tj * TILE + wn * HALF;   // first column
   const bool diag = SYM && (ti == tj);
@@ -759,7 +775,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
             for (int e = 0; e < 8; ++e)
               if (gi >= gj + e) cp[e] = o[e];
           }
-          if (need_col) {
+          if constexpr (TR_MIRROR) {
+            u16x8 w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = __builtin_bit_cast(unsigned short, o[e]);
+            *reinterpret_cast<u16x8*>(stg16 + soff16(rr, cc)) = w;
+          } else if (need_col) {
             sp[0] = make_float4(to_f32(o[0]), to_f32(o[1]), to_f32(o[2]), to_f32(o[3]));
             sp[1] = make_float4(to_f32(o[4]), to_f32(o[5]), to_f32(o[6]), to_f32(o[7]));
           }
@@ -793,6 +814,29 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int prob, int ti, in
       } else {
         auto col_pass = [&](auto PLAIN) {
           constexpr bool PL = decltype(PLAIN)::value;
+          if constexpr (TR_MIRROR) {
+            // lane (g, s) = (lane / 16, lane % 16): rows 8g .. 8g + 7 of column
+            // 16t + s, two transposed reads of 4 rows each
+            const int g = lane >> 4, s16 = lane & 15;
+            const int r0 = 8 * g + (s16 >> 2);
+#pragma unroll
+            for (int t = 0; t < NC; ++t) {
+              const int c0 = 16 * t + 4 * (s16 & 3);
+              const u16x4 lo = __builtin_bit_cast(u16x4, TrRead<T>::get(stg16 + soff16(r0, c0)));
+              const u16x4 hi = __builtin_bit_cast(u16x4, TrRead<T>::get(stg16 + soff16(r0 + 4, c0)));
+              const int gi = gi_w + i * 32 + 8 * g, gj = gj_w + 16 * t + s16;
+              const u16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              unsigned short* cp = reinterpret_cast<unsigned short*>(Ct + static_cast<int64_t>(prob) * ct_ps +
+                                                                     static_cast<int64_t>(gj) * ldct + gi);
+              if (PL || !diag || gi > gj) {
+                *reinterpret_cast<u16x8*>(cp) = w;
+              } else {
+                for (int e = 0; e < 8; ++e)
+                  if (gi + e > gj) cp[e] = w[e];
+              }
+            }
+            return;
+          }
 #pragma unroll
           for (int t = 0; t < NC; ++t) {
             const int q = lane + 64 * t;
