@@ -7,7 +7,7 @@ element. A wrong or missing mirror element changes a step's result by far less
 than the parity gates can see, so these tests read the workspace after a step
 instead: it was filled with a sentinel first, and it must then hold the expected
 number of m x m regions (at the padded row pitch the library uses) that are
-bit-for-bit symmetric, free of the sentinel and not all zero.
+bit-for-bit symmetric, free of the sentinel and with a non-zero diagonal.
 
 The workspace is scanned at every 256-byte boundary, where its buffers start,
 so the test depends on no other detail of its layout.
@@ -19,10 +19,13 @@ import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-# (method, iteration type, rows, cols, symmetric buffers at least): rows > 128,
-# so every product runs through the tiled launches; the sizes cover symmetric
-# 128-tiles (m mod 256 <= 128) and 256-tiles, ragged diagonal tiles and a
-# matrix stored transposed (rows > cols)
+# (method, iteration type, rows, cols, symmetric buffers at least). With a
+# short side above 128 every product runs through the tiled launches; the sizes
+# cover symmetric 128-tiles (m mod 256 <= 128) and 256-tiles, ragged diagonal
+# tiles and a matrix stored transposed (rows > cols). With a short side of at
+# most 128 the 16-bit paths are fused: standard keeps A' (from the update + Gram
+# pass) and B; Gram keeps R0 (from the X0 + R0 pass) in the workspace, its chain
+# runs in LDS.
 CASES = [
     ("standard", "bf16", 300, 520, 2),
     ("standard", "bf16", 700, 900, 2),
@@ -30,12 +33,14 @@ CASES = [
     ("standard", "f32", 300, 520, 2),
     ("gram", "f16", 300, 700, 3),
     ("gram", "f16", 700, 1000, 3),
+    ("standard", "bf16", 100, 700, 2),
+    ("gram", "f16", 700, 100, 1),
 ]
 
 
 def _symmetric_regions(ws, m, esz):
     """Offsets (bytes) and pitches of the m x m regions of `ws` (raw bytes) that
-    are exactly symmetric, sentinel-free and not all zero."""
+    are exactly symmetric, sentinel-free and have no zero on the diagonal."""
     words = ws.view(np.uint16 if esz == 2 else np.uint32)
     sentinel = np.iinfo(words.dtype).max
     found = []
@@ -52,11 +57,21 @@ def _symmetric_regions(ws, m, esz):
         for s in starts[np.all(a == b, axis=1)]:
             R = words[s:s + span + (pitch - m)].reshape(m, pitch)[:, :m] if span + (pitch - m) <= words.size - s \
                 else np.stack([words[s + i * pitch:s + i * pitch + m] for i in range(m)])
-            if np.any(R == sentinel) or not np.any(R):
+            # every diagonal entry of these products is non-zero (R and A have
+            # squared row norms there), while a principal submatrix that starts
+            # inside a buffer runs into its zero padding rows
+            if np.any(R == sentinel) or np.any((np.diagonal(R) & (sentinel >> 1)) == 0):
                 continue
             if np.array_equal(R, R.T):
                 found.append((int(s) * esz, pitch))
-    return found
+    # a principal submatrix of a symmetric buffer is symmetric too: keep only
+    # regions that do not overlap one found earlier, one per buffer
+    kept, end = [], -1
+    for off, pitch in sorted(found):
+        if off >= end:
+            kept.append((off, pitch))
+            end = off + m * pitch * esz
+    return kept
 
 
 @pytest.mark.parametrize("method,ns_dtype,rows,cols,expect", CASES)
